@@ -1,0 +1,247 @@
+"""fp64 CPU oracle for softmax attention -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path never calls it and it
+imports nothing from the product package: the two share no code.
+
+Everything is computed in double precision by the plain C routines in
+``oracle.c`` (explicit score and probability rows, no tiling), wrapped here
+with ctypes over numpy arrays.  Inputs are bf16 bit patterns held in numpy
+``uint16`` arrays; outputs are float64.
+
+What each routine follows:
+
+* ``attn_rows`` -- exact attention O = softmax(Q K^T * scale + mask) V and its
+  natural-log LSE ("flashattention-kernels" page, §0/§1: tiling and online
+  softmax preserve exact attention; "cuda-kernel-pretrain" page, §2).  Also the
+  decode case (one query row, ``kv_len`` valid keys) and partial attention over
+  a key range (Flash-Decoding's chunks, "flashattention-kernels" page, §3).
+* ``lse_merge`` -- the reduction that combines per-chunk partial results
+  (same page, §3; the pages give no formula, the log-sum-exp weighting used
+  here is the unique one that reproduces the unsplit softmax).
+* ``sage_rows`` / ``sage_quantise`` -- the quantised recipe (Smooth-K, INT8
+  Q/K per 64-token block, E4M3 P and per-channel E4M3 V, fp32 accumulation)
+  emulated step by step ("GPU kernel overview" page, SageAttention chain and
+  its insight that QK suits INT8 while PV suits FP8).
+* ``e4m3_decode`` / ``e4m3_encode`` -- the OCP E4M3 ("fn") format.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_f64p = ctypes.POINTER(ctypes.c_double)
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_i8p = ctypes.POINTER(ctypes.c_int8)
+
+
+def build(force: bool = True) -> str:
+    """Compile ``oracle.c`` into ``liboracle.so`` with gcc (fp64, OpenMP)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11",
+               "-Wall", "-Wextra", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build(force=False)
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.oracle_attn_rows.restype = ctypes.c_double
+    lib.oracle_attn_rows.argtypes = [
+        _u16p, _u16p, _u16p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_double, _i64p, ctypes.c_int64, _f64p, _f64p, ctypes.c_int]
+    lib.oracle_lse_merge.restype = None
+    lib.oracle_lse_merge.argtypes = [_f64p, _f64p, ctypes.c_int, ctypes.c_int64,
+                                     ctypes.c_int, _f64p, _f64p]
+    lib.oracle_sage_rows.restype = ctypes.c_double
+    lib.oracle_sage_rows.argtypes = [
+        _u16p, _u16p, _u16p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_int, ctypes.c_int,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
+        _i64p, ctypes.c_int64, _f64p, _f64p, ctypes.c_int]
+    lib.oracle_sage_quantise.restype = ctypes.c_int
+    lib.oracle_sage_quantise.argtypes = [
+        _u16p, _u16p, _u16p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, _f64p, _i8p, _f64p, _i8p, _f64p,
+        _f64p, _f64p]
+    lib.oracle_e4m3_decode.restype = ctypes.c_double
+    lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+    lib.oracle_e4m3_encode.argtypes = [ctypes.c_double]
+    lib.oracle_quant_i8.restype = ctypes.c_int
+    lib.oracle_quant_i8.argtypes = [ctypes.c_double, ctypes.c_double]
+    lib.oracle_num_threads.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _u16(a) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint16:
+        raise TypeError("oracle inputs are bf16 bit patterns (numpy uint16), got %s" % a.dtype)
+    return a
+
+
+def _ptr(a, t):
+    return a.ctypes.data_as(t)
+
+
+def default_threads() -> int:
+    return len(os.sched_getaffinity(0))
+
+
+def attn_rows(q, k, v, *, causal: bool, scale: float, rows=None, kv_len=None,
+              k_range=None, threads: int | None = None):
+    """Exact attention rows in fp64.
+
+    q: [B,H,Nq,d]; k, v: [B,Hkv,Nk,d] (uint16 bf16 bits).  ``rows`` lists
+    flattened (b*H + h)*Nq + i indices (None: all rows, returned as
+    [B,H,Nq,d] / [B,H,Nq]).  ``kv_len`` [B] limits the visible keys per batch.
+    ``k_range`` (lo, hi) restricts the keys to [lo, hi).
+    Returns (o, lse, max |1 - sum P|).
+    """
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    B, H, Nq, d = q.shape
+    Bk, Hkv, Nk, dk = k.shape
+    if (Bk, dk) != (B, d) or v.shape != k.shape:
+        raise ValueError("shape mismatch")
+    lib = _load()
+    if rows is None:
+        nrows = B * H * Nq
+        rows_p = None
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        nrows = rows.size
+        rows_p = _ptr(rows, _i64p)
+    o = np.empty((nrows, d), dtype=np.float64)
+    lse = np.empty((nrows,), dtype=np.float64)
+    kl = None
+    if kv_len is not None:
+        kv_len = np.ascontiguousarray(kv_len, dtype=np.int32)
+        kl = _ptr(kv_len, _i32p)
+    lo, hi = (0, Nk) if k_range is None else k_range
+    err = lib.oracle_attn_rows(_ptr(q, _u16p), _ptr(k, _u16p), _ptr(v, _u16p), B, H, Hkv,
+                               Nq, Nk, d, int(bool(causal)), kl, int(lo), int(hi),
+                               float(scale), rows_p, nrows, _ptr(o, _f64p),
+                               _ptr(lse, _f64p), int(threads or default_threads()))
+    if err < 0:
+        raise ValueError("oracle_attn_rows rejected its arguments")
+    if rows is None:
+        o = o.reshape(B, H, Nq, d)
+        lse = lse.reshape(B, H, Nq)
+    return o, lse, err
+
+
+def lse_merge(o_parts, lse_parts):
+    """Merge partial (O_s, lse_s) over disjoint key sets.
+
+    o_parts [S, R, d], lse_parts [S, R] (float64).  Returns (o [R,d], lse [R]).
+    """
+    o_parts = np.ascontiguousarray(o_parts, dtype=np.float64)
+    lse_parts = np.ascontiguousarray(lse_parts, dtype=np.float64)
+    S, R, d = o_parts.shape
+    o = np.empty((R, d), dtype=np.float64)
+    lse = np.empty((R,), dtype=np.float64)
+    _load().oracle_lse_merge(_ptr(o_parts, _f64p), _ptr(lse_parts, _f64p), S, R, d,
+                             _ptr(o, _f64p), _ptr(lse, _f64p))
+    return o, lse
+
+
+def sage_rows(q, k, v, *, causal: bool, scale: float, rows=None, blk: int = 64,
+              tile_n: int = 64, smooth_k: bool = True, quant_qk: bool = True,
+              quant_p: bool = True, quant_v: bool = True, p_scale: float = 448.0,
+              threads: int | None = None):
+    """Quantised (SageAttention-style) attention emulated step by step in fp64.
+
+    Same shapes and ``rows`` convention as :func:`attn_rows` (Nq == Nk == N).
+    ``tile_n`` is the key-tile width of the online softmax, which decides the
+    running max that P is quantised against.  Returns (o, lse).
+    """
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, N, d) or v.shape != k.shape:
+        raise ValueError("shape mismatch")
+    if rows is None:
+        nrows = B * H * N
+        rows_p = None
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        nrows = rows.size
+        rows_p = _ptr(rows, _i64p)
+    o = np.empty((nrows, d), dtype=np.float64)
+    lse = np.empty((nrows,), dtype=np.float64)
+    r = _load().oracle_sage_rows(_ptr(q, _u16p), _ptr(k, _u16p), _ptr(v, _u16p), B, H, Hkv, N,
+                                 d, int(bool(causal)), float(scale), int(blk), int(tile_n),
+                                 int(smooth_k), int(quant_qk), int(quant_p), int(quant_v),
+                                 float(p_scale), rows_p, nrows, _ptr(o, _f64p),
+                                 _ptr(lse, _f64p), int(threads or default_threads()))
+    if r < 0:
+        raise ValueError("oracle_sage_rows rejected its arguments")
+    if rows is None:
+        o = o.reshape(B, H, N, d)
+        lse = lse.reshape(B, H, N)
+    return o, lse
+
+
+def sage_quantise(q, k, v, *, blk: int = 64, smooth_k: bool = True):
+    """Quantisation state of the recipe (see ``oracle_sage_quantise`` in oracle.c)."""
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    nb = (N + blk - 1) // blk
+    out = dict(
+        kmean=np.empty((B, Hkv, d)), qhat=np.empty((B, H, N, d), dtype=np.int8),
+        qdelta=np.empty((B, H, nb)), khat=np.empty((B, Hkv, N, d), dtype=np.int8),
+        kdelta=np.empty((B, Hkv, nb)), vq=np.empty((B, Hkv, N, d)),
+        vdelta=np.empty((B, Hkv, d)))
+    r = _load().oracle_sage_quantise(
+        _ptr(q, _u16p), _ptr(k, _u16p), _ptr(v, _u16p), B, H, Hkv, N, d, int(blk),
+        int(smooth_k), _ptr(out["kmean"], _f64p), _ptr(out["qhat"], _i8p),
+        _ptr(out["qdelta"], _f64p), _ptr(out["khat"], _i8p), _ptr(out["kdelta"], _f64p),
+        _ptr(out["vq"], _f64p), _ptr(out["vdelta"], _f64p))
+    if r < 0:
+        raise ValueError("oracle_sage_quantise rejected its arguments")
+    return out
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    lib = _load()
+    codes = np.asarray(codes, dtype=np.uint8)
+    return np.array([lib.oracle_e4m3_decode(int(c)) for c in codes.ravel()]).reshape(codes.shape)
+
+
+def e4m3_encode(x) -> np.ndarray:
+    lib = _load()
+    x = np.asarray(x, dtype=np.float64)
+    return np.array([lib.oracle_e4m3_encode(float(t)) for t in x.ravel()],
+                    dtype=np.uint8).reshape(x.shape)
+
+
+def quant_i8(x, delta) -> np.ndarray:
+    lib = _load()
+    x = np.asarray(x, dtype=np.float64)
+    return np.array([lib.oracle_quant_i8(float(t), float(delta)) for t in x.ravel()],
+                    dtype=np.int64).reshape(x.shape)
+
+
+def num_threads() -> int:
+    return _load().oracle_num_threads()

@@ -1,0 +1,543 @@
+/*
+ * Plain fp64 CPU oracle for softmax attention — TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the tests, the smoke check and the bench's CPU-baseline leg may load
+ * this library.  It shares no code, header, table or helper with the GPU
+ * path: every routine here is written from the definition of the operation,
+ * in double precision, as plainly as possible.  Nothing here is blocked,
+ * fused or reordered beyond what the definition states.
+ *
+ * Sources (the web pages this build follows):
+ *  - "flashattention-kernels" page (cyk1337 paper-daily), §0 lineage and §1
+ *    four-layer breakdown: exact softmax attention is the semantics every
+ *    FlashAttention-style kernel keeps; tiling + online softmax only change
+ *    how it is evaluated.  §3 (inference side): Flash-Decoding splits the KV
+ *    sequence into chunks, computes partial attention per chunk, then reduces.
+ *  - "cuda-kernel-pretrain" page (cyk1337 paper-daily), §2 (attention): the
+ *    IO-aware kernel keeps exactness; numerics must be regression-checked
+ *    against an unfused reference.  §3: GQA/MQA share one K/V head per group.
+ *  - "GPU kernel overview" page (zhaifeiyue.github.io/overview/kernel.html),
+ *    SageAttention chain and the "INT for QK, FP for PV" insight: Smooth-K,
+ *    per-block INT8 Q/K for QK^T, FP8 (E4M3) for P and V.
+ *
+ * Conventions (readings of what the pages leave open):
+ *  - inputs are bf16 bit patterns (uint16), decoded exactly to double;
+ *  - causal masking is top-left aligned: key j is visible to query i iff j <= i;
+ *  - kv head of query head h is h / (H / Hkv) (consecutive groups);
+ *  - lse is the natural-log log-sum-exp of the scaled, masked scores;
+ *  - a row with no visible key gets O = 0 and lse = -inf.
+ *
+ * Build: gcc -O2 -fopenmp -shared -fPIC oracle.c -o liboracle.so -lm
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ------------------------------------------------------------------------ */
+/* Number formats                                                            */
+/* ------------------------------------------------------------------------ */
+
+/* bf16 is the upper half of an IEEE binary32; widening is exact. */
+static double bf16_to_f64(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/*
+ * OCP FP8 E4M3 ("fn" variant): 1 sign, 4 exponent bits (bias 7), 3 mantissa
+ * bits, no infinities, S.1111.111 is NaN, largest finite magnitude 448.
+ * Decoding is the closed form of the format definition.
+ */
+double oracle_e4m3_decode(uint8_t code)
+{
+    int s = (code >> 7) & 1;
+    int e = (code >> 3) & 0xF;
+    int m = code & 7;
+    double mag;
+    if (e == 0xF && m == 7)
+        return NAN;
+    if (e == 0)
+        mag = ldexp((double)m / 8.0, -6); /* subnormal */
+    else
+        mag = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return s ? -mag : mag;
+}
+
+/*
+ * Encode to E4M3 with round-to-nearest, ties to the even code, saturating at
+ * +-448 (infinities also saturate; NaN maps to the NaN code).  The positive
+ * finite codes 0x00..0x7E are strictly increasing in value, so the nearest
+ * code is found by a binary search over that ordered table followed by a
+ * comparison with the neighbour above.
+ */
+uint8_t oracle_e4m3_encode(double x)
+{
+    uint8_t sign = 0;
+    double a = x;
+    if (isnan(x))
+        return 0x7F;
+    if (a < 0) {
+        sign = 0x80;
+        a = -a;
+    }
+    if (a >= 448.0)
+        return sign | 0x7E;
+    /* largest code c in [0, 0x7E] with value(c) <= a */
+    int lo = 0, hi = 0x7E;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) / 2;
+        if (oracle_e4m3_decode((uint8_t)mid) <= a)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    int c = lo;
+    if (c < 0x7E) {
+        double below = oracle_e4m3_decode((uint8_t)c);
+        double above = oracle_e4m3_decode((uint8_t)(c + 1));
+        double db = a - below, da = above - a;
+        if (da < db || (da == db && ((c + 1) & 1) == 0))
+            c = c + 1;
+    }
+    return sign | (uint8_t)c;
+}
+
+double oracle_e4m3_round(double x) { return oracle_e4m3_decode(oracle_e4m3_encode(x)); }
+
+/* Symmetric INT8 quantisation: round half to even, clamp to [-127, 127]. */
+static int quant_i8(double x, double delta)
+{
+    double r = nearbyint(x / delta); /* default FP environment: ties to even */
+    if (r > 127.0)
+        r = 127.0;
+    if (r < -127.0)
+        r = -127.0;
+    return (int)r;
+}
+
+int oracle_quant_i8(double x, double delta) { return quant_i8(x, delta); }
+
+/* ------------------------------------------------------------------------ */
+/* Exact attention, one query row at a time                                  */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Row (b, h, i) of softmax(Q K^T * scale + mask) V over the keys j in
+ * [k_lo, k_hi) that the mask leaves visible.  The score row and the
+ * probability row are materialised explicitly.
+ *
+ * Layouts: q [B,H,Nq,d]; k, v [B,Hkv,Nk,d]; all bf16 bits, contiguous.
+ * kv_len (may be NULL): per-batch number of valid keys (decode caches);
+ * keys at or beyond kv_len[b] are never read.
+ * Returns |1 - sum_j P_ij| (0 for an empty row).
+ */
+static double attn_row(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                       int B, int H, int Hkv, int Nq, int Nk, int d, int causal,
+                       const int32_t *kv_len, int64_t k_lo, int64_t k_hi,
+                       double scale, int64_t row, double *o_row, double *lse_out,
+                       double *S, double *P)
+{
+    int64_t i = row % Nq;
+    int64_t bh = row / Nq;
+    int64_t h = bh % H;
+    int64_t b = bh / H;
+    int64_t g = h / (H / Hkv);
+    const uint16_t *qi = q + ((b * H + h) * (int64_t)Nq + i) * d;
+    const uint16_t *kb = k + (b * Hkv + g) * (int64_t)Nk * d;
+    const uint16_t *vb = v + (b * Hkv + g) * (int64_t)Nk * d;
+    (void)B;
+
+    int64_t hi = k_hi;
+    if (hi > Nk)
+        hi = Nk;
+    if (kv_len && hi > kv_len[b])
+        hi = kv_len[b];
+    if (causal && hi > i + 1)
+        hi = i + 1;
+    int64_t lo = k_lo < 0 ? 0 : k_lo;
+
+    for (int c = 0; c < d; ++c)
+        o_row[c] = 0.0;
+    if (hi <= lo) {
+        *lse_out = -INFINITY;
+        return 0.0;
+    }
+    int64_t n = hi - lo;
+
+    /* scores */
+    for (int64_t j = 0; j < n; ++j) {
+        const uint16_t *kj = kb + (lo + j) * d;
+        double dot = 0.0;
+        for (int c = 0; c < d; ++c)
+            dot += bf16_to_f64(qi[c]) * bf16_to_f64(kj[c]);
+        S[j] = dot * scale;
+    }
+    /* explicit softmax */
+    double m = S[0];
+    for (int64_t j = 1; j < n; ++j)
+        if (S[j] > m)
+            m = S[j];
+    double sum = 0.0;
+    for (int64_t j = 0; j < n; ++j) {
+        P[j] = exp(S[j] - m);
+        sum += P[j];
+    }
+    double psum = 0.0;
+    for (int64_t j = 0; j < n; ++j) {
+        P[j] /= sum;
+        psum += P[j];
+    }
+    /* O = P V */
+    for (int64_t j = 0; j < n; ++j) {
+        const uint16_t *vj = vb + (lo + j) * d;
+        for (int c = 0; c < d; ++c)
+            o_row[c] += P[j] * bf16_to_f64(vj[c]);
+    }
+    *lse_out = m + log(sum);
+    return fabs(1.0 - psum);
+}
+
+/*
+ * Exact attention for the listed rows (flattened (b*H + h)*Nq + i), or for
+ * every row when rows == NULL.  Outputs o [nrows, d] and lse [nrows] in fp64.
+ * Keys are restricted to [k_lo, k_hi) (pass 0 and Nk for the whole sequence).
+ * Returns the largest |1 - sum_j P_ij| seen (a self-check of the softmax),
+ * or -1 on invalid arguments.
+ */
+double oracle_attn_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                        int B, int H, int Hkv, int Nq, int Nk, int d, int causal,
+                        const int32_t *kv_len, int64_t k_lo, int64_t k_hi,
+                        double scale, const int64_t *rows, int64_t nrows,
+                        double *o, double *lse, int nthreads)
+{
+    if (B <= 0 || H <= 0 || Hkv <= 0 || H % Hkv != 0 || Nq <= 0 || Nk <= 0 || d <= 0)
+        return -1.0;
+    if (!rows)
+        nrows = (int64_t)B * H * Nq;
+    double worst = 0.0;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel reduction(max : worst)
+    {
+        double *S = (double *)malloc(sizeof(double) * (size_t)Nk);
+        double *P = (double *)malloc(sizeof(double) * (size_t)Nk);
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t r = 0; r < nrows; ++r) {
+            int64_t row = rows ? rows[r] : r;
+            double e = attn_row(q, k, v, B, H, Hkv, Nq, Nk, d, causal, kv_len, k_lo, k_hi,
+                                scale, row, o + r * d, lse + r, S, P);
+            if (e > worst)
+                worst = e;
+        }
+        free(S);
+        free(P);
+    }
+    return worst;
+}
+
+/*
+ * Merge of partial results over disjoint key sets (the reduction step of
+ * split-KV decoding): with M = max_s lse_s and w_s = exp(lse_s - M),
+ * O = sum_s w_s O_s / sum_s w_s and lse = M + ln sum_s w_s.
+ * o_parts [nparts, nrows, d], lse_parts [nparts, nrows]; parts whose lse is
+ * -inf (no visible key) carry no weight.
+ */
+void oracle_lse_merge(const double *o_parts, const double *lse_parts, int nparts,
+                      int64_t nrows, int d, double *o, double *lse)
+{
+    for (int64_t r = 0; r < nrows; ++r) {
+        double M = -INFINITY;
+        for (int s = 0; s < nparts; ++s)
+            if (lse_parts[s * nrows + r] > M)
+                M = lse_parts[s * nrows + r];
+        for (int c = 0; c < d; ++c)
+            o[r * d + c] = 0.0;
+        if (M == -INFINITY) {
+            lse[r] = -INFINITY;
+            continue;
+        }
+        double wsum = 0.0;
+        for (int s = 0; s < nparts; ++s) {
+            double w = exp(lse_parts[s * nrows + r] - M);
+            wsum += w;
+            for (int c = 0; c < d; ++c)
+                o[r * d + c] += w * o_parts[((int64_t)s * nrows + r) * d + c];
+        }
+        for (int c = 0; c < d; ++c)
+            o[r * d + c] /= wsum;
+        lse[r] = M + log(wsum);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* SageAttention-style quantised attention, emulated step by step            */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Quantisation state computed once per call from the bf16 inputs:
+ *  kmean[b,g,c]     Smooth-K channel mean of K over all Nk tokens
+ *  qhat, qdelta     per (b, h, 64-token block) INT8 codes of Q and their scale
+ *  khat, kdelta     the same for K - kmean
+ *  vhat, vdelta     per (b, g, channel) E4M3 values of V / vdelta (decoded)
+ */
+typedef struct {
+    double *kmean;
+    int8_t *qhat, *khat;
+    double *qdelta, *kdelta;
+    double *vq;     /* decoded E4M3 value of V / vdelta */
+    double *vdelta;
+} sage_state;
+
+static void sage_prepare(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                         int B, int H, int Hkv, int N, int d, int blk, int smooth_k,
+                         sage_state *st)
+{
+    int64_t nqb = (N + blk - 1) / blk;
+    st->kmean = (double *)calloc((size_t)B * Hkv * d, sizeof(double));
+    st->qhat = (int8_t *)malloc((size_t)B * H * N * d);
+    st->khat = (int8_t *)malloc((size_t)B * Hkv * N * d);
+    st->qdelta = (double *)malloc(sizeof(double) * (size_t)B * H * nqb);
+    st->kdelta = (double *)malloc(sizeof(double) * (size_t)B * Hkv * nqb);
+    st->vq = (double *)malloc(sizeof(double) * (size_t)B * Hkv * N * d);
+    st->vdelta = (double *)malloc(sizeof(double) * (size_t)B * Hkv * d);
+
+    /* Smooth-K: subtract the per-channel mean of K over the tokens. */
+#pragma omp parallel for
+    for (int64_t bg = 0; bg < (int64_t)B * Hkv; ++bg) {
+        const uint16_t *kb = k + bg * (int64_t)N * d;
+        if (smooth_k) {
+            for (int c = 0; c < d; ++c) {
+                double s = 0.0;
+                for (int64_t n = 0; n < N; ++n)
+                    s += bf16_to_f64(kb[n * d + c]);
+                st->kmean[bg * d + c] = s / N;
+            }
+        }
+        /* INT8 per 64-token block of K - kmean */
+        for (int64_t t = 0; t < nqb; ++t) {
+            int64_t n0 = t * blk, n1 = n0 + blk < N ? n0 + blk : N;
+            double amax = 0.0;
+            for (int64_t n = n0; n < n1; ++n)
+                for (int c = 0; c < d; ++c) {
+                    double x = bf16_to_f64(kb[n * d + c]) - st->kmean[bg * d + c];
+                    if (fabs(x) > amax)
+                        amax = fabs(x);
+                }
+            double delta = amax > 0.0 ? amax / 127.0 : 1.0;
+            st->kdelta[bg * nqb + t] = delta;
+            for (int64_t n = n0; n < n1; ++n)
+                for (int c = 0; c < d; ++c) {
+                    double x = bf16_to_f64(kb[n * d + c]) - st->kmean[bg * d + c];
+                    st->khat[(bg * N + n) * d + c] = (int8_t)quant_i8(x, delta);
+                }
+        }
+        /* V: per-channel scale over all tokens, E4M3 values */
+        const uint16_t *vb = v + bg * (int64_t)N * d;
+        for (int c = 0; c < d; ++c) {
+            double amax = 0.0;
+            for (int64_t n = 0; n < N; ++n)
+                if (fabs(bf16_to_f64(vb[n * d + c])) > amax)
+                    amax = fabs(bf16_to_f64(vb[n * d + c]));
+            double delta = amax > 0.0 ? amax / 448.0 : 1.0;
+            st->vdelta[bg * d + c] = delta;
+            for (int64_t n = 0; n < N; ++n)
+                st->vq[(bg * N + n) * d + c] = oracle_e4m3_round(bf16_to_f64(vb[n * d + c]) / delta);
+        }
+    }
+    /* INT8 per 64-token block of Q */
+#pragma omp parallel for
+    for (int64_t bh = 0; bh < (int64_t)B * H; ++bh) {
+        const uint16_t *qb = q + bh * (int64_t)N * d;
+        for (int64_t t = 0; t < nqb; ++t) {
+            int64_t n0 = t * blk, n1 = n0 + blk < N ? n0 + blk : N;
+            double amax = 0.0;
+            for (int64_t n = n0; n < n1; ++n)
+                for (int c = 0; c < d; ++c)
+                    if (fabs(bf16_to_f64(qb[n * d + c])) > amax)
+                        amax = fabs(bf16_to_f64(qb[n * d + c]));
+            double delta = amax > 0.0 ? amax / 127.0 : 1.0;
+            st->qdelta[bh * nqb + t] = delta;
+            for (int64_t n = n0; n < n1; ++n)
+                for (int c = 0; c < d; ++c)
+                    st->qhat[(bh * N + n) * d + c] = (int8_t)quant_i8(bf16_to_f64(qb[n * d + c]), delta);
+        }
+    }
+}
+
+static void sage_free(sage_state *st)
+{
+    free(st->kmean);
+    free(st->qhat);
+    free(st->khat);
+    free(st->qdelta);
+    free(st->kdelta);
+    free(st->vq);
+    free(st->vdelta);
+}
+
+/*
+ * Quantised attention for the listed rows, following the recipe's steps in
+ * order:
+ *   1. Smooth-K: K' = K - mean_n K (per channel, all tokens of the kv head);
+ *   2. INT8 Q and K' per 64-token block, delta = max|x| / 127;
+ *   3. V per channel: delta_V = max_n |V| / 448, V^ = E4M3(V / delta_V);
+ *   4. S_ij = scale * dQ(i) * dK(j) * (q^_i . k^_j)   (exact integer dot);
+ *   5. keys in tiles of `tile_n` from key 0 upward, with a running max m:
+ *        m' = max(m, max of the tile's visible scores),
+ *        p_j = exp(S_ij - m'),  l = l * exp(m - m') + sum_j p_j,
+ *        P^_j = E4M3(448 * p_j),
+ *        acc = acc * exp(m - m') + sum_j P^_j V^_j;
+ *   6. O = acc * delta_V / (448 * l);
+ *      lse = m + ln l + scale * (q_i . kmean)  (the true LSE: Smooth-K shifts
+ *      every score of row i by the constant -scale * q_i . kmean).
+ * The static factor 448 puts P in E4M3's full range (P lies in [0, 1]); its
+ * inverse is folded into the final division.  The result depends on tile_n
+ * because P is quantised against the running max.
+ * p_scale: factor applied to p before the E4M3 cast (448 for the recipe);
+ * quant_p = 0 skips P quantisation, quant_v = 0 skips V quantisation (used for
+ * error attributions); quant_qk = 0 uses the unquantised (smoothed) Q and K.
+ */
+double oracle_sage_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                        int B, int H, int Hkv, int N, int d, int causal, double scale,
+                        int blk, int tile_n, int smooth_k, int quant_qk, int quant_p,
+                        int quant_v, double p_scale,
+                        const int64_t *rows, int64_t nrows, double *o, double *lse,
+                        int nthreads)
+{
+    if (B <= 0 || H <= 0 || Hkv <= 0 || H % Hkv != 0 || N <= 0 || d <= 0 || blk <= 0 || tile_n <= 0)
+        return -1.0;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    if (!rows)
+        nrows = (int64_t)B * H * N;
+    sage_state st;
+    sage_prepare(q, k, v, B, H, Hkv, N, d, blk, smooth_k, &st);
+    int64_t nqb = (N + blk - 1) / blk;
+
+#pragma omp parallel
+    {
+        double *S = (double *)malloc(sizeof(double) * (size_t)tile_n);
+        double *acc = (double *)malloc(sizeof(double) * (size_t)d);
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t r = 0; r < nrows; ++r) {
+            int64_t row = rows ? rows[r] : r;
+            int64_t i = row % N, bh = row / N, h = bh % H, b = bh / H;
+            int64_t g = h / (H / Hkv), bg = b * Hkv + g;
+            const int8_t *qh = st.qhat + (bh * N + i) * d;
+            const uint16_t *qraw = q + (bh * N + i) * d;
+            double dq = st.qdelta[bh * nqb + i / blk];
+            int64_t nvis = causal ? i + 1 : N;
+            double m = -INFINITY, l = 0.0;
+            for (int c = 0; c < d; ++c)
+                acc[c] = 0.0;
+            for (int64_t j0 = 0; j0 < nvis; j0 += tile_n) {
+                int64_t j1 = j0 + tile_n < nvis ? j0 + tile_n : nvis;
+                double tmax = -INFINITY;
+                for (int64_t j = j0; j < j1; ++j) {
+                    double sc;
+                    if (quant_qk) {
+                        const int8_t *kh = st.khat + (bg * N + j) * d;
+                        int64_t dot = 0;
+                        for (int c = 0; c < d; ++c)
+                            dot += (int64_t)qh[c] * kh[c];
+                        sc = scale * dq * st.kdelta[bg * nqb + j / blk] * (double)dot;
+                    } else {
+                        const uint16_t *kr = k + (bg * N + j) * d;
+                        double dot = 0.0;
+                        for (int c = 0; c < d; ++c)
+                            dot += bf16_to_f64(qraw[c]) * (bf16_to_f64(kr[c]) - st.kmean[bg * d + c]);
+                        sc = scale * dot;
+                    }
+                    S[j - j0] = sc;
+                    if (sc > tmax)
+                        tmax = sc;
+                }
+                double mnew = tmax > m ? tmax : m;
+                double alpha = exp(m - mnew); /* exp(-inf) = 0 on the first tile */
+                l *= alpha;
+                for (int c = 0; c < d; ++c)
+                    acc[c] *= alpha;
+                for (int64_t j = j0; j < j1; ++j) {
+                    double p = exp(S[j - j0] - mnew);
+                    l += p;
+                    double ph = quant_p ? oracle_e4m3_round(p_scale * p) : p_scale * p;
+                    const double *vj = st.vq + (bg * N + j) * d;
+                    const uint16_t *vr = v + (bg * N + j) * d;
+                    for (int c = 0; c < d; ++c) {
+                        double vv = quant_v ? vj[c] : bf16_to_f64(vr[c]) / st.vdelta[bg * d + c];
+                        acc[c] += ph * vv;
+                    }
+                }
+                m = mnew;
+            }
+            double qk = 0.0;
+            for (int c = 0; c < d; ++c)
+                qk += bf16_to_f64(qraw[c]) * st.kmean[bg * d + c];
+            for (int c = 0; c < d; ++c)
+                o[r * d + c] = acc[c] * st.vdelta[bg * d + c] / (p_scale * l);
+            lse[r] = m + log(l) + scale * qk;
+        }
+        free(S);
+        free(acc);
+    }
+    sage_free(&st);
+    return 0.0;
+}
+
+/*
+ * Expose the quantisation state for tests of the individual steps:
+ * kmean [B,Hkv,d], qhat [B,H,N,d], qdelta [B,H,nblk], khat [B,Hkv,N,d],
+ * kdelta [B,Hkv,nblk], vq [B,Hkv,N,d] (decoded E4M3 of V/delta_V),
+ * vdelta [B,Hkv,d].  Any output pointer may be NULL.
+ */
+int oracle_sage_quantise(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                         int B, int H, int Hkv, int N, int d, int blk, int smooth_k,
+                         double *kmean, int8_t *qhat, double *qdelta, int8_t *khat,
+                         double *kdelta, double *vq, double *vdelta)
+{
+    if (B <= 0 || H <= 0 || Hkv <= 0 || H % Hkv != 0 || N <= 0 || d <= 0 || blk <= 0)
+        return -1;
+    sage_state st;
+    sage_prepare(q, k, v, B, H, Hkv, N, d, blk, smooth_k, &st);
+    int64_t nqb = (N + blk - 1) / blk;
+    if (kmean)
+        memcpy(kmean, st.kmean, sizeof(double) * (size_t)B * Hkv * d);
+    if (qhat)
+        memcpy(qhat, st.qhat, (size_t)B * H * N * d);
+    if (qdelta)
+        memcpy(qdelta, st.qdelta, sizeof(double) * (size_t)B * H * nqb);
+    if (khat)
+        memcpy(khat, st.khat, (size_t)B * Hkv * N * d);
+    if (kdelta)
+        memcpy(kdelta, st.kdelta, sizeof(double) * (size_t)B * Hkv * nqb);
+    if (vq)
+        memcpy(vq, st.vq, sizeof(double) * (size_t)B * Hkv * N * d);
+    if (vdelta)
+        memcpy(vdelta, st.vdelta, sizeof(double) * (size_t)B * Hkv * d);
+    sage_free(&st);
+    return 0;
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
