@@ -1,0 +1,234 @@
+"""Benchmark of the fused attention forward on one MI355X.
+
+One step is one call of the library on the headline workload (exact bf16
+causal prefill, B=4 H=32 N=4096 d=128), with inputs resident in HBM.  W
+untimed warm-up steps, then K timed steps between two events on the launch
+stream (torch's current stream), synchronised on both sides.  The library's
+own per-kernel HIP events (attn_profiler_*) time the dominant kernel inside
+the same timed region for the roofline figure.
+
+The same JSON line also carries the split-KV decode workload (HBM bound,
+GB/s) and, when built, the quantised prefill workload, each with its own
+roofline object, and the fp64 CPU oracle timed on a bounded sample of the
+headline workload.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                  [--only prefill|decode|sage] [--calibrate-copy]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+import workloads  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_FP8_TFLOPS = 5033.2    # fp8 / int8 dense
+PEAK_HBM_GBS = 8000.0       # HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+CSRC = os.path.join(ROOT, "softmax_attention_attn_amd", "csrc")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, files):
+    """HBM bytes per launch from the committed counter runs, or None when the
+    kernel sources changed since the counters were taken."""
+    try:
+        data = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    ent = data.get(kernel)
+    if not ent or ent.get("source_hash") != kernel_source_hash(files):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def time_calls(fn, steps, warmup, stream):
+    import softmax_attention_attn_amd as A
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    A.attn_profiler_enable(True)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    kern = A.attn_profiler_read()
+    A.attn_profiler_enable(False)
+    per_kernel = {k: (t / n if n else 0.0, n) for k, (t, n) in kern.items()}
+    return total_ms / steps, per_kernel
+
+
+def bench_prefill(args, stream):
+    import softmax_attention_attn_amd as A
+    w = workloads.WORKLOADS["llm_prefill"]
+    inp = workloads.make(w)
+    q, k, v = inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda()
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+
+    def step():
+        A.fwd(q, k, v, causal=w.causal, o=o, lse=lse, stream=stream)
+
+    ms, per_kernel = time_calls(step, args.steps, args.warmup, stream)
+    flops = w.flops()
+    kms = per_kernel["prefill_exact"][0]
+    achieved = flops / (kms * 1e-3) / 1e12
+    res = {
+        "workload": w, "ms_per_step": ms, "value": flops / (ms * 1e-3) / 1e12,
+        "roofline": {"bound": "mfma", "kernel": "prefill_exact", "achieved": achieved,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS,
+                     "kernel_ms": kms,
+                     "traffic": measured_traffic("prefill_exact",
+                                                 ["prefill_exact.hip", "cdna4.hpp"])},
+        "inputs": (inp["q"], inp["k"], inp["v"]),
+    }
+    return res
+
+
+def bench_decode(args, stream):
+    import softmax_attention_attn_amd as A
+    w = workloads.WORKLOADS["gqa_decode"]
+    inp = workloads.make(w)
+    q, k, v = inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda()
+    seqlens = inp["seqlens"].cuda()
+    sum_len = int(inp["seqlens"].sum())
+    del inp
+    o = torch.empty((w.B, w.H, w.d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.B, w.H), dtype=torch.float32, device="cuda")
+    ws = torch.empty((A.attn_decode_workspace_size(w.B, w.H, w.N, w.d, w.split_tokens),),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        A.decode(q, k, v, seqlens, split_tokens=w.split_tokens, o=o, lse=lse, workspace=ws,
+                 stream=stream)
+
+    ms, per_kernel = time_calls(step, max(args.steps, 20), args.warmup, stream)
+    # algorithmic bytes: every valid K and V row once, q, o (bf16) and lse (fp32)
+    alg_bytes = sum_len * w.Hkv * w.d * 2 * 2 + w.B * w.H * w.d * 2 * 2 + w.B * w.H * 4
+    kms = per_kernel["decode_split"][0]
+    achieved = alg_bytes / (kms * 1e-3) / 1e9
+    return {
+        "workload": w.name, "value": alg_bytes / (ms * 1e-3) / 1e9, "unit": "GB/s",
+        "ms_per_step": ms, "sum_seqlen": sum_len, "algorithmic_bytes": alg_bytes,
+        "kernels_ms": {k_: t for k_, (t, _) in per_kernel.items()},
+        "roofline": {"bound": "hbm", "kernel": "decode_split", "achieved": achieved,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                     "kernel_ms": kms,
+                     "traffic": measured_traffic("decode_split", ["decode.hip", "cdna4.hpp"])},
+    }
+
+
+def cpu_baseline(w, q, k, v):
+    """fp64 oracle on every 4th query row of every (b, h) slice of the
+    headline workload; its throughput in the headline's unit."""
+    import oracle
+    oracle.build(force=False)
+    rows = np.arange(0, w.B * w.H * w.N, 4, dtype=np.int64)
+    i = rows % w.N
+    flops = float(np.sum(4.0 * w.d * (i + 1 if w.causal else w.N)))
+    threads = oracle.default_threads()
+    qb, kb, vb = (workloads.bf16_bits(t) for t in (q, k, v))
+    t0 = time.perf_counter()
+    oracle.attn_rows(qb, kb, vb, causal=w.causal, scale=w.scale, rows=rows, threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "fp64 C oracle, every 4th query row of all %d (b,h) slices of %s "
+                      "(%d rows, %.3g FLOP) in %.1f s" % (w.B * w.H, w.name, len(rows), flops, dt)}
+
+
+def calibrate_copy():
+    """A plain device-to-device copy of a known size, for scaling the
+    FETCH_SIZE / WRITE_SIZE counters of a rocprofv3 --pmc run."""
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": nbytes, "launches": 3}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode", "sage"], default=None)
+    ap.add_argument("--calibrate-copy", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(requested --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    stream = torch.cuda.current_stream()
+    out = {}
+    pre = None
+    if args.only in (None, "prefill"):
+        log("prefill: llm_prefill")
+        pre = bench_prefill(args, stream)
+        log("prefill %.3f ms/step, %.1f TFLOP/s" % (pre["ms_per_step"], pre["value"]))
+    if args.only in (None, "decode"):
+        log("decode: gqa_decode")
+        dec = bench_decode(args, stream)
+        log("decode %.3f ms/step, %.1f GB/s" % (dec["ms_per_step"], dec["value"]))
+        out["decode"] = dec
+        torch.cuda.empty_cache()
+    if pre is None:
+        print(json.dumps(out))
+        return
+    w = pre["workload"]
+    line = {
+        "metric": "attn fwd TFLOPS & % MFMA peak (prefill); decode HBM GB/s & % peak",
+        "value": round(pre["value"], 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(pre["ms_per_step"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.Hkv, "N": w.N, "d": w.d,
+                   "causal": w.causal, "out": "bf16 O + fp32 LSE"},
+        "roofline": pre["roofline"],
+    }
+    line.update(out)
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        line["cpu_baseline"] = cpu_baseline(w, *pre["inputs"])
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,153 @@
+/*
+ * attn.h — C ABI of the MI355X (gfx950) fused softmax-attention library.
+ *
+ * The library computes the attention forward pass
+ *     O = softmax(Q K^T * scale + mask) V,   lse_i = ln sum_j exp(S_ij)
+ * without ever writing the score matrix to memory: Q tiles stay in registers,
+ * K/V tiles stream through LDS, and an online softmax (running row max and
+ * row sum, rescaled per tile) keeps the result exact.  Sources:
+ *   - "flashattention-kernels" page (cyk1337 paper-daily), §0 and §1: the
+ *     tiling + online-softmax dataflow and the parallel work partitioning of
+ *     the FlashAttention line; §3: Flash-Decoding (split the KV sequence,
+ *     compute partial attention per chunk, reduce) for one-token decode, and
+ *     an engine-style interface covering GQA/MQA and prefill/decode;
+ *   - "cuda-kernel-pretrain" page (cyk1337 paper-daily), §2 and §3: IO-aware
+ *     exact attention; GQA/MQA share one K/V head per group of query heads;
+ *     the practice list asks that a low-precision path state its scale
+ *     granularity and accumulation precision as part of its contract;
+ *   - "GPU kernel overview" page (zhaifeiyue.github.io), SageAttention chain
+ *     and the INT-for-QK / FP-for-PV insight: Smooth-K, per-block INT8 Q/K,
+ *     FP8 (E4M3) P and V.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or synchronises inside a call (scratch memory is
+ *     the caller's `workspace`, sized by the *_workspace_size functions).
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream).  Inputs must stay valid until the work on `stream` completes.
+ *   - Layouts are dense row-major (C order):
+ *       q [B, H, N, d],  k and v [B, Hkv, N, d],  o [B, H, N, d],  lse [B, H, N].
+ *     Query head h reads kv head h / (H / Hkv) (consecutive groups; H % Hkv == 0;
+ *     Hkv == H is plain multi-head attention, Hkv == 1 is MQA).
+ *   - q, k, v are bf16.  o is bf16 or fp32 (o_dtype).  lse is fp32, natural log,
+ *     over the scaled and masked scores; lse may be NULL (not written).
+ *   - causal != 0 applies the top-left aligned mask: key j is visible to query
+ *     i iff j <= i.
+ *   - Every argument is validated before any HIP call: an invalid call returns
+ *     an error status and launches nothing.  A failed launch returns
+ *     ATTN_ERR_HIP.  No C++ exception crosses this interface.
+ *     attn_last_error() gives a human-readable reason for the last failure on
+ *     the calling thread.
+ */
+#ifndef MI355X_ATTN_H
+#define MI355X_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, H % Hkv != 0, bad scale */
+    ATTN_ERR_UNSUPPORTED = -2, /* valid but not implemented (e.g. d not in {64, 128}) */
+    ATTN_ERR_WORKSPACE = -3,   /* workspace missing or smaller than *_workspace_size */
+    ATTN_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
+} attn_status;
+
+typedef enum {
+    /* bf16 inputs, bf16 MFMA for QK^T and PV, fp32 accumulation and softmax. */
+    ATTN_MODE_EXACT_BF16 = 0,
+    /* SageAttention-style quantised mode ("GPU kernel overview" page, Sage
+     * chain): Smooth-K (K minus its per-channel mean over all N tokens of the
+     * kv head, in fp32); Q and K' quantised to symmetric INT8 per block of 64
+     * consecutive tokens of one (batch, head) with scale max|x|/127; S from an
+     * INT8 MFMA with exact int32 accumulation; P quantised to OCP E4M3 as
+     * E4M3(448 * exp(S - m_running)); V quantised to E4M3 per (batch, kv head,
+     * channel) with scale max|V|/448; PV by an FP8 MFMA with fp32
+     * accumulation.  lse is the true LSE (the Smooth-K shift q_i . kmean is
+     * added back).  Needs a workspace. */
+    ATTN_MODE_SAGE_QK_I8_BLK64_PV_FP8_E4M3 = 1
+} attn_mode;
+
+typedef enum { ATTN_OUT_BF16 = 0, ATTN_OUT_FP32 = 1 } attn_dtype;
+
+/*
+ * Attention forward pass (prefill: N queries against the same N keys).
+ *   q, k, v    device inputs (bf16), layouts above.
+ *   o          device output, [B, H, N, d], dtype o_dtype.
+ *   lse        device output fp32 [B, H, N], or NULL.
+ *   B, H, Hkv, N, d   sizes; d must be 64 or 128; N >= 1.
+ *   causal     0 = no mask, else the top-left causal mask.
+ *   scale      multiplier of Q K^T (finite, > 0); usually 1/sqrt(d).
+ *   mode       attn_mode.
+ *   o_dtype    attn_dtype.
+ *   workspace  device scratch of at least attn_fwd_workspace_size() bytes
+ *              (may be NULL when that size is 0).  Its content on entry is
+ *              irrelevant; it is overwritten.
+ */
+attn_status attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+                     int B, int H, int Hkv, int N, int d, int causal, float scale,
+                     int mode, int o_dtype, void *workspace, size_t workspace_bytes,
+                     void *stream);
+
+/* Bytes of workspace attn_fwd needs for these sizes and mode (0 for the exact
+ * mode).  Returns 0 for invalid sizes as well; attn_fwd then reports the error. */
+size_t attn_fwd_workspace_size(int B, int H, int Hkv, int N, int d, int mode);
+
+/*
+ * One-token decode against per-sequence KV caches with split-KV
+ * (Flash-Decoding, "flashattention-kernels" page §3): the valid keys
+ * [0, seqlens[b]) of each sequence are cut into chunks of split_tokens keys,
+ * each chunk's partial attention (O_s, lse_s) is computed in parallel, and the
+ * partials are merged by log-sum-exp weights:
+ *     M = max_s lse_s,  w_s = exp(lse_s - M),
+ *     O = sum_s w_s O_s / sum_s w_s,  lse = M + ln sum_s w_s.
+ * The single query of sequence b sits at position seqlens[b] - 1 and sees every
+ * valid key, so there is no causal argument.
+ *   q          device bf16 [B, H, d].
+ *   k_cache, v_cache   device bf16 [B, Hkv, N_max, d]; rows >= seqlens[b] are
+ *              never read.
+ *   seqlens    device int32 [B]; each value must lie in [1, N_max] (values
+ *              outside are clamped to that range by the kernels).
+ *   o          device output [B, H, d], dtype o_dtype.
+ *   lse        device fp32 [B, H] or NULL.
+ *   mode       only ATTN_MODE_EXACT_BF16 (others return ATTN_ERR_UNSUPPORTED).
+ *   split_tokens   chunk length; a positive multiple of 64.
+ *   workspace  at least attn_decode_workspace_size() bytes: fp32 partial
+ *              outputs and LSEs of every (b, h, chunk).
+ */
+attn_status attn_decode(const void *q, const void *k_cache, const void *v_cache,
+                        const int32_t *seqlens, void *o, float *lse, int B, int H, int Hkv,
+                        int N_max, int d, float scale, int mode, int o_dtype,
+                        int split_tokens, void *workspace, size_t workspace_bytes,
+                        void *stream);
+
+/* Bytes of workspace attn_decode needs (0 for invalid sizes). */
+size_t attn_decode_workspace_size(int B, int H, int N_max, int d, int split_tokens);
+
+/* Static description of a status code. */
+const char *attn_status_string(int status);
+
+/* Detailed message of the last failed call on the calling thread ("" if none). */
+const char *attn_last_error(void);
+
+/*
+ * Kernel timing hooks for benchmarks.  While enabled, every kernel the library
+ * launches on the calling thread is bracketed by a pair of HIP events recorded
+ * on the launch stream.  attn_profiler_read() waits for those events, adds each
+ * launch's elapsed time to a per-kernel-name total, and clears the record.
+ * For i < returned count: names + i*name_stride holds the kernel name
+ * (NUL-terminated, truncated to name_stride - 1 chars), total_ms[i] the summed
+ * time and launches[i] the number of launches.  Returns the number of distinct
+ * kernels (at most cap) or a negative attn_status.
+ */
+attn_status attn_profiler_enable(int enable);
+int attn_profiler_read(char *names, int name_stride, double *total_ms, int *launches, int cap);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MI355X_ATTN_H */

@@ -1,0 +1,224 @@
+"""Python binding of the MI355X fused-attention library (``libattn.so``).
+
+This module only marshals arguments: it checks torch tensors (device, dtype,
+shape, contiguity), allocates outputs and workspaces with torch when the
+caller does not pass them, and calls the C ABI of ``include/attn.h`` through
+ctypes on torch's current HIP stream.  Every step of the computation runs in
+the library's HIP kernels; there is no fallback.  Importing this package
+fails loudly when the library has not been built.
+
+The functions carry the C names (``attn_fwd``, ``attn_decode``, ...); the
+convenience wrappers ``fwd`` and ``decode`` allocate what the caller omits.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch  # loaded first so that the library binds to torch's HIP runtime
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn.so")
+
+ATTN_OK = 0
+ATTN_ERR_INVALID_ARG = -1
+ATTN_ERR_UNSUPPORTED = -2
+ATTN_ERR_WORKSPACE = -3
+ATTN_ERR_HIP = -4
+
+ATTN_MODE_EXACT_BF16 = 0
+ATTN_MODE_SAGE_QK_I8_BLK64_PV_FP8_E4M3 = 1
+ATTN_OUT_BF16 = 0
+ATTN_OUT_FP32 = 1
+
+MODES = {"exact": ATTN_MODE_EXACT_BF16, "sage": ATTN_MODE_SAGE_QK_I8_BLK64_PV_FP8_E4M3}
+
+EXPORTS = ("attn_fwd", "attn_fwd_workspace_size", "attn_decode", "attn_decode_workspace_size",
+           "attn_status_string", "attn_last_error", "attn_profiler_enable",
+           "attn_profiler_read")
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s (status %d): %s" % (_status_name(status), status, message))
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libattn.so is not built (%s); run __graft_entry__.build() or "
+                          "python softmax_attention_attn_amd/_build.py" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.attn_fwd.restype = i
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, sz, vp]
+    lib.attn_fwd_workspace_size.restype = sz
+    lib.attn_fwd_workspace_size.argtypes = [i, i, i, i, i, i]
+    lib.attn_decode.restype = i
+    lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, sz, vp]
+    lib.attn_decode_workspace_size.restype = sz
+    lib.attn_decode_workspace_size.argtypes = [i, i, i, i, i]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_status_string.argtypes = [i]
+    lib.attn_last_error.restype = ctypes.c_char_p
+    lib.attn_last_error.argtypes = []
+    lib.attn_profiler_enable.restype = i
+    lib.attn_profiler_enable.argtypes = [i]
+    lib.attn_profiler_read.restype = i
+    lib.attn_profiler_read.argtypes = [ctypes.c_char_p, i, ctypes.POINTER(ctypes.c_double),
+                                       ctypes.POINTER(ctypes.c_int), i]
+    return lib
+
+
+_lib = _load()
+
+
+def _status_name(status: int) -> str:
+    return _lib.attn_status_string(int(status)).decode()
+
+
+def attn_status_string(status: int) -> str:
+    return _status_name(status)
+
+
+def attn_last_error() -> str:
+    return _lib.attn_last_error().decode()
+
+
+def _check(status: int):
+    if status != ATTN_OK:
+        raise AttnError(status, attn_last_error())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+# ----------------------------------------------------------------- raw C ABI
+
+def attn_fwd_workspace_size(B, H, Hkv, N, d, mode) -> int:
+    return int(_lib.attn_fwd_workspace_size(B, H, Hkv, N, d, mode))
+
+
+def attn_decode_workspace_size(B, H, N_max, d, split_tokens) -> int:
+    return int(_lib.attn_decode_workspace_size(B, H, N_max, d, split_tokens))
+
+
+def attn_fwd(q, k, v, o, lse, B, H, Hkv, N, d, causal, scale, mode, o_dtype, workspace,
+             workspace_bytes, stream) -> int:
+    """Direct call of the C function with raw pointers (ints or None)."""
+    return int(_lib.attn_fwd(q, k, v, o, lse, B, H, Hkv, N, d, causal, scale, mode, o_dtype,
+                             workspace, workspace_bytes, stream))
+
+
+def attn_decode(q, k_cache, v_cache, seqlens, o, lse, B, H, Hkv, N_max, d, scale, mode,
+                o_dtype, split_tokens, workspace, workspace_bytes, stream) -> int:
+    return int(_lib.attn_decode(q, k_cache, v_cache, seqlens, o, lse, B, H, Hkv, N_max, d,
+                                scale, mode, o_dtype, split_tokens, workspace,
+                                workspace_bytes, stream))
+
+
+def attn_profiler_enable(enable: bool) -> None:
+    _check(_lib.attn_profiler_enable(int(bool(enable))))
+
+
+def attn_profiler_read(cap: int = 16, name_len: int = 64) -> dict:
+    """{kernel name: (total_ms, launches)} since the profiler was enabled/read."""
+    names = ctypes.create_string_buffer(cap * name_len)
+    tot = (ctypes.c_double * cap)()
+    cnt = (ctypes.c_int * cap)()
+    n = _lib.attn_profiler_read(names, name_len, tot, cnt, cap)
+    if n < 0:
+        _check(n)
+    out = {}
+    for j in range(n):
+        nm = names.raw[j * name_len:(j + 1) * name_len].split(b"\0", 1)[0].decode()
+        out[nm] = (tot[j], cnt[j])
+    return out
+
+
+# ----------------------------------------------------------------- tensor API
+
+def _need(t, name, dtype, ndim):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a GPU tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if t.dim() != ndim:
+        raise ValueError("%s must have %d dims, got %s" % (name, ndim, tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, mode: str = "exact",
+        out_dtype=torch.bfloat16, o=None, lse=None, with_lse: bool = True, workspace=None,
+        stream=None):
+    """Attention forward.  q [B,H,N,d], k/v [B,Hkv,N,d] bf16 GPU tensors.
+
+    Returns (o, lse) with o [B,H,N,d] of ``out_dtype`` and lse fp32 [B,H,N]
+    (None when ``with_lse`` is False).
+    """
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(v, "v", torch.bfloat16, 4)
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (B, Hkv, N, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k/v shape %s does not match q %s" % (tuple(k.shape), tuple(q.shape)))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    m = MODES[mode]
+    o_code = {torch.bfloat16: ATTN_OUT_BF16, torch.float32: ATTN_OUT_FP32}[out_dtype]
+    if o is None:
+        o = torch.empty((B, H, N, d), dtype=out_dtype, device=q.device)
+    if lse is None and with_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    ws_bytes = attn_fwd_workspace_size(B, H, Hkv, N, d, m)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=q.device)
+    st = _lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, N, d,
+                       int(bool(causal)), float(scale), m, o_code, _ptr(workspace),
+                       workspace.numel() if workspace is not None else 0, _stream(stream))
+    _check(st)
+    return o, lse
+
+
+def decode(q, k_cache, v_cache, seqlens, *, scale: float | None = None,
+           split_tokens: int = 512, out_dtype=torch.bfloat16, o=None, lse=None,
+           with_lse: bool = True, workspace=None, stream=None):
+    """Split-KV decode.  q [B,H,d]; caches [B,Hkv,N_max,d] bf16; seqlens int32 [B]."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, 4)
+    _need(seqlens, "seqlens", torch.int32, 1)
+    B, H, d = q.shape
+    _, Hkv, N_max, _ = k_cache.shape
+    if tuple(k_cache.shape) != (B, Hkv, N_max, d) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("cache shapes do not match q")
+    if seqlens.shape[0] != B:
+        raise ValueError("seqlens must have B entries")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o_code = {torch.bfloat16: ATTN_OUT_BF16, torch.float32: ATTN_OUT_FP32}[out_dtype]
+    if o is None:
+        o = torch.empty((B, H, d), dtype=out_dtype, device=q.device)
+    if lse is None and with_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    ws_bytes = attn_decode_workspace_size(B, H, N_max, d, split_tokens)
+    if workspace is None:
+        workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=q.device)
+    st = _lib.attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(o),
+                          _ptr(lse), B, H, Hkv, N_max, d, float(scale), ATTN_MODE_EXACT_BF16,
+                          o_code, int(split_tokens), _ptr(workspace), workspace.numel(),
+                          _stream(stream))
+    _check(st)
+    return o, lse

@@ -1,0 +1,270 @@
+// C-ABI layer: argument validation, workspace sizing, kernel dispatch and
+// the benchmark timing hooks.  Every check runs before any HIP call, so an
+// invalid call launches nothing (and can be tested without a GPU).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/attn.h"
+#include "attn_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+attn_status fail(attn_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+attn_status fail(attn_status st, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+attn_status ok()
+{
+    g_last_error.clear();
+    return ATTN_OK;
+}
+
+attn_status from_hip(hipError_t e, const char *what)
+{
+    if (e == hipSuccess)
+        return ok();
+    return fail(ATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool valid_scale(float s) { return std::isfinite(s) && s > 0.f; }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ---------------------------------------------------------------- profiler
+struct ProfEvent {
+    std::string name;
+    hipEvent_t begin, end;
+};
+thread_local bool g_prof_on = false;
+thread_local std::vector<ProfEvent> g_prof;
+
+}  // namespace
+
+namespace attn {
+
+void prof_begin(const char *name, hipStream_t s)
+{
+    if (!g_prof_on)
+        return;
+    ProfEvent ev{name, nullptr, nullptr};
+    if (hipEventCreate(&ev.begin) != hipSuccess || hipEventCreate(&ev.end) != hipSuccess)
+        return;
+    hipEventRecord(ev.begin, s);
+    g_prof.push_back(ev);
+}
+
+void prof_end(hipStream_t s)
+{
+    if (!g_prof_on || g_prof.empty())
+        return;
+    hipEventRecord(g_prof.back().end, s);
+}
+
+}  // namespace attn
+
+extern "C" {
+
+const char *attn_status_string(int status)
+{
+    switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID_ARG: return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case ATTN_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+const char *attn_last_error(void) { return g_last_error.c_str(); }
+
+size_t attn_fwd_workspace_size(int B, int H, int Hkv, int N, int d, int mode)
+{
+    if (B <= 0 || H <= 0 || Hkv <= 0 || N <= 0 || d <= 0 || H % Hkv != 0)
+        return 0;
+    if (mode == ATTN_MODE_SAGE_QK_I8_BLK64_PV_FP8_E4M3)
+        return attn::sage_workspace_bytes(B, H, Hkv, N, d);
+    return 0;
+}
+
+attn_status attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                     int H, int Hkv, int N, int d, int causal, float scale, int mode,
+                     int o_dtype, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!q || !k || !v || !o)
+        return fail(ATTN_ERR_INVALID_ARG, "q, k, v and o must be non-null device pointers");
+    if (B <= 0 || H <= 0 || Hkv <= 0 || N <= 0 || d <= 0)
+        return fail(ATTN_ERR_INVALID_ARG, "sizes must be positive (B=%d H=%d Hkv=%d N=%d d=%d)",
+                    B, H, Hkv, N, d);
+    if (H % Hkv != 0)
+        return fail(ATTN_ERR_INVALID_ARG, "H=%d is not a multiple of Hkv=%d", H, Hkv);
+    if (!valid_scale(scale))
+        return fail(ATTN_ERR_INVALID_ARG, "scale must be finite and > 0");
+    if (o_dtype != ATTN_OUT_BF16 && o_dtype != ATTN_OUT_FP32)
+        return fail(ATTN_ERR_INVALID_ARG, "unknown output dtype %d", o_dtype);
+    if (mode != ATTN_MODE_EXACT_BF16 && mode != ATTN_MODE_SAGE_QK_I8_BLK64_PV_FP8_E4M3)
+        return fail(ATTN_ERR_INVALID_ARG, "unknown mode %d", mode);
+    if (d != 64 && d != 128)
+        return fail(ATTN_ERR_UNSUPPORTED, "head dim d=%d (supported: 64, 128)", d);
+    if ((long long)B * H > 0x7fffffffLL || (long long)N > (1LL << 24))
+        return fail(ATTN_ERR_UNSUPPORTED, "problem too large for the grid mapping");
+    const size_t need = attn_fwd_workspace_size(B, H, Hkv, N, d, mode);
+    if (need && (!workspace || workspace_bytes < need))
+        return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+
+    attn::PrefillArgs a{q, k, v, o, lse, B, H, Hkv, N, d, causal != 0, scale,
+                        o_dtype == ATTN_OUT_FP32};
+    hipStream_t s = (hipStream_t)stream;
+    if (mode == ATTN_MODE_EXACT_BF16)
+        return from_hip(attn::launch_prefill_exact(a, s), "prefill launch");
+    attn::SageArgs sa{a, workspace, workspace_bytes};
+    return from_hip(attn::launch_sage(sa, s), "sage launch");
+}
+
+size_t attn_decode_workspace_size(int B, int H, int N_max, int d, int split_tokens)
+{
+    if (B <= 0 || H <= 0 || N_max <= 0 || d <= 0 || split_tokens <= 0)
+        return 0;
+    const size_t splits = ((size_t)N_max + split_tokens - 1) / split_tokens;
+    const size_t o_bytes = align_up(sizeof(float) * (size_t)B * H * splits * d, 256);
+    const size_t l_bytes = align_up(sizeof(float) * (size_t)B * H * splits, 256);
+    return o_bytes + l_bytes;
+}
+
+attn_status attn_decode(const void *q, const void *k_cache, const void *v_cache,
+                        const int32_t *seqlens, void *o, float *lse, int B, int H, int Hkv,
+                        int N_max, int d, float scale, int mode, int o_dtype, int split_tokens,
+                        void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!q || !k_cache || !v_cache || !seqlens || !o)
+        return fail(ATTN_ERR_INVALID_ARG,
+                    "q, k_cache, v_cache, seqlens and o must be non-null device pointers");
+    if (B <= 0 || H <= 0 || Hkv <= 0 || N_max <= 0 || d <= 0)
+        return fail(ATTN_ERR_INVALID_ARG, "sizes must be positive (B=%d H=%d Hkv=%d N_max=%d d=%d)",
+                    B, H, Hkv, N_max, d);
+    if (H % Hkv != 0)
+        return fail(ATTN_ERR_INVALID_ARG, "H=%d is not a multiple of Hkv=%d", H, Hkv);
+    if (!valid_scale(scale))
+        return fail(ATTN_ERR_INVALID_ARG, "scale must be finite and > 0");
+    if (o_dtype != ATTN_OUT_BF16 && o_dtype != ATTN_OUT_FP32)
+        return fail(ATTN_ERR_INVALID_ARG, "unknown output dtype %d", o_dtype);
+    if (split_tokens <= 0 || split_tokens % 64 != 0)
+        return fail(ATTN_ERR_INVALID_ARG, "split_tokens=%d must be a positive multiple of 64",
+                    split_tokens);
+    if (mode != ATTN_MODE_EXACT_BF16)
+        return fail(mode == ATTN_MODE_SAGE_QK_I8_BLK64_PV_FP8_E4M3 ? ATTN_ERR_UNSUPPORTED
+                                                                   : ATTN_ERR_INVALID_ARG,
+                    "decode supports only the exact bf16 mode (mode=%d)", mode);
+    if (d != 64 && d != 128)
+        return fail(ATTN_ERR_UNSUPPORTED, "head dim d=%d (supported: 64, 128)", d);
+    const int G = H / Hkv;
+    if (G != 1 && G != 2 && G != 4 && G != 8)
+        return fail(ATTN_ERR_UNSUPPORTED, "query heads per kv head %d (supported: 1, 2, 4, 8)", G);
+    if ((long long)G * split_tokens > 4096)
+        return fail(ATTN_ERR_UNSUPPORTED,
+                    "split_tokens=%d too large for %d heads per kv head (G*split <= 4096)",
+                    split_tokens, G);
+    const long long splits = ((long long)N_max + split_tokens - 1) / split_tokens;
+    if (splits > 0x7fffffffLL || Hkv > 65535 || B > 65535)
+        return fail(ATTN_ERR_UNSUPPORTED, "problem too large for the grid mapping");
+    const size_t need = attn_decode_workspace_size(B, H, N_max, d, split_tokens);
+    if (!workspace || workspace_bytes < need)
+        return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+
+    attn::DecodeArgs a{};
+    a.q = q;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.seqlens = seqlens;
+    a.o = o;
+    a.lse = lse;
+    a.B = B;
+    a.H = H;
+    a.Hkv = Hkv;
+    a.N_max = N_max;
+    a.d = d;
+    a.scale = scale;
+    a.out_fp32 = o_dtype == ATTN_OUT_FP32;
+    a.split_tokens = split_tokens;
+    a.max_splits = (int)splits;
+    a.part_o = (float *)workspace;
+    a.part_lse = (float *)((char *)workspace +
+                           align_up(sizeof(float) * (size_t)B * H * splits * d, 256));
+    return from_hip(attn::launch_decode(a, (hipStream_t)stream), "decode launch");
+}
+
+attn_status attn_profiler_enable(int enable)
+{
+    for (auto &ev : g_prof) {
+        hipEventDestroy(ev.begin);
+        hipEventDestroy(ev.end);
+    }
+    g_prof.clear();
+    g_prof_on = enable != 0;
+    return ok();
+}
+
+int attn_profiler_read(char *names, int name_stride, double *total_ms, int *launches, int cap)
+{
+    if (!names || !total_ms || !launches || name_stride <= 1 || cap <= 0)
+        return fail(ATTN_ERR_INVALID_ARG, "profiler_read: bad output buffers");
+    std::vector<std::string> seen;
+    std::vector<double> tot;
+    std::vector<int> cnt;
+    attn_status st = ATTN_OK;
+    for (auto &ev : g_prof) {
+        float ms = 0.f;
+        hipError_t e = hipEventSynchronize(ev.end);
+        if (e == hipSuccess)
+            e = hipEventElapsedTime(&ms, ev.begin, ev.end);
+        if (e != hipSuccess) {
+            st = fail(ATTN_ERR_HIP, "profiler_read: %s", hipGetErrorString(e));
+            break;
+        }
+        size_t i = 0;
+        while (i < seen.size() && seen[i] != ev.name)
+            ++i;
+        if (i == seen.size()) {
+            seen.push_back(ev.name);
+            tot.push_back(0.0);
+            cnt.push_back(0);
+        }
+        tot[i] += ms;
+        cnt[i] += 1;
+    }
+    for (auto &ev : g_prof) {
+        hipEventDestroy(ev.begin);
+        hipEventDestroy(ev.end);
+    }
+    g_prof.clear();
+    if (st != ATTN_OK)
+        return st;
+    int n = (int)seen.size() < cap ? (int)seen.size() : cap;
+    for (int i = 0; i < n; ++i) {
+        std::snprintf(names + (size_t)i * name_stride, name_stride, "%s", seen[i].c_str());
+        total_ms[i] = tot[i];
+        launches[i] = cnt[i];
+    }
+    ok();
+    return n;
+}
+
+}  // extern "C"

@@ -1,0 +1,59 @@
+// Internal interface between the C-ABI layer (api.cpp) and the HIP kernels.
+// Not installed; the public contract is include/attn.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn {
+
+struct PrefillArgs {
+    const void *q, *k, *v;
+    void *o;
+    float *lse;  // may be null
+    int B, H, Hkv, N, d;
+    int causal;
+    float scale;
+    int out_fp32;  // 0: bf16 output, 1: fp32 output
+};
+
+struct DecodeArgs {
+    const void *q, *k, *v;
+    const int32_t *seqlens;
+    void *o;
+    float *lse;  // may be null
+    int B, H, Hkv, N_max, d;
+    float scale;
+    int out_fp32;
+    int split_tokens;
+    int max_splits;   // ceil(N_max / split_tokens)
+    float *part_o;    // [B, H, max_splits, d]
+    float *part_lse;  // [B, H, max_splits]
+};
+
+struct SageArgs {
+    PrefillArgs p;
+    void *workspace;
+    size_t workspace_bytes;
+};
+
+// Kernel launchers (defined in the .hip files).  They assume validated
+// arguments and return the launch status.
+hipError_t launch_prefill_exact(const PrefillArgs &a, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_sage(const SageArgs &a, hipStream_t s);
+size_t sage_workspace_bytes(int B, int H, int Hkv, int N, int d);
+
+// Benchmark timing hooks (api.cpp): bracket one kernel launch with events when
+// the profiler is enabled on this thread.
+void prof_begin(const char *name, hipStream_t s);
+void prof_end(hipStream_t s);
+
+struct ProfScope {
+    hipStream_t s;
+    ProfScope(const char *name, hipStream_t st) : s(st) { prof_begin(name, s); }
+    ~ProfScope() { prof_end(s); }
+};
+
+}  // namespace attn

@@ -1,0 +1,73 @@
+// Device primitives for gfx950 (CDNA4): vector types, MFMA wrappers,
+// conversions and lane exchanges used by the attention kernels.
+//
+// MFMA register layouts relied on (wave64, 32x32 output tiles):
+//  * v_mfma_f32_32x32x16_bf16  D[32x32] += A[32x16] * B[16x32]
+//      A: lane l holds 8 bf16 of row (l % 32); B: lane l holds 8 bf16 of
+//      column (l % 32).  Element i of lane l in A multiplies element i of lane
+//      (l' with the same l / 32) in B: the contraction index is a function of
+//      (l / 32, i) that is the same for A and B, so any consistent assignment
+//      of K-indices to (l / 32, i) gives the same product.
+//      D: lane l, register r holds row 8*(r/4) + 4*(l/32) + (r%4), column l%32.
+//  * v_mfma_i32_32x32x32_i8 and v_mfma_scale_f32_32x32x64_f8f6f4 (fp8) use
+//    the same row/column/output layout with 16 and 32 8-bit values per lane.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma_bf16_32x32x16(bf16x8 a, bf16x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ i32x16 mfma_i8_32x32x32(i32x4 a, i32x4 b, i32x16 c)
+{
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+
+// FP8 (E4M3, format code 0 for both operands) with unit block scales
+// (E8M0 exponent 127 == 2^0).
+__device__ __forceinline__ f32x16 mfma_fp8_32x32x64(i32x8 a, i32x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+// Round-to-nearest-even fp32 -> bf16, two values packed low/high.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// v_exp_f32: 2^x (exp2(-inf) == 0).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Value held by the lane 32 positions away (lanes l and l ^ 32 exchange).
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+// Global loads/stores of 16 bytes.
+__device__ __forceinline__ u32x4 ld16(const void *p) { return *(const u32x4 *)p; }
+__device__ __forceinline__ void st16(void *p, u32x4 v) { *(u32x4 *)p = v; }
+
+}  // namespace attn

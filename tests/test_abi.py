@@ -1,0 +1,100 @@
+"""The C-ABI library loads, exports every entry point that include/attn.h
+declares, and rejects invalid arguments before touching the GPU (these calls
+pass dummy non-null pointers: validation must fail before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def A():
+    import softmax_attention_attn_amd as A
+    return A
+
+
+def test_header_declares_expected(A):
+    assert set(_declared()) == set(A.EXPORTS)
+
+
+def test_library_exports_every_symbol(A):
+    lib = ctypes.CDLL(A.LIB_PATH)
+    for name in _declared():
+        assert hasattr(lib, name), name
+        assert hasattr(A, name), "binding lacks %s" % name
+
+
+P = ctypes.c_void_p(256)  # dummy non-null device pointer; never dereferenced
+
+
+def _fwd(A, **kw):
+    args = dict(q=P, k=P, v=P, o=P, lse=None, B=1, H=4, Hkv=2, N=16, d=128, causal=0,
+                scale=0.1, mode=0, o_dtype=0, workspace=None, workspace_bytes=0, stream=None)
+    args.update(kw)
+    return A.attn_fwd(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(o=None), -1), (dict(B=0), -1), (dict(N=-3), -1),
+    (dict(H=3), -1), (dict(Hkv=0), -1), (dict(scale=0.0), -1), (dict(scale=float("nan")), -1),
+    (dict(scale=float("inf")), -1), (dict(o_dtype=7), -1), (dict(mode=9), -1),
+    (dict(d=96), -2), (dict(d=256), -2),
+])
+def test_fwd_validation(A, kw, status):
+    assert _fwd(A, **kw) == status
+    assert A.attn_last_error() != ""
+
+
+def test_fwd_sage_workspace_required(A):
+    need = A.attn_fwd_workspace_size(1, 4, 2, 16, 128, A.ATTN_MODE_SAGE_QK_I8_BLK64_PV_FP8_E4M3)
+    if need == 0:
+        pytest.skip("quantised mode needs no workspace in this build")
+    assert _fwd(A, mode=1) == A.ATTN_ERR_WORKSPACE
+    assert _fwd(A, mode=1, workspace=P, workspace_bytes=need - 1) == A.ATTN_ERR_WORKSPACE
+
+
+def _dec(A, **kw):
+    args = dict(q=P, k_cache=P, v_cache=P, seqlens=P, o=P, lse=None, B=2, H=8, Hkv=2,
+                N_max=1024, d=128, scale=0.1, mode=0, o_dtype=0, split_tokens=512,
+                workspace=P, workspace_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return A.attn_decode(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(seqlens=None), -1), (dict(k_cache=None), -1), (dict(B=0), -1), (dict(H=7), -1),
+    (dict(H=6), -2),
+    (dict(scale=-1.0), -1), (dict(split_tokens=0), -1), (dict(split_tokens=100), -1),
+    (dict(mode=1), -2), (dict(mode=5), -1), (dict(d=80), -2), (dict(H=24, Hkv=2), -2),
+    (dict(split_tokens=1024, H=16), -2), (dict(workspace=None), -3),
+    (dict(workspace_bytes=1000), -3),
+])
+def test_decode_validation(A, kw, status):
+    assert _dec(A, **kw) == status
+
+
+def test_workspace_sizes(A):
+    # partial O fp32 [B,H,splits,d] + partial lse fp32 [B,H,splits], each 256-B aligned
+    B, H, N, d, s = 64, 32, 32768, 128, 512
+    splits = N // s
+    o_b = 4 * B * H * splits * d
+    l_b = 4 * B * H * splits
+    assert A.attn_decode_workspace_size(B, H, N, d, s) == o_b + ((l_b + 255) // 256) * 256
+    assert A.attn_decode_workspace_size(0, H, N, d, s) == 0
+    assert A.attn_fwd_workspace_size(1, 4, 2, 16, 128, 0) == 0
+
+
+def test_status_strings(A):
+    for st in (0, -1, -2, -3, -4):
+        assert A.attn_status_string(st)
+    assert A.attn_status_string(123) == "unknown status"

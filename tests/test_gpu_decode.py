@@ -1,0 +1,99 @@
+"""GPU parity of the split-KV GQA decode (split kernel + LSE merge) against the
+fp64 oracle, which computes each query row over its valid keys without any
+splitting.  Cache positions beyond each sequence length hold NaN, so any
+over-read poisons the output."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests._compare import check_exact
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def attn():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import softmax_attention_attn_amd as A
+    return A
+
+
+def _oracle(q, k, v, seqlens, scale):
+    B, H, d = q.shape
+    o, lse, err = oracle.attn_rows(workloads.bf16_bits(q.reshape(B, H, 1, d)),
+                                   workloads.bf16_bits(k), workloads.bf16_bits(v),
+                                   causal=False, scale=scale, kv_len=seqlens.numpy())
+    assert err <= 1e-12
+    return o.reshape(B, H, d), lse.reshape(B, H)
+
+
+CASES = [
+    # B, H, Hkv, N_max, d, lengths, split
+    (3, 8, 2, 1000, 128, (1, 513, 1000), 512),
+    (3, 8, 2, 1000, 128, (64, 65, 999), 64),
+    (2, 4, 4, 700, 64, (700, 129), 128),
+    (2, 16, 2, 300, 128, (300, 17), 256),
+    (4, 2, 1, 2048, 128, (2048, 1, 1536, 777), 512),
+]
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B%dH%dKV%dN%dd%d-%s-s%d" % (
+    c[0], c[1], c[2], c[3], c[4], "_".join(map(str, c[5])), c[6]))
+def test_small_decode(attn, case, out_dtype):
+    B, H, Hkv, N, d, lens, split = case
+    q, k, v, _ = workloads.make_prefill(B, H, Hkv, N, d, seed=B + H + N)
+    q = q[:, :, 0].contiguous()
+    seqlens = torch.tensor(lens, dtype=torch.int32)
+    for b, L in enumerate(lens):
+        k[b, :, L:] = float("nan")
+        v[b, :, L:] = float("nan")
+    scale = 1 / math.sqrt(d)
+    o, lse = attn.decode(q.cuda(), k.cuda(), v.cuda(), seqlens.cuda(), split_tokens=split,
+                         out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = _oracle(q, k, v, seqlens, scale)
+    check_exact(o.float().cpu().numpy(), o_ref, lse.cpu().numpy(), lse_ref,
+                bf16_out=out_dtype == torch.bfloat16, what=str(case))
+
+
+def test_split_size_invariance(attn):
+    B, H, Hkv, N, d = 2, 8, 2, 2000, 128
+    q, k, v, seqlens = workloads.make_decode(B, H, Hkv, N, d, len_lo=1500, len_hi=2000, seed=9)
+    outs = []
+    for split in (64, 256, 512):
+        o, lse = attn.decode(q.cuda(), k.cuda(), v.cuda(), seqlens.cuda(), split_tokens=split,
+                             out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        outs.append((o.cpu().numpy(), lse.cpu().numpy()))
+    for o, lse in outs[1:]:
+        assert np.abs(o - outs[0][0]).max() < 1e-5
+        assert np.abs(lse - outs[0][1]).max() < 1e-5
+
+
+def test_gqa_decode_workload_full(attn):
+    """The full decode workload, every (b, h) row compared."""
+    w = workloads.WORKLOADS["gqa_decode"]
+    inp = workloads.make(w)
+    q, k, v, seqlens = inp["q"], inp["k"], inp["v"], inp["seqlens"]
+    o, lse = attn.decode(q.cuda(), k.cuda(), v.cuda(), seqlens.cuda(),
+                         split_tokens=w.split_tokens)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = _oracle(q, k, v, seqlens, w.scale)
+    res = check_exact(o.float().cpu().numpy(), o_ref, lse.cpu().numpy(), lse_ref,
+                      bf16_out=True, what=w.name)
+    print(w.name, res)
+
+
+def test_decode_rejects_unsupported(attn):
+    q = torch.zeros((1, 8, 128), dtype=torch.bfloat16, device="cuda")
+    kc = torch.zeros((1, 2, 64, 128), dtype=torch.bfloat16, device="cuda")
+    sl = torch.ones((1,), dtype=torch.int32, device="cuda")
+    with pytest.raises(attn.AttnError) as e:
+        attn.decode(q, kc, kc, sl, split_tokens=100)
+    assert e.value.status == attn.ATTN_ERR_INVALID_ARG

@@ -1,0 +1,196 @@
+"""GPU parity of the exact bf16 prefill kernel against the fp64 oracle.
+
+All calls go through the C ABI (the ctypes binding).  Small shapes span
+several tiles and ragged tails and are compared element by element over every
+row; the full-size workloads are compared on a declared sample of rows (whole
+(b, h) slices where affordable, tile-edge rows of every slice, seeded random
+rows, rows around outlier keys), each sampled row being an exact check of
+that row.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests._compare import check_exact
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def attn():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import softmax_attention_attn_amd as A
+    return A
+
+
+def _oracle_full(q, k, v, causal, scale, rows=None):
+    o, lse, err = oracle.attn_rows(workloads.bf16_bits(q), workloads.bf16_bits(k),
+                                   workloads.bf16_bits(v), causal=causal, scale=scale, rows=rows)
+    assert err <= 1e-12
+    return o, lse
+
+
+def _run(attn, q, k, v, causal, out_dtype, scale=None):
+    o, lse = attn.fwd(q.cuda(), k.cuda(), v.cuda(), causal=causal, out_dtype=out_dtype,
+                      scale=scale)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+CASES = [
+    # B, H, Hkv, N, d
+    (1, 1, 1, 1, 64),
+    (1, 2, 2, 63, 64),
+    (2, 2, 1, 65, 128),
+    (1, 4, 2, 128, 128),
+    (1, 3, 3, 257, 128),
+    (2, 4, 4, 300, 64),
+    (1, 8, 2, 520, 128),
+]
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("shape", CASES, ids=lambda s: "B%dH%dKV%dN%dd%d" % s)
+def test_small_shapes(attn, shape, causal, out_dtype):
+    B, H, Hkv, N, d = shape
+    q, k, v, _ = workloads.make_prefill(B, H, Hkv, N, d, seed=N + d + causal)
+    o, lse = _run(attn, q, k, v, causal, out_dtype)
+    o_ref, lse_ref = _oracle_full(q, k, v, causal, 1 / math.sqrt(d))
+    check_exact(o, o_ref, lse, lse_ref, bf16_out=out_dtype == torch.bfloat16,
+                what="%s causal=%s" % (shape, causal))
+
+
+def test_tiny_exact_workload(attn):
+    w = workloads.WORKLOADS["tiny_exact"]
+    inp = workloads.make(w)
+    o, lse = _run(attn, inp["q"], inp["k"], inp["v"], w.causal, torch.float32)
+    o_ref, lse_ref = _oracle_full(inp["q"], inp["k"], inp["v"], w.causal, w.scale)
+    res = check_exact(o, o_ref, lse, lse_ref, bf16_out=False, what=w.name)
+    print(w.name, res)
+
+
+def test_large_scores_and_scale(attn):
+    """Scores of magnitude ~100 (online-softmax rescaling must not overflow)."""
+    g = torch.Generator().manual_seed(21)
+    B, H, N, d = 1, 2, 333, 128
+    q = (torch.randn((B, H, N, d), generator=g) * 4).to(torch.bfloat16)
+    k = (torch.randn((B, H, N, d), generator=g) * 4).to(torch.bfloat16)
+    v = torch.randn((B, H, N, d), generator=g).to(torch.bfloat16)
+    for causal in (False, True):
+        o, lse = _run(attn, q, k, v, causal, torch.float32, scale=0.5)
+        o_ref, lse_ref = _oracle_full(q, k, v, causal, 0.5)
+        check_exact(o, o_ref, lse, lse_ref, bf16_out=False, what="large scores")
+
+
+def test_closed_forms_on_device(attn):
+    g = torch.Generator().manual_seed(22)
+    B, H, N, d = 1, 2, 200, 128
+    v = torch.randn((B, H, N, d), generator=g).to(torch.bfloat16)
+    k = torch.randn((B, H, N, d), generator=g).to(torch.bfloat16)
+    q0 = torch.zeros((B, H, N, d), dtype=torch.bfloat16)
+    o, lse = _run(attn, q0, k, v, True, torch.float32)
+    vd = v.double().numpy()
+    cm = np.cumsum(vd, axis=2) / np.arange(1, N + 1)[None, None, :, None]
+    assert np.abs(o - cm).max() < 1e-2
+    assert np.abs(lse - np.log(np.arange(1, N + 1))[None, None]).max() < 1e-4
+    # causal row 0 is V[0] exactly, also in bf16
+    q = torch.randn((B, H, N, d), generator=g).to(torch.bfloat16)
+    ob, _ = attn.fwd(q.cuda(), k.cuda(), v.cuda(), causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(ob[:, :, 0].cpu(), v[:, :, 0])
+
+
+def test_deterministic(attn):
+    q, k, v, _ = workloads.make_prefill(1, 4, 2, 700, 128, seed=3)
+    q, k, v = q.cuda(), k.cuda(), v.cuda()
+    o1, l1 = attn.fwd(q, k, v, causal=True)
+    o2, l2 = attn.fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_no_over_read(attn):
+    """Inputs embedded in NaN-filled storage: any read past a tensor's end
+    would poison the output."""
+    B, H, N, d = 1, 2, 77, 128
+    q, k, v, _ = workloads.make_prefill(B, H, H, N, d, seed=4)
+    dev = []
+    for t in (q, k, v):
+        buf = torch.full((t.numel() + 4096,), float("nan"), dtype=torch.bfloat16, device="cuda")
+        buf[: t.numel()] = t.reshape(-1).cuda()
+        dev.append(buf[: t.numel()].view(t.shape))
+    for causal in (False, True):
+        o, lse = attn.fwd(*dev, causal=causal, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = _oracle_full(q, k, v, causal, 1 / math.sqrt(d))
+        check_exact(o.cpu().numpy(), o_ref, lse.cpu().numpy(), lse_ref, bf16_out=False,
+                    what="nan-poisoned")
+
+
+def test_lse_optional(attn):
+    q, k, v, _ = workloads.make_prefill(1, 2, 2, 100, 64, seed=5)
+    o, lse = attn.fwd(q.cuda(), k.cuda(), v.cuda(), causal=True, with_lse=False)
+    torch.cuda.synchronize()
+    assert lse is None
+    o_ref, _ = _oracle_full(q, k, v, True, 1 / 8)
+    check_exact(o.float().cpu().numpy(), o_ref, None, None, bf16_out=True, what="no lse")
+
+
+def _sampled_check(attn, w, rows, out_dtype=torch.bfloat16):
+    inp = workloads.make(w)
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    o, lse = attn.fwd(q.cuda(), k.cuda(), v.cuda(), causal=w.causal, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy().reshape(-1, w.d)[rows]
+    lse = lse.cpu().numpy().reshape(-1)[rows]
+    o_ref, lse_ref = _oracle_full(q, k, v, w.causal, w.scale, rows=rows)
+    return check_exact(o, o_ref, lse, lse_ref, bf16_out=out_dtype == torch.bfloat16,
+                       what=w.name), inp
+
+
+def test_llm_prefill_workload_sampled(attn):
+    w = workloads.WORKLOADS["llm_prefill"]
+    rows = workloads.sample_rows(w.B, w.H, w.N, n_random=1024,
+                                 whole_slices=((0, 0), (w.B - 1, w.H - 1)))
+    res, _ = _sampled_check(attn, w, rows)
+    print(w.name, len(rows), "rows", res)
+
+
+def test_long_prefill_workload_sampled(attn):
+    """Outlier keys (x20) stress the running-max rescaling; the sample holds
+    rows around every outlier of head 0 as well as tile edges and random rows.
+    The fp32-store instantiation must meet max |dO| <= 1e-2 literally."""
+    w = workloads.WORKLOADS["long_prefill"]
+    base = workloads.sample_rows(w.B, w.H, w.N, n_random=384, whole_slices=())
+    # rows right after the first outliers of kv head 0 (their key is visible from there)
+    inp = workloads.make(w)
+    out_rows = inp["outlier_rows"].numpy()
+    head0 = out_rows[out_rows < w.N][:16]
+    extra = np.concatenate([np.clip(head0 + dlt, 0, w.N - 1) for dlt in (0, 1, 2)])
+    rows = np.unique(np.concatenate([base, extra]))
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    o_ref, lse_ref = _oracle_full(q, k, v, True, w.scale, rows=rows)
+    for out_dtype in (torch.bfloat16, torch.float32):
+        o, lse = attn.fwd(q.cuda(), k.cuda(), v.cuda(), causal=True, out_dtype=out_dtype)
+        torch.cuda.synchronize()
+        o = o.float().cpu().numpy().reshape(-1, w.d)[rows]
+        lse = lse.cpu().numpy().reshape(-1)[rows]
+        res = check_exact(o, o_ref, lse, lse_ref, bf16_out=out_dtype == torch.bfloat16,
+                          what="%s %s" % (w.name, out_dtype))
+        print(w.name, out_dtype, len(rows), "rows", res)
+        del o, lse
+    torch.cuda.empty_cache()
+
+
+def test_invalid_args_launch_nothing(attn):
+    q = torch.zeros((1, 3, 8, 64), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros((1, 2, 8, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(attn.AttnError) as e:
+        attn.fwd(q, k, k)
+    assert e.value.status == attn.ATTN_ERR_INVALID_ARG
