@@ -66,6 +66,22 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // Value held by the lane 32 positions away (lanes l and l ^ 32 exchange).
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
+// v_permlane32_swap on two copies of x: one result holds the lower-half
+// lanes' values in both halves, the other the upper-half lanes' values, so a
+// symmetric combination of the two is the combination of lanes l and l ^ 32.
+__device__ __forceinline__ float max_xor32(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Global loads/stores of 16 bytes.
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *(const u32x4 *)p; }
 __device__ __forceinline__ void st16(void *p, u32x4 v) { *(u32x4 *)p = v; }
