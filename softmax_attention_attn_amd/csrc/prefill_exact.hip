@@ -191,34 +191,15 @@ __device__ __forceinline__ LaneOffsets<D> lane_offsets(int lane)
     return off;
 }
 
-// Everything one wave does for key tile t: wait for the tile, start the
-// next tile's loads into the other stage, S^T = K Q^T, mask, online softmax,
-// O^T += V^T P^T.
-template <int D, bool CAUSAL>
-__device__ __forceinline__ void process_tile(WaveState<D> &st, const bf16x8 (&qf)[D / 16],
-                                             const LaneOffsets<D> &off, unsigned char *kbuf,
-                                             unsigned char *vbuf, unsigned char *nkbuf,
-                                             unsigned char *nvbuf, int t, int ntiles,
-                                             const uint16_t *kb, const uint16_t *vb, int N,
-                                             int qw0, int my_q, float cs, int wave, int lane)
+// S^T = K Q^T for one key tile: MFMA i = KS*blk + ks reads K row 32*blk + n,
+// chunk 2*ks + g; the reads run four MFMAs ahead.
+template <int D>
+__device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const bf16x8 (&qf)[D / 16], uint32_t kaddr)
 {
-    const int g = lane >> 5;
-    const int k0 = t * kBN;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (t + 1 < ntiles) {
-        issue_k<D>(nkbuf, kb, k0 + kBN, N, wave, lane);
-        issue_v<D>(nvbuf, vb, k0 + kBN, N, wave, lane);
-    }
-    if (CAUSAL && k0 > qw0 + kQW - 1)
-        return;  // every key of this tile lies above the diagonal for this wave
-
-    // S^T = K Q^T: MFMA i = KS*blk + ks reads K row 32*blk + n, chunk 2*ks + g;
-    // the reads run four MFMAs ahead.
     constexpr int KS = D / 16, NK = 2 * KS, KLA = 4;
-    const uint32_t kaddr = lds_addr(kbuf) + off.k;
     u32x4 kv[KLA + 1];
-    f32x16 s[2] = {f32x16{}, f32x16{}};
+    s[0] = f32x16{};
+    s[1] = f32x16{};
     static_for<0, KLA>([&](auto i) {
         constexpr int I = decltype(i)::value;
         kv[I] = lds_read_b128<(I / KS) * 32 * Cfg<D>::kKPitch + (I % KS) * 32>(kaddr);
@@ -235,59 +216,18 @@ __device__ __forceinline__ void process_tile(WaveState<D> &st, const bf16x8 (&qf
         }
         s[I / KS] = mfma_bf16_32x32x16(as_bf16x8(kv[I % (KLA + 1)]), qf[I % KS], s[I / KS]);
     });
+}
 
-    if ((CAUSAL && k0 + kBN - 1 > qw0) || k0 + kBN > N) {
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = k0 + 32 * blk + 8 * (r >> 2) + 4 * g + (r & 3);
-                if (key >= N || (CAUSAL && key > my_q))
-                    s[blk][r] = -INFINITY;
-            }
-    }
-    float mx = s[0][0];
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            mx = fmaxf(mx, s[blk][r]);
-    mx = max_xor32(mx) * cs;
-    // The first tile always holds key 0, visible to every query, so m is
-    // finite from the first tile on.
-    if (__any(mx > st.m + kRescaleLog2)) {
-        const float m_new = mx > st.m + kRescaleLog2 ? mx : st.m;
-        const float alpha = fast_exp2(st.m - m_new);
-        st.l *= alpha;
-#pragma unroll
-        for (int c = 0; c < D / 32; ++c)
-            st.o[c] *= alpha;
-        st.m = m_new;
-    }
-
-    // probabilities, rounded to bf16 for the PV product; the row sum is taken
-    // over the unrounded fp32 values (a bf16-rounded sum would carry up to
-    // 2^-9 relative error into the LSE of rows with few keys)
-    uint32_t pk[2][8];
-    float rs0 = 0.f, rs1 = 0.f;
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-            const float p0 = fast_exp2(fmaf(s[blk][r], cs, -st.m));
-            const float p1 = fast_exp2(fmaf(s[blk][r + 1], cs, -st.m));
-            rs0 += p0;
-            rs1 += p1;
-            pk[blk][r >> 1] = pack_bf16x2(p0, p1);
-        }
-    st.l += rs0 + rs1;
-
-    // O^T += V^T P^T: MFMA i = 4c + 2*blk + hh takes as B operand registers
-    // 8*hh .. 8*hh+7 of s[blk], i.e. keys 32*blk + 16*hh + 8*(e/4) + 4*g + e%4
-    // for element e; its V^T operand is two transposing reads of key rows
-    // 32*blk + 16*hh + 4g + 0..3 and +8..11.  Reads run two MFMAs ahead.
+// O^T += V^T P^T for one key tile: MFMA i = 4c + 2*blk + hh takes as B
+// operand registers 8*hh .. 8*hh+7 of s[blk], i.e. keys 32*blk + 16*hh +
+// 8*(e/4) + 4*g + e%4 for element e; its V^T operand is two transposing reads
+// of key rows 32*blk + 16*hh + 4g + 0..3 and +8..11.  Reads run two MFMAs
+// ahead.
+template <int D>
+__device__ __forceinline__ void pv_tile(f32x16 (&o)[D / 32], const uint32_t (&pk)[2][8],
+                                        uint32_t vaddr, const LaneOffsets<D> &off)
+{
     constexpr int NV = 4 * (D / 32), VLA = 2;
-    const uint32_t vaddr = lds_addr(vbuf);
     u32x4 vw[VLA + 1];
     auto read_v = [&](auto i) -> u32x4 {
         constexpr int I = decltype(i)::value;
@@ -310,35 +250,193 @@ __device__ __forceinline__ void process_tile(WaveState<D> &st, const bf16x8 (&qf
         constexpr int c = I >> 2, blk = (I >> 1) & 1, hh = I & 1;
         const u32x4 pw = {pk[blk][4 * hh], pk[blk][4 * hh + 1], pk[blk][4 * hh + 2],
                           pk[blk][4 * hh + 3]};
-        st.o[c] = mfma_bf16_32x32x16(as_bf16x8(vw[I % (VLA + 1)]), as_bf16x8(pw), st.o[c]);
+        o[c] = mfma_bf16_32x32x16(as_bf16x8(vw[I % (VLA + 1)]), as_bf16x8(pw), o[c]);
     });
 }
 
-template <int D, bool CAUSAL, bool OUT_F32>
-__global__ __launch_bounds__(kThreads) void prefill_exact_kernel(PrefillArgs a)
+// p = 2^(s*cs - m), rounded to bf16 for the PV product; the row sum is taken
+// over the unrounded fp32 values (a bf16-rounded sum would carry up to 2^-9
+// relative error into the LSE of rows with few keys).
+__device__ __forceinline__ void exp_tile(const f32x16 (&s)[2], float m, float cs,
+                                         uint32_t (&pk)[2][8], float &l)
 {
-    __shared__ __attribute__((aligned(1024))) unsigned char k_st0[Cfg<D>::kKBytes];
-    __shared__ __attribute__((aligned(1024))) unsigned char v_st0[Cfg<D>::kVBytes];
-    __shared__ __attribute__((aligned(1024))) unsigned char k_st1[Cfg<D>::kKBytes];
-    __shared__ __attribute__((aligned(1024))) unsigned char v_st1[Cfg<D>::kVBytes];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+            const float p0 = fast_exp2(fmaf(s[blk][r], cs, -m));
+            const float p1 = fast_exp2(fmaf(s[blk][r + 1], cs, -m));
+            rs0 += p0;
+            rs1 += p1;
+            pk[blk][r >> 1] = pack_bf16x2(p0, p1);
+        }
+    l += rs0 + rs1;
+}
+
+__device__ __forceinline__ float tile_max(const f32x16 (&s)[2])
+{
+    float mx = s[0][0];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            mx = fmaxf(mx, s[blk][r]);
+    return mx;
+}
+
+template <bool CAUSAL>
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int k0, int N, int g, int my_q)
+{
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = k0 + 32 * blk + 8 * (r >> 2) + 4 * g + (r & 3);
+            if (key >= N || (CAUSAL && key > my_q))
+                s[blk][r] = -INFINITY;
+        }
+}
+
+// Raise the reference max when the tile max (log2 units) exceeds it by more
+// than 2^8 for some lane of the wave, rescaling O and l.  The first tile
+// always holds key 0, visible to every query, so m is finite from the first
+// tile on.
+template <int D>
+__device__ __forceinline__ void update_max(WaveState<D> &st, float mx)
+{
+    if (__any(mx > st.m + kRescaleLog2)) {
+        const float m_new = mx > st.m + kRescaleLog2 ? mx : st.m;
+        const float alpha = fast_exp2(st.m - m_new);
+        st.l *= alpha;
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c)
+            st.o[c] *= alpha;
+        st.m = m_new;
+    }
+}
+
+// Phase A of the software pipeline: the QK MFMAs of the next tile, each
+// followed by a slice of the exponentials of the current tile.  The two
+// 32-key accumulators alternate so that consecutive MFMAs are independent.
+// Each step exponentiates two scores and folds the two of the previous step
+// into the row sum and the bf16 P fragment (the exp latency is then covered
+// by the MFMA in between).  Steps are fenced with scheduling barriers and
+// their results pinned, so the wave issues VALU work between its MFMAs
+// instead of in one block.
+template <int D>
+__device__ __forceinline__ void phase_a(f32x16 (&s_next)[2], const bf16x8 (&qf)[D / 16],
+                                        uint32_t kaddr, const f32x16 (&s_cur)[2], float m,
+                                        float cs, uint32_t (&pk)[2][8], float &l)
+{
+    constexpr int KS = D / 16, NK = 2 * KS, KLA = 4;
+    constexpr int EPS = 32 / NK;  // scores exponentiated per step
+    static_assert(EPS == 2 || EPS == 4, "slice size");
+    u32x4 kv[KLA + 1];
+    s_next[0] = f32x16{};
+    s_next[1] = f32x16{};
+    float rs0 = 0.f, rs1 = 0.f;
+    float pp[2][EPS];  // exponentials of the previous and the current step
+    // MFMA i: block i % 2, k-step i / 2
+    auto kread = [&](auto i) -> u32x4 {
+        constexpr int I = decltype(i)::value;
+        return lds_read_b128<(I % 2) * 32 * Cfg<D>::kKPitch + (I / 2) * 32>(kaddr);
+    };
+    auto fold = [&](auto i) {  // row sum and bf16 packing of step i's slice
+        constexpr int I = decltype(i)::value;
+        static_for<0, EPS / 2>([&](auto e) {
+            constexpr int R = I * EPS + 2 * decltype(e)::value;
+            constexpr int blk = R / 16, r = R % 16;
+            const float p0 = pp[I % 2][2 * decltype(e)::value];
+            const float p1 = pp[I % 2][2 * decltype(e)::value + 1];
+            rs0 += p0;
+            rs1 += p1;
+            pk[blk][r >> 1] = pack_bf16x2(p0, p1);
+            asm volatile("" : "+v"(pk[blk][r >> 1]), "+v"(rs0), "+v"(rs1));
+        });
+    };
+    static_for<0, KLA>([&](auto i) { kv[decltype(i)::value] = kread(i); });
+    static_for<0, NK>([&](auto i) {
+        constexpr int I = decltype(i)::value;
+        if constexpr (I + KLA < NK) {
+            kv[(I + KLA) % (KLA + 1)] = kread(std::integral_constant<int, I + KLA>{});
+            lgkm_wait<KLA>(kv[I % (KLA + 1)]);
+        } else {
+            lgkm_wait<NK - 1 - I>(kv[I % (KLA + 1)]);
+        }
+        s_next[I % 2] =
+            mfma_bf16_32x32x16(as_bf16x8(kv[I % (KLA + 1)]), qf[I / 2], s_next[I % 2]);
+        static_for<0, EPS>([&](auto e) {
+            constexpr int R = I * EPS + decltype(e)::value;
+            pp[I % 2][decltype(e)::value] = fast_exp2(fmaf(s_cur[R / 16][R % 16], cs, -m));
+            asm volatile("" : "+v"(pp[I % 2][decltype(e)::value]));
+        });
+        if constexpr (I > 0)
+            fold(std::integral_constant<int, I - 1>{});
+        __builtin_amdgcn_sched_barrier(0);
+    });
+    fold(std::integral_constant<int, NK - 1>{});
+    l += rs0 + rs1;
+}
+
+// Phase B: the PV MFMAs of the current tile, each followed by a slice of the
+// row max of the next tile; returns that max (this lane's keys only).
+// Consecutive MFMAs accumulate into different feature blocks.
+template <int D>
+__device__ __forceinline__ float phase_b(f32x16 (&o)[D / 32], const uint32_t (&pk)[2][8],
+                                         uint32_t vaddr, const LaneOffsets<D> &off,
+                                         const f32x16 (&s_next)[2])
+{
+    constexpr int NC = D / 32, NV = 4 * NC, VLA = 2;
+    constexpr int MPS = 32 / NV;  // scores reduced per step
+    u32x4 vw[VLA + 1];
+    // MFMA i: feature block i % NC, key quarter q = i / NC (blk = q / 2, hh = q % 2)
+    auto read_v = [&](auto i) -> u32x4 {
+        constexpr int I = decltype(i)::value;
+        constexpr int c = I % NC, q = I / NC, blk = q >> 1, hh = q & 1;
+        constexpr int row0 = 32 * blk + 16 * hh;
+        const uint32_t a = vaddr + off.v[c];
+        const u32x2 w0 = lds_read_tr16_b64<row0 * Cfg<D>::kVPitch>(a);
+        const u32x2 w1 = lds_read_tr16_b64<(row0 + 8) * Cfg<D>::kVPitch>(a);
+        return u32x4{w0[0], w0[1], w1[0], w1[1]};
+    };
+    float mx0 = -INFINITY, mx1 = -INFINITY;
+    static_for<0, VLA>([&](auto i) { vw[decltype(i)::value] = read_v(i); });
+    static_for<0, NV>([&](auto i) {
+        constexpr int I = decltype(i)::value;
+        if constexpr (I + VLA < NV) {
+            vw[(I + VLA) % (VLA + 1)] = read_v(std::integral_constant<int, I + VLA>{});
+            lgkm_wait<2 * VLA>(vw[I % (VLA + 1)]);
+        } else {
+            lgkm_wait<2 * (NV - 1 - I)>(vw[I % (VLA + 1)]);
+        }
+        constexpr int c = I % NC, q = I / NC, blk = q >> 1, hh = q & 1;
+        const u32x4 pw = {pk[blk][4 * hh], pk[blk][4 * hh + 1], pk[blk][4 * hh + 2],
+                          pk[blk][4 * hh + 3]};
+        o[c] = mfma_bf16_32x32x16(as_bf16x8(vw[I % (VLA + 1)]), as_bf16x8(pw), o[c]);
+        static_for<0, MPS / 2>([&](auto e) {
+            constexpr int R = I * MPS + 2 * decltype(e)::value;
+            constexpr int sb = R / 16, r = R % 16;
+            if constexpr ((I * (MPS / 2) + decltype(e)::value) % 2 == 0)
+                mx0 = vmax3(mx0, s_next[sb][r], s_next[sb][r + 1]);
+            else
+                mx1 = vmax3(mx1, s_next[sb][r], s_next[sb][r + 1]);
+            asm volatile("" : "+v"(mx0), "+v"(mx1));
+        });
+        __builtin_amdgcn_sched_barrier(0);
+    });
+    return vmax3(mx0, mx1, mx1);
+}
+
+// One query tile of one (batch, head): load its Q fragments, stream every
+// visible K/V tile through the LDS stages, write O and the LSE.
+template <int D, bool CAUSAL, bool OUT_F32>
+__device__ __forceinline__ void attend_qtile(const PrefillArgs &a, unsigned char *smem, int bh,
+                                             int qt, int wave, int lane)
+{
+    constexpr int kStage = Cfg<D>::kKBytes + Cfg<D>::kVBytes;
     const int g = lane >> 5, n = lane & 31;
     const int N = a.N;
-    const int nqt = (N + kBM - 1) / kBM;
-    const int BH = a.B * a.H;
-
-    // workgroup -> (head, query tile)
-    int bh, qi;
-    const int wg = blockIdx.x;
-    if ((BH & 7) == 0) {
-        const int xcd = wg & 7, slot = wg >> 3;
-        bh = xcd + 8 * (slot / nqt);
-        qi = slot % nqt;
-    } else {
-        bh = wg / nqt;
-        qi = wg % nqt;
-    }
-    const int qt = CAUSAL ? nqt - 1 - qi : qi;
     const int h = bh % a.H, b = bh / a.H;
     const int q0 = qt * kBM;
     const int kvh = h / (a.H / a.Hkv);
@@ -350,10 +448,21 @@ __global__ __launch_bounds__(kThreads) void prefill_exact_kernel(PrefillArgs a)
 
     const int kend = CAUSAL ? min(N, q0 + kBM) : N;
     const int ntiles = (kend + kBN - 1) / kBN;
+    // tiles this wave computes (the rest lie above its causal diagonal)
+    const int ntw = CAUSAL ? min(ntiles, (qw0 + kQW - 1) / kBN + 1) : ntiles;
+    auto kst = [&](int t) { return smem + (t % 3) * kStage; };
+    auto vst = [&](int t) { return smem + (t % 3) * kStage + Cfg<D>::kKBytes; };
+    auto needs_mask = [&](int t) {
+        const int k0 = t * kBN;
+        return (CAUSAL && k0 + kBN - 1 > qw0) || k0 + kBN > N;
+    };
 
-    // first tile in flight while Q is fetched
-    issue_k<D>(k_st0, kb, 0, N, wave, lane);
-    issue_v<D>(v_st0, vb, 0, N, wave, lane);
+    issue_k<D>(kst(0), kb, 0, N, wave, lane);
+    issue_v<D>(vst(0), vb, 0, N, wave, lane);
+    if (ntiles > 1) {
+        issue_k<D>(kst(1), kb, kBN, N, wave, lane);
+        issue_v<D>(vst(1), vb, kBN, N, wave, lane);
+    }
 
     // Q^T fragments (B operand): lane holds Q[my_q][16*ks + 8*g .. +7].
     bf16x8 qf[D / 16];
@@ -371,12 +480,43 @@ __global__ __launch_bounds__(kThreads) void prefill_exact_kernel(PrefillArgs a)
     st.l = 0.f;
     const float cs = a.scale * kLog2e;
 
+    // Software pipeline: iteration t runs the QK MFMAs of tile t+1 next to
+    // the exponentials of tile t, then the PV MFMAs of tile t next to the
+    // masking and max of tile t+1, so each wave has independent VALU work to
+    // issue between its MFMAs.  The loop is unrolled twice so that the two
+    // score buffers swap roles without register copies.
+    f32x16 sa[2], sb[2];
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    qk_tile<D>(sa, qf, lds_addr(kst(0)) + off.k);
+    if (needs_mask(0))
+        mask_tile<CAUSAL>(sa, 0, N, g, my_q);
+    update_max<D>(st, max_xor32(tile_max(sa)) * cs);
+
+    auto step = [&](int t, f32x16(&s_cur)[2], f32x16(&s_next)[2]) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (t + 2 < ntiles) {
+            issue_k<D>(kst(t + 2), kb, (t + 2) * kBN, N, wave, lane);
+            issue_v<D>(vst(t + 2), vb, (t + 2) * kBN, N, wave, lane);
+        }
+        if (t >= ntw)
+            return;
+        // QK(t+1) also runs when this wave does not need tile t+1 (the result
+        // is then dropped) so that phase A has no branch.
+        uint32_t pk[2][8];
+        phase_a<D>(s_next, qf, lds_addr(kst(t + 1)) + off.k, s_cur, st.m, cs, pk, st.l);
+        const bool more = t + 1 < ntw;
+        if (more && needs_mask(t + 1))
+            mask_tile<CAUSAL>(s_next, (t + 1) * kBN, N, g, my_q);
+        const float mx = phase_b<D>(st.o, pk, lds_addr(vst(t)), off, s_next);
+        if (more)
+            update_max<D>(st, max_xor32(mx) * cs);
+    };
     for (int t = 0; t < ntiles; t += 2) {
-        process_tile<D, CAUSAL>(st, qf, off, k_st0, v_st0, k_st1, v_st1, t, ntiles, kb, vb, N,
-                                qw0, my_q, cs, wave, lane);
+        step(t, sa, sb);
         if (t + 1 < ntiles)
-            process_tile<D, CAUSAL>(st, qf, off, k_st1, v_st1, k_st0, v_st0, t + 1, ntiles, kb,
-                                    vb, N, qw0, my_q, cs, wave, lane);
+            step(t + 1, sb, sa);
     }
 
     const float lt = sum_xor32(st.l);
@@ -412,10 +552,45 @@ __global__ __launch_bounds__(kThreads) void prefill_exact_kernel(PrefillArgs a)
 }
 
 template <int D, bool CAUSAL, bool OUT_F32>
+__global__ __launch_bounds__(kThreads) void prefill_exact_kernel(PrefillArgs a)
+{
+    // three K/V stages: tile t+2 loads while tile t+1's K and tile t's V are read
+    constexpr int kStage = Cfg<D>::kKBytes + Cfg<D>::kVBytes;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[3 * kStage];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nqt = (a.N + kBM - 1) / kBM;
+    // Causal: workgroup j of a head takes query tiles nqt-1-j and j, so every
+    // workgroup streams the same number of key tiles (no long tail of heavy
+    // tiles started last).  Non-causal: one query tile per workgroup.
+    const int nw = CAUSAL ? (nqt + 1) / 2 : nqt;
+    const int BH = a.B * a.H;
+    int bh, j;
+    const int wg = blockIdx.x;
+    if ((BH & 7) == 0) {
+        // workgroup i runs on XCD i % 8: keep a head's workgroups on one XCD
+        const int xcd = wg & 7, slot = wg >> 3;
+        bh = xcd + 8 * (slot / nw);
+        j = slot % nw;
+    } else {
+        bh = wg / nw;
+        j = wg % nw;
+    }
+    if (CAUSAL) {
+        attend_qtile<D, CAUSAL, OUT_F32>(a, smem, bh, nqt - 1 - j, wave, lane);
+        if (j < nqt - 1 - j) {
+            __syncthreads();  // every wave is done with the LDS stages
+            attend_qtile<D, CAUSAL, OUT_F32>(a, smem, bh, j, wave, lane);
+        }
+    } else {
+        attend_qtile<D, CAUSAL, OUT_F32>(a, smem, bh, j, wave, lane);
+    }
+}
+
+template <int D, bool CAUSAL, bool OUT_F32>
 hipError_t launch_t(const PrefillArgs &a, hipStream_t s)
 {
     const int nqt = (a.N + kBM - 1) / kBM;
-    dim3 grid(a.B * a.H * nqt);
+    dim3 grid(a.B * a.H * (CAUSAL ? (nqt + 1) / 2 : nqt));
     ProfScope ps("prefill_exact", s);
     hipLaunchKernelGGL((prefill_exact_kernel<D, CAUSAL, OUT_F32>), grid, dim3(kThreads), 0, s, a);
     return hipGetLastError();
