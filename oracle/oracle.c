@@ -303,6 +303,15 @@ static void sage_prepare(const uint16_t *q, const uint16_t *k, const uint16_t *v
                          int B, int H, int Hkv, int N, int d, int blk, int smooth_k,
                          sage_state *st)
 {
+    /*
+     * The quantisation decisions (INT8 codes, E4M3 codes) are taken in fp32,
+     * the precision the GPU kernel takes them in: the pages fix no precision
+     * for them, and taking an integer decision in a different precision than
+     * the kernel would flip codes at rounding ties.  Each step is otherwise
+     * the plain formula: K' = K - kmean; delta = max|x| / 127; code =
+     * rint(x * (127 / max|x|)); V code = E4M3(V * (448 / max|V|)).  The mean
+     * itself is taken in fp64 and rounded to fp32.
+     */
     int64_t nqb = (N + blk - 1) / blk;
     st->kmean = (double *)calloc((size_t)B * Hkv * d, sizeof(double));
     st->qhat = (int8_t *)malloc((size_t)B * H * N * d);
@@ -312,7 +321,6 @@ static void sage_prepare(const uint16_t *q, const uint16_t *k, const uint16_t *v
     st->vq = (double *)malloc(sizeof(double) * (size_t)B * Hkv * N * d);
     st->vdelta = (double *)malloc(sizeof(double) * (size_t)B * Hkv * d);
 
-    /* Smooth-K: subtract the per-channel mean of K over the tokens. */
 #pragma omp parallel for
     for (int64_t bg = 0; bg < (int64_t)B * Hkv; ++bg) {
         const uint16_t *kb = k + bg * (int64_t)N * d;
@@ -321,38 +329,39 @@ static void sage_prepare(const uint16_t *q, const uint16_t *k, const uint16_t *v
                 double s = 0.0;
                 for (int64_t n = 0; n < N; ++n)
                     s += bf16_to_f64(kb[n * d + c]);
-                st->kmean[bg * d + c] = s / N;
+                st->kmean[bg * d + c] = (double)(float)(s / N);
             }
         }
         /* INT8 per 64-token block of K - kmean */
         for (int64_t t = 0; t < nqb; ++t) {
             int64_t n0 = t * blk, n1 = n0 + blk < N ? n0 + blk : N;
-            double amax = 0.0;
+            float amax = 0.0f;
             for (int64_t n = n0; n < n1; ++n)
                 for (int c = 0; c < d; ++c) {
-                    double x = bf16_to_f64(kb[n * d + c]) - st->kmean[bg * d + c];
-                    if (fabs(x) > amax)
-                        amax = fabs(x);
+                    float x = (float)bf16_to_f64(kb[n * d + c]) - (float)st->kmean[bg * d + c];
+                    if (fabsf(x) > amax)
+                        amax = fabsf(x);
                 }
-            double delta = amax > 0.0 ? amax / 127.0 : 1.0;
-            st->kdelta[bg * nqb + t] = delta;
+            float inv = amax > 0.0f ? 127.0f / amax : 1.0f;
+            st->kdelta[bg * nqb + t] = amax > 0.0f ? (double)(amax / 127.0f) : 1.0;
             for (int64_t n = n0; n < n1; ++n)
                 for (int c = 0; c < d; ++c) {
-                    double x = bf16_to_f64(kb[n * d + c]) - st->kmean[bg * d + c];
-                    st->khat[(bg * N + n) * d + c] = (int8_t)quant_i8(x, delta);
+                    float x = (float)bf16_to_f64(kb[n * d + c]) - (float)st->kmean[bg * d + c];
+                    st->khat[(bg * N + n) * d + c] = (int8_t)quant_i8((double)(x * inv), 1.0);
                 }
         }
         /* V: per-channel scale over all tokens, E4M3 values */
         const uint16_t *vb = v + bg * (int64_t)N * d;
         for (int c = 0; c < d; ++c) {
-            double amax = 0.0;
+            float amax = 0.0f;
             for (int64_t n = 0; n < N; ++n)
-                if (fabs(bf16_to_f64(vb[n * d + c])) > amax)
-                    amax = fabs(bf16_to_f64(vb[n * d + c]));
-            double delta = amax > 0.0 ? amax / 448.0 : 1.0;
-            st->vdelta[bg * d + c] = delta;
+                if (fabsf((float)bf16_to_f64(vb[n * d + c])) > amax)
+                    amax = fabsf((float)bf16_to_f64(vb[n * d + c]));
+            float inv = amax > 0.0f ? 448.0f / amax : 1.0f;
+            st->vdelta[bg * d + c] = amax > 0.0f ? (double)(amax / 448.0f) : 1.0;
             for (int64_t n = 0; n < N; ++n)
-                st->vq[(bg * N + n) * d + c] = oracle_e4m3_round(bf16_to_f64(vb[n * d + c]) / delta);
+                st->vq[(bg * N + n) * d + c] =
+                    oracle_e4m3_round((double)((float)bf16_to_f64(vb[n * d + c]) * inv));
         }
     }
     /* INT8 per 64-token block of Q */
@@ -361,16 +370,17 @@ static void sage_prepare(const uint16_t *q, const uint16_t *k, const uint16_t *v
         const uint16_t *qb = q + bh * (int64_t)N * d;
         for (int64_t t = 0; t < nqb; ++t) {
             int64_t n0 = t * blk, n1 = n0 + blk < N ? n0 + blk : N;
-            double amax = 0.0;
+            float amax = 0.0f;
             for (int64_t n = n0; n < n1; ++n)
                 for (int c = 0; c < d; ++c)
-                    if (fabs(bf16_to_f64(qb[n * d + c])) > amax)
-                        amax = fabs(bf16_to_f64(qb[n * d + c]));
-            double delta = amax > 0.0 ? amax / 127.0 : 1.0;
-            st->qdelta[bh * nqb + t] = delta;
+                    if (fabsf((float)bf16_to_f64(qb[n * d + c])) > amax)
+                        amax = fabsf((float)bf16_to_f64(qb[n * d + c]));
+            float inv = amax > 0.0f ? 127.0f / amax : 1.0f;
+            st->qdelta[bh * nqb + t] = amax > 0.0f ? (double)(amax / 127.0f) : 1.0;
             for (int64_t n = n0; n < n1; ++n)
                 for (int c = 0; c < d; ++c)
-                    st->qhat[(bh * N + n) * d + c] = (int8_t)quant_i8(bf16_to_f64(qb[n * d + c]), delta);
+                    st->qhat[(bh * N + n) * d + c] =
+                        (int8_t)quant_i8((double)((float)bf16_to_f64(qb[n * d + c]) * inv), 1.0);
         }
     }
 }

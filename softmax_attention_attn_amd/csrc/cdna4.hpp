@@ -16,6 +16,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace attn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -90,6 +92,62 @@ __device__ __forceinline__ float sum_xor32(float x)
                                                     false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [I0, N).
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
+// Row m of a 32-row MFMA block is taken from index perm32(m): lane half g
+// then holds indices 16g .. 16g+15 in accumulator registers 0..15.
+__device__ __forceinline__ int perm32(int m) { return ((m >> 2) & 1) * 16 + (m >> 3) * 4 + (m & 3); }
+
+// LDS byte address of a __shared__ pointer.
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// LDS reads issued as inline asm.  Kernels that fill LDS with direct
+// global->LDS loads use them because the compiler cannot tell these reads
+// from the in-flight direct loads of another stage and would otherwise wait
+// for those loads; completion is awaited explicitly with lgkm_wait.
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_read_b128(uint32_t addr)
+{
+    u32x4 r;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF) : "memory");
+    return r;
+}
+template <int OFF>
+__device__ __forceinline__ u32x2 lds_read_tr16_b64(uint32_t addr)
+{
+    u32x2 r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF) : "memory");
+    return r;
+}
+
+// Wait until at most N LDS operations are outstanding; the operand is tied
+// to the wait so that its consumer cannot be scheduled above it.
+template <int N, typename T>
+__device__ __forceinline__ void lgkm_wait(T &v)
+{
+    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(v) : "n"(N));
+}
+
+// Direct 16-byte global->LDS load: lane l's 16 bytes land at lds + 16*l.
+__device__ __forceinline__ void dma16(const void *gsrc, void *lds)
+{
+    __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void *)lds, 16, 0,
+                                     0);
+}
+
+__device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Global loads/stores of 16 bytes.
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *(const u32x4 *)p; }

@@ -38,8 +38,6 @@
 //    mapped to the query tiles of one head (heaviest causal tile first): the
 //    head's K/V stays in that XCD's L2 ("GPU kernel overview" page,
 //    NUMA-aware attention entry: head-first chiplet swizzle).
-#include <type_traits>
-
 #include "attn_internal.hpp"
 #include "cdna4.hpp"
 
@@ -71,15 +69,6 @@ template <int D>
 __device__ __forceinline__ int vswz(int row)
 {
     return D >= 128 ? (row & 3) : ((row >> 1) & 1);
-}
-
-template <int I, int N, typename F>
-__device__ __forceinline__ void static_for(F &&f)
-{
-    if constexpr (I < N) {
-        f(std::integral_constant<int, I>{});
-        static_for<I + 1, N>(f);
-    }
 }
 
 // Direct global->LDS loads of one K tile (padded rows): LDS slot p of the
@@ -121,38 +110,6 @@ __device__ __forceinline__ void issue_v(unsigned char *lds_tile, const uint16_t 
             (const void *)(src + (size_t)grow * D + c * 8),
             (__attribute__((address_space(3))) void *)(lds_tile + piece * 1024), 16, 0, 0);
     }
-}
-
-// LDS byte address of a __shared__ pointer.
-__device__ __forceinline__ uint32_t lds_addr(const void *p)
-{
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
-}
-
-// LDS reads issued as inline asm: the compiler cannot tell them from the
-// next stage's in-flight direct loads and would otherwise wait for those.
-// Their completion is awaited explicitly with lgkm_wait.
-template <int OFF>
-__device__ __forceinline__ u32x4 lds_read_b128(uint32_t addr)
-{
-    u32x4 r;
-    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF) : "memory");
-    return r;
-}
-template <int OFF>
-__device__ __forceinline__ u32x2 lds_read_tr16_b64(uint32_t addr)
-{
-    u32x2 r;
-    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF) : "memory");
-    return r;
-}
-
-// Wait until at most N LDS operations are outstanding; the operand is tied
-// to the wait so that its consumer cannot be scheduled above it.
-template <int N>
-__device__ __forceinline__ void lgkm_wait(u32x4 &v)
-{
-    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(v) : "n"(N));
 }
 
 // Per-wave running state of the online softmax and the output accumulator.
