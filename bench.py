@@ -146,12 +146,42 @@ def bench_decode(args, stream):
     }
 
 
+def bench_sage(args, stream):
+    import softmax_attention_attn_amd as A
+    w = workloads.WORKLOADS["sage_prefill"]
+    inp = workloads.make(w)
+    q, k, v = inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda()
+    del inp
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    ws = torch.empty((A.attn_fwd_workspace_size(w.B, w.H, w.Hkv, w.N, w.d, A.MODES["sage"]),),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        A.fwd(q, k, v, causal=w.causal, mode="sage", o=o, lse=lse, workspace=ws, stream=stream)
+
+    ms, per_kernel = time_calls(step, max(5, args.steps // 2), args.warmup, stream)
+    ops = w.flops()
+    kms = per_kernel["sage_attn"][0]
+    achieved = ops / (kms * 1e-3) / 1e12
+    return {
+        "workload": w.name, "value": ops / (ms * 1e-3) / 1e12, "unit": "TOP/s",
+        "ms_per_step": ms, "note": "INT8 QK^T + FP8 PV MFMA; value includes the quantisation "
+                                   "prologue kernels, the roofline the fused attention kernel",
+        "kernels_ms": {k_: t for k_, (t, _) in per_kernel.items()},
+        "roofline": {"bound": "mfma", "kernel": "sage_attn", "achieved": achieved,
+                     "peak": PEAK_FP8_TFLOPS, "unit": "TOP/s", "frac": achieved / PEAK_FP8_TFLOPS,
+                     "kernel_ms": kms,
+                     "traffic": measured_traffic("sage_attn", ["sage.hip", "cdna4.hpp"])},
+    }
+
+
 def cpu_baseline(w, q, k, v):
-    """fp64 oracle on every 4th query row of every (b, h) slice of the
-    headline workload; its throughput in the headline's unit."""
+    """fp64 oracle over every query row of the headline workload; its
+    throughput in the headline's unit."""
     import oracle
     oracle.build(force=False)
-    rows = np.arange(0, w.B * w.H * w.N, 4, dtype=np.int64)
+    rows = np.arange(0, w.B * w.H * w.N, 1, dtype=np.int64)
     i = rows % w.N
     flops = float(np.sum(4.0 * w.d * (i + 1 if w.causal else w.N)))
     threads = oracle.default_threads()
@@ -160,7 +190,7 @@ def cpu_baseline(w, q, k, v):
     oracle.attn_rows(qb, kb, vb, causal=w.causal, scale=w.scale, rows=rows, threads=threads)
     dt = time.perf_counter() - t0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": "fp64 C oracle, every 4th query row of all %d (b,h) slices of %s "
+            "sample": "fp64 C oracle, every query row of all %d (b,h) slices of %s "
                       "(%d rows, %.3g FLOP) in %.1f s" % (w.B * w.H, w.name, len(rows), flops, dt)}
 
 
@@ -203,6 +233,13 @@ def main():
         log("prefill: llm_prefill")
         pre = bench_prefill(args, stream)
         log("prefill %.3f ms/step, %.1f TFLOP/s" % (pre["ms_per_step"], pre["value"]))
+    if args.only in (None, "sage"):
+        log("sage: sage_prefill")
+        sg = bench_sage(args, stream)
+        log("sage %.3f ms/step, %.1f TOP/s (attention kernel %.1f TOP/s)" % (
+            sg["ms_per_step"], sg["value"], sg["roofline"]["achieved"]))
+        out["sage"] = sg
+        torch.cuda.empty_cache()
     if args.only in (None, "decode"):
         log("decode: gqa_decode")
         dec = bench_decode(args, stream)

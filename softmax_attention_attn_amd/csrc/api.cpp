@@ -175,12 +175,9 @@ attn_status attn_decode(const void *q, const void *k_cache, const void *v_cache,
     if (d != 64 && d != 128)
         return fail(ATTN_ERR_UNSUPPORTED, "head dim d=%d (supported: 64, 128)", d);
     const int G = H / Hkv;
-    if (G != 1 && G != 2 && G != 4 && G != 8)
-        return fail(ATTN_ERR_UNSUPPORTED, "query heads per kv head %d (supported: 1, 2, 4, 8)", G);
-    if ((long long)G * split_tokens > 4096)
+    if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
         return fail(ATTN_ERR_UNSUPPORTED,
-                    "split_tokens=%d too large for %d heads per kv head (G*split <= 4096)",
-                    split_tokens, G);
+                    "query heads per kv head %d (supported: 1, 2, 4, 8, 16)", G);
     const long long splits = ((long long)N_max + split_tokens - 1) / split_tokens;
     if (splits > 0x7fffffffLL || Hkv > 65535 || B > 65535)
         return fail(ATTN_ERR_UNSUPPORTED, "problem too large for the grid mapping");

@@ -1,63 +1,25 @@
 // Split-KV GQA decode for gfx950 (Flash-Decoding, "flashattention-kernels"
 // page §3; GQA from the "cuda-kernel-pretrain" page §3).
 //
-// decode_split_kernel: one workgroup per (chunk, kv head, sequence).  It
-// streams its chunk of the K and V caches exactly once for all G = H/Hkv query
-// heads of the group (the GQA saving: each cache byte is read once per group,
-// not once per query head), computes the chunk's scores, a local softmax and
-// the partial output O_s with its log2-domain LSE.  Workgroups whose chunk
-// starts at or beyond the sequence length exit at once.
+// decode_split_kernel: each wave owns one chunk of split_tokens keys of one
+// (sequence, kv head) and computes the chunk's partial attention for all
+// G = H/Hkv query heads of the group at once: each K/V cache byte is read
+// once per group, not once per query head (the GQA saving).  It writes the
+// partial output O_s (normalised by the chunk's own row sum) and its log2
+// LSE.  Chunks starting at or beyond the sequence length do no work.
 //
 // decode_merge_kernel: one workgroup per (sequence, query head) combines the
 // chunk partials with log-sum-exp weights into O and the natural-log LSE.
 //
-// The path is HBM bound (a few FLOPs per byte), so the kernels use plain fp32
-// VALU arithmetic and spend their effort on memory: 16-byte coalesced loads
-// (16 lanes read one 256-byte cache row), eight loads in flight per thread,
-// and no register spills.
+// The path is HBM bound (a few FLOPs per byte): the split kernel keeps two
+// sub-tiles of K and V in flight per wave (about 32 KB), uses the matrix
+// cores for the small products so the VALU stays free, and never stalls on
+// other waves.
 #include "attn_internal.hpp"
 #include "cdna4.hpp"
 
 namespace attn {
 namespace {
-
-constexpr int kThreads = 256;
-constexpr int kUnroll = 8;
-constexpr int kHeadsPerPass = 4;  // heads reduced per LDS pass
-
-// LDS bytes of decode_split_kernel: scores [G][S], row-group partials
-// [RPP][min(G,4)][D], per-head max and sum.
-inline size_t split_lds_bytes(int D, int G, int S)
-{
-    const int rpp = kThreads / (D / 8);
-    const int hp = G < kHeadsPerPass ? G : kHeadsPerPass;
-    return sizeof(float) * ((size_t)G * S + (size_t)rpp * hp * D + 2 * G);
-}
-
-template <int TPR>
-__device__ __forceinline__ float group_sum(float x)
-{
-#pragma unroll
-    for (int off = 1; off < TPR; off <<= 1)
-        x += __shfl_xor(x, off, 64);
-    return x;
-}
-
-__device__ __forceinline__ float wave_max(float x)
-{
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1)
-        x = fmaxf(x, __shfl_xor(x, off, 64));
-    return x;
-}
-
-__device__ __forceinline__ float wave_sum(float x)
-{
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1)
-        x += __shfl_xor(x, off, 64);
-    return x;
-}
 
 __device__ __forceinline__ int clamp_len(const int32_t *seqlens, int b, int n_max)
 {
@@ -65,153 +27,202 @@ __device__ __forceinline__ int clamp_len(const int32_t *seqlens, int b, int n_ma
     return L < 1 ? 1 : (L > n_max ? n_max : L);
 }
 
-// Dynamic LDS: see split_lds_bytes().
-template <int D, int G>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a)
-{
-    constexpr int TPR = D / 8;           // threads per cache row (16 bytes each)
-    constexpr int RPP = kThreads / TPR;  // rows per pass
-    extern __shared__ __attribute__((aligned(16))) float lds[];
-    const int S = a.split_tokens;
-    float *sc = lds;                  // [G][S]
-    constexpr int HP = G < kHeadsPerPass ? G : kHeadsPerPass;
-    float *red = lds + G * S;          // [RPP][HP][D]
-    float *stat = red + RPP * HP * D;  // [2][G]
+// One 512-token (split_tokens) chunk per wave.  The wave streams its chunk
+// in sub-tiles of kSub keys: K straight into the registers of the MFMA A
+// operand, V into a 3-stage LDS ring of this wave through direct loads; both
+// run two sub-tiles ahead.  S^T = K q^T and O^T += V^T P^T run on
+// v_mfma_f32_16x16x32_bf16 with the G query heads of the group as the MFMA
+// columns (columns >= G are zero), so the chunk's keys are read once for all
+// G heads.  Waves never synchronise with each other.
+constexpr int kSub = 32;       // keys per sub-tile
+constexpr int kVStages = 3;
+constexpr int kWavesPerWG = 4;
 
-    const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+template <int D>
+struct DCfg {
+    static constexpr int kVBytes = kSub * D * 2;   // one V sub-tile
+    static constexpr int kChunks = D / 8;          // 16-byte chunks per row
+    static constexpr int kVPieces = kVBytes / 1024;
+};
+
+// V sub-tile: 16-byte chunk c of row r is stored at chunk c ^ (2 * (r & 7))
+// (mod the row's chunk count), so the 8 rows x 32 bytes that 32 lanes read
+// with one transposing read fall on distinct bank slots.
+template <int D>
+__device__ __forceinline__ int dvswz(int r)
+{
+    return (2 * (r & 7)) & (DCfg<D>::kChunks - 1);
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(64 * kWavesPerWG) void decode_split_kernel(DecodeArgs a)
+{
+    __shared__ __attribute__((aligned(1024)))
+    unsigned char vlds[kWavesPerWG][kVStages][DCfg<D>::kVBytes];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int kvh = blockIdx.y, b = blockIdx.z;
+    const int split = blockIdx.x * kWavesPerWG + wave;
     const int L = clamp_len(a.seqlens, b, a.N_max);
+    const int S = a.split_tokens;
     const int c0 = split * S;
-    if (c0 >= L)
-        return;
+    if (split >= a.max_splits || c0 >= L)
+        return;  // this wave's chunk is empty (no barrier follows)
     const int n = min(S, L - c0);
-    const int tid = threadIdx.x, fc = tid % TPR, rg = tid / TPR;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int nsub = (n + kSub - 1) / kSub;
+    const int col = lane & 15, G4 = lane >> 4;  // MFMA column (head) and lane group
     const size_t cache_off = ((size_t)(b * a.Hkv + kvh) * a.N_max + c0) * D;
     const uint16_t *kb = (const uint16_t *)a.k + cache_off;
     const uint16_t *vb = (const uint16_t *)a.v + cache_off;
+    unsigned char *vst = &vlds[wave][0][0];
+
+    // q^T fragments (B operand of QK): lane holds q[head col][32*ks + 8*G4 .. +7]
+    bf16x8 qf[D / 32];
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks)
+        qf[ks] = as_bf16x8(col < G ? ld16((const uint16_t *)a.q +
+                                          ((size_t)b * a.H + kvh * G + col) * D + 32 * ks + 8 * G4)
+                                   : u32x4{0, 0, 0, 0});
+
+    // K sub-tile into registers: MFMA (blk, ks) A operand = row 16*blk + col,
+    // features 32*ks + 8*G4 .. +7.  Rows past the chunk re-read its last row.
+    auto load_k = [&](int i, u32x4 (&kr)[2][D / 32]) {
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            const int row = min(i * kSub + 16 * blk + col, n - 1);
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks)
+                kr[blk][ks] = ld16(kb + (size_t)row * D + 32 * ks + 8 * G4);
+        }
+    };
+    // V sub-tile into LDS stage i % 3 (row-major rows of D bf16, swizzled)
+    auto load_v = [&](int i) {
+        unsigned char *dst = vst + (i % kVStages) * DCfg<D>::kVBytes;
+        constexpr int C = DCfg<D>::kChunks;
+#pragma unroll
+        for (int piece = 0; piece < DCfg<D>::kVPieces; ++piece) {
+            const int p = piece * 64 + lane;
+            const int r = p / C;
+            const int c = (p % C) ^ dvswz<D>(r);
+            const int row = min(i * kSub + r, n - 1);
+            dma16(vb + (size_t)row * D + c * 8, dst + piece * 1024);
+        }
+    };
+
+    u32x4 kr0[2][D / 32], kr1[2][D / 32], kr2[2][D / 32];
+    load_k(0, kr0);
+    load_v(0);
+    if (nsub > 1) {
+        load_k(1, kr1);
+        load_v(1);
+    }
     const float cs = a.scale * kLog2e;
+    float m = -INFINITY, l = 0.f;
+    f32x4 o[D / 16];
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+        o[c] = f32x4{};
+    // per-lane transposing-read offset: lane 4j + q of its 16-lane group
+    // reads key row (base + j), features 16c + 4q .. +3
+    const int trl = lane & 15, trj = trl >> 2, trq = trl & 3;
 
-    // q fragment of every head of the group, features fc*8 .. fc*8+7
-    float qv[G][8];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        u32x4 w = ld16((const uint16_t *)a.q + ((size_t)b * a.H + kvh * G + h) * D + fc * 8);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            qv[h][2 * e] = bf16_lo(w[e]) * cs;
-            qv[h][2 * e + 1] = bf16_hi(w[e]) * cs;
+    // sub-tile i: K in registers k (loaded two sub-tiles earlier), V in LDS
+    // stage i % 3; the loads of sub-tile i+2 go to kn and stage (i+2) % 3
+    auto step = [&](int i, const u32x4(&k)[2][D / 32], u32x4(&kn)[2][D / 32]) {
+        // sub-tile i has landed when at most the loads of sub-tile i+1 are pending
+        if (i + 1 < nsub)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (D / 32) + DCfg<D>::kVPieces) : "memory");
+        else
+            vm_wait_all();
+        if (i + 2 < nsub) {
+            load_k(i + 2, kn);
+            load_v(i + 2);
         }
-    }
-
-    // scores (log2 domain) of every key of the chunk
-    for (int r0 = 0; r0 < n; r0 += RPP * kUnroll) {
-        u32x4 kw[kUnroll];
+        // S^T = K q^T: lane holds head col, keys 16*blk + 4*G4 + r
+        f32x4 s[2] = {f32x4{}, f32x4{}};
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            int row = r0 + u * RPP + rg;
-            kw[u] = row < n ? ld16(kb + (size_t)row * D + fc * 8) : u32x4{0, 0, 0, 0};
-        }
+        for (int ks = 0; ks < D / 32; ++ks)
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            int row = r0 + u * RPP + rg;
-            float kf[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                kf[2 * e] = bf16_lo(kw[u][e]);
-                kf[2 * e + 1] = bf16_hi(kw[u][e]);
-            }
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-                float dot = 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    dot = fmaf(qv[h][e], kf[e], dot);
-                dot = group_sum<TPR>(dot);
-                if (fc == 0 && row < n)
-                    sc[h * S + row] = dot;
-            }
-        }
-    }
-    __syncthreads();
-
-    // chunk-local softmax per head: p = 2^(s - m), l = sum p
-    for (int h = wave; h < G; h += kThreads / 64) {
+            for (int blk = 0; blk < 2; ++blk)
+                s[blk] = mfma_bf16_16x16x32(as_bf16x8(k[blk][ks]), qf[ks], s[blk]);
         float mx = -INFINITY;
-        for (int j = lane; j < n; j += 64)
-            mx = fmaxf(mx, sc[h * S + j]);
-        mx = wave_max(mx);
-        float sum = 0.f;
-        for (int j = lane; j < n; j += 64) {
-            float p = fast_exp2(sc[h * S + j] - mx);
-            sc[h * S + j] = p;
-            sum += p;
-        }
-        sum = wave_sum(sum);
-        if (lane == 0) {
-            stat[h] = mx;
-            stat[G + h] = sum;
-        }
-    }
-    __syncthreads();
-
-    // partial P V: thread accumulates features fc*8..+7 over rows rg, rg+RPP, ...
-    float acc[G][8];
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+        for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            acc[h][e] = 0.f;
-    for (int r0 = 0; r0 < n; r0 += RPP * kUnroll) {
-        u32x4 vw[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            int row = r0 + u * RPP + rg;
-            vw[u] = row < n ? ld16(vb + (size_t)row * D + fc * 8) : u32x4{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            int row = r0 + u * RPP + rg;
-            if (row < n) {
-                float vf[8];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    vf[2 * e] = bf16_lo(vw[u][e]);
-                    vf[2 * e + 1] = bf16_hi(vw[u][e]);
-                }
-#pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    float p = sc[h * S + row];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        acc[h][e] = fmaf(p, vf[e], acc[h][e]);
-                }
+            for (int r = 0; r < 4; ++r) {
+                const int key = i * kSub + 16 * blk + 4 * G4 + r;
+                s[blk][r] = key < n ? s[blk][r] * cs : -INFINITY;
+                mx = fmaxf(mx, s[blk][r]);
             }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        // lazy rescale (the reference max moves only by more than 2^8); the
+        // first sub-tile always has a visible key
+        if (__any(mx > m + 8.f)) {
+            const float m_new = mx > m + 8.f ? mx : m;
+            const float alpha = fast_exp2(m - m_new);
+            l *= alpha;
+#pragma unroll
+            for (int c = 0; c < D / 16; ++c)
+                o[c] *= alpha;
+            m = m_new;
         }
+        // P^T B operand: element e is key 16*(e/4) + 4*G4 + e%4
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            p[e] = fast_exp2(s[e >> 2][e & 3] - m);
+            l += p[e];
+        }
+        const u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                          pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+        // O^T += V^T P^T: per 16-feature block c, the A operand is keys
+        // 4*G4 + 0..3 and 16 + 4*G4 + 0..3 of features 16c + col, gathered by
+        // two transposing reads
+        const uint32_t vbase = lds_addr(vst + (i % kVStages) * DCfg<D>::kVBytes);
+        auto vaddr = [&](int row, int c) {
+            const int chunk = 2 * c + (trq >> 1);
+            return vbase + row * (D * 2) + ((chunk ^ dvswz<D>(row)) << 4) + (trq & 1) * 8;
+        };
+        u32x4 va[2];
+        auto read_va = [&](int c) -> u32x4 {
+            const u32x2 w0 = lds_read_tr16_b64<0>(vaddr(4 * G4 + trj, c));
+            const u32x2 w1 = lds_read_tr16_b64<0>(vaddr(16 + 4 * G4 + trj, c));
+            return u32x4{w0[0], w0[1], w1[0], w1[1]};
+        };
+        va[0] = read_va(0);
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) {
+            if (c + 1 < D / 16) {
+                va[(c + 1) & 1] = read_va(c + 1);
+                lgkm_wait<2>(va[c & 1]);
+            } else {
+                lgkm_wait<0>(va[c & 1]);
+            }
+            o[c] = mfma_bf16_16x16x32(as_bf16x8(va[c & 1]), as_bf16x8(pw), o[c]);
+        }
+    };
+    for (int i = 0; i < nsub; i += 3) {
+        step(i, kr0, kr2);
+        if (i + 1 < nsub)
+            step(i + 1, kr1, kr0);
+        if (i + 2 < nsub)
+            step(i + 2, kr2, kr1);
     }
-    // reduce the RPP row-group partials through LDS, four heads at a time
+
+    // partial of this chunk: O_s = acc / l, lse_s = m + log2 l (log2 units);
+    // lane holds head col, features 16c + 4*G4 + r
+    float lt = l + __shfl_xor(l, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+    if (col < G) {
+        const float inv = 1.f / lt;
+        const size_t pidx = ((size_t)b * a.H + kvh * G + col) * a.max_splits + split;
+        float *po = a.part_o + pidx * D;
 #pragma unroll
-    for (int hg = 0; hg < G; hg += kHeadsPerPass) {
-#pragma unroll
-        for (int hh = 0; hh < HP; ++hh)
-#pragma unroll
-            for (int e = 0; e < 8; e += 4)
-                *(f32x4 *)(red + ((size_t)rg * HP + hh) * D + fc * 8 + e) =
-                    f32x4{acc[hg + hh][e], acc[hg + hh][e + 1], acc[hg + hh][e + 2],
-                          acc[hg + hh][e + 3]};
-        __syncthreads();
-        for (int idx = tid; idx < HP * D; idx += kThreads) {
-            const int hh = idx / D, dd = idx % D, h = hg + hh;
-            float sum = 0.f;
-#pragma unroll 4
-            for (int r = 0; r < RPP; ++r)
-                sum += red[((size_t)r * HP + hh) * D + dd];
-            const float l = stat[G + h];
-            const size_t pidx = ((size_t)b * a.H + kvh * G + h) * a.max_splits + split;
-            a.part_o[pidx * D + dd] = sum / l;
-            if (dd == 0)
-                a.part_lse[pidx] = stat[h] + log2f(l);
-        }
-        __syncthreads();
+        for (int c = 0; c < D / 16; ++c)
+            *(f32x4 *)(po + 16 * c + 4 * G4) =
+                f32x4{o[c][0] * inv, o[c][1] * inv, o[c][2] * inv, o[c][3] * inv};
+        if (G4 == 0)
+            a.part_lse[pidx] = m + log2f(lt);
     }
 }
 
@@ -244,10 +255,9 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a)
 template <int D, int G>
 hipError_t launch_split(const DecodeArgs &a, hipStream_t s)
 {
-    const size_t lds = split_lds_bytes(D, G, a.split_tokens);
-    dim3 grid(a.max_splits, a.Hkv, a.B);
+    dim3 grid((a.max_splits + kWavesPerWG - 1) / kWavesPerWG, a.Hkv, a.B);
     ProfScope ps("decode_split", s);
-    hipLaunchKernelGGL((decode_split_kernel<D, G>), grid, dim3(kThreads), lds, s, a);
+    hipLaunchKernelGGL((decode_split_kernel<D, G>), grid, dim3(64 * kWavesPerWG), 0, s, a);
     return hipGetLastError();
 }
 
@@ -259,7 +269,8 @@ hipError_t launch_d(const DecodeArgs &a, hipStream_t s)
     case 1: e = launch_split<D, 1>(a, s); break;
     case 2: e = launch_split<D, 2>(a, s); break;
     case 4: e = launch_split<D, 4>(a, s); break;
-    default: e = launch_split<D, 8>(a, s); break;
+    case 8: e = launch_split<D, 8>(a, s); break;
+    default: e = launch_split<D, 16>(a, s); break;
     }
     if (e != hipSuccess)
         return e;

@@ -75,8 +75,8 @@ def _dec(A, **kw):
     (dict(seqlens=None), -1), (dict(k_cache=None), -1), (dict(B=0), -1), (dict(H=7), -1),
     (dict(H=6), -2),
     (dict(scale=-1.0), -1), (dict(split_tokens=0), -1), (dict(split_tokens=100), -1),
-    (dict(mode=1), -2), (dict(mode=5), -1), (dict(d=80), -2), (dict(H=24, Hkv=2), -2),
-    (dict(split_tokens=1024, H=16), -2), (dict(workspace=None), -3),
+    (dict(mode=1), -2), (dict(mode=5), -1), (dict(d=80), -2), (dict(H=24, Hkv=2), -2), (dict(H=64, Hkv=2), -2),
+    (dict(workspace=None), -3),
     (dict(workspace_bytes=1000), -3),
 ])
 def test_decode_validation(A, kw, status):

@@ -39,6 +39,7 @@ CASES = [
     (2, 4, 4, 700, 64, (700, 129), 128),
     (2, 16, 2, 300, 128, (300, 17), 256),
     (4, 2, 1, 2048, 128, (2048, 1, 1536, 777), 512),
+    (2, 32, 2, 1100, 128, (1100, 31), 128),
 ]
 
 
@@ -71,8 +72,11 @@ def test_split_size_invariance(attn):
                              out_dtype=torch.float32)
         torch.cuda.synchronize()
         outs.append((o.cpu().numpy(), lse.cpu().numpy()))
+    # P is rounded to bf16 relative to each chunk's own max before the PV
+    # product, so chunkings agree to bf16 precision (each is checked against
+    # the oracle elsewhere); the LSE does not see that rounding
     for o, lse in outs[1:]:
-        assert np.abs(o - outs[0][0]).max() < 1e-5
+        assert np.abs(o - outs[0][0]).max() < 2e-3
         assert np.abs(lse - outs[0][1]).max() < 1e-5
 
 
