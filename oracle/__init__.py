@@ -105,7 +105,14 @@ def _ptr(a, t):
 
 
 def default_threads() -> int:
-    return len(os.sched_getaffinity(0))
+    """Host threads for the oracle: the affinity mask, capped by
+    OMP_NUM_THREADS (else 16) so that a shared host is not oversubscribed."""
+    n = len(os.sched_getaffinity(0))
+    try:
+        cap = int(os.environ.get("OMP_NUM_THREADS", "16"))
+    except ValueError:
+        cap = 16
+    return max(1, min(n, cap if cap > 0 else 16))
 
 
 def attn_rows(q, k, v, *, causal: bool, scale: float, rows=None, kv_len=None,

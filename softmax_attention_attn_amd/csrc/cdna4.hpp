@@ -67,6 +67,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// acc + lo + hi of a packed bf16 pair (one v_dot2c_f32_bf16 against (1, 1)):
+// the sum of exactly the rounded values that enter a bf16 MFMA.
+__device__ __forceinline__ float add_bf16x2(uint32_t u, float acc)
+{
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u), ones, acc, false);
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 

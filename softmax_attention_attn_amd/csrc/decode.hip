@@ -116,7 +116,9 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void decode_split_kernel(DecodeAr
         load_v(1);
     }
     const float cs = a.scale * kLog2e;
-    float m = -INFINITY, l = 0.f;
+    // l: row sum of the unrounded p (for the LSE); lp: of the bf16-rounded p
+    // that enter the PV MFMA (normalises O, so the weights on V sum to one)
+    float m = -INFINITY, l = 0.f, lp = 0.f;
     f32x4 o[D / 16];
 #pragma unroll
     for (int c = 0; c < D / 16; ++c)
@@ -161,6 +163,7 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void decode_split_kernel(DecodeAr
             const float m_new = mx > m + 8.f ? mx : m;
             const float alpha = fast_exp2(m - m_new);
             l *= alpha;
+            lp *= alpha;
 #pragma unroll
             for (int c = 0; c < D / 16; ++c)
                 o[c] *= alpha;
@@ -175,6 +178,9 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void decode_split_kernel(DecodeAr
         }
         const u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
                           pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            lp = add_bf16x2(pw[e], lp);
         // O^T += V^T P^T: per 16-feature block c, the A operand is keys
         // 4*G4 + 0..3 and 16 + 4*G4 + 0..3 of features 16c + col, gathered by
         // two transposing reads
@@ -209,12 +215,14 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void decode_split_kernel(DecodeAr
             step(i + 2, kr2, kr1);
     }
 
-    // partial of this chunk: O_s = acc / l, lse_s = m + log2 l (log2 units);
+    // partial of this chunk: O_s = acc / lp, lse_s = m + log2 l (log2 units);
     // lane holds head col, features 16c + 4*G4 + r
     float lt = l + __shfl_xor(l, 16, 64);
     lt += __shfl_xor(lt, 32, 64);
+    float ltp = lp + __shfl_xor(lp, 16, 64);
+    ltp += __shfl_xor(ltp, 32, 64);
     if (col < G) {
-        const float inv = 1.f / lt;
+        const float inv = 1.f / ltp;
         const size_t pidx = ((size_t)b * a.H + kvh * G + col) * a.max_splits + split;
         float *po = a.part_o + pidx * D;
 #pragma unroll

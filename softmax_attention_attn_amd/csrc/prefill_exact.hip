@@ -118,6 +118,7 @@ struct WaveState {
     f32x16 o[D / 32];  // O^T accumulator: register r of lane (n, g) = O[query n][32c + 16g + r]
     float m;           // reference max of score * scale * log2(e), raised lazily
     float l;           // this lane's part of the row sum (its 16 of every 32 keys)
+    float lp;          // the same sum over the bf16-rounded P that enters the PV MFMA
 };
 
 // Per-lane LDS offsets of the MFMA operand reads (independent of the stage).
@@ -211,26 +212,6 @@ __device__ __forceinline__ void pv_tile(f32x16 (&o)[D / 32], const uint32_t (&pk
     });
 }
 
-// p = 2^(s*cs - m), rounded to bf16 for the PV product; the row sum is taken
-// over the unrounded fp32 values (a bf16-rounded sum would carry up to 2^-9
-// relative error into the LSE of rows with few keys).
-__device__ __forceinline__ void exp_tile(const f32x16 (&s)[2], float m, float cs,
-                                         uint32_t (&pk)[2][8], float &l)
-{
-    float rs0 = 0.f, rs1 = 0.f;
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-            const float p0 = fast_exp2(fmaf(s[blk][r], cs, -m));
-            const float p1 = fast_exp2(fmaf(s[blk][r + 1], cs, -m));
-            rs0 += p0;
-            rs1 += p1;
-            pk[blk][r >> 1] = pack_bf16x2(p0, p1);
-        }
-    l += rs0 + rs1;
-}
-
 __device__ __forceinline__ float tile_max(const f32x16 (&s)[2])
 {
     float mx = s[0][0];
@@ -266,6 +247,7 @@ __device__ __forceinline__ void update_max(WaveState<D> &st, float mx)
         const float m_new = mx > st.m + kRescaleLog2 ? mx : st.m;
         const float alpha = fast_exp2(st.m - m_new);
         st.l *= alpha;
+        st.lp *= alpha;
 #pragma unroll
         for (int c = 0; c < D / 32; ++c)
             st.o[c] *= alpha;
@@ -277,14 +259,19 @@ __device__ __forceinline__ void update_max(WaveState<D> &st, float mx)
 // followed by a slice of the exponentials of the current tile.  The two
 // 32-key accumulators alternate so that consecutive MFMAs are independent.
 // Each step exponentiates two scores and folds the two of the previous step
-// into the row sum and the bf16 P fragment (the exp latency is then covered
-// by the MFMA in between).  Steps are fenced with scheduling barriers and
+// into the row sums and the bf16 P fragment (the exp latency is then covered
+// by the MFMA in between).  p = 2^(s*cs - m) is rounded to bf16 for the PV
+// product, and two row sums are kept: l over the unrounded values, for the
+// LSE (a rounded sum would carry up to 2^-9 relative error into the LSE of
+// rows with few keys), and lp over the rounded values, for normalising O (the
+// weights applied to V then sum to one, so a row dominated by one key returns
+// that key's V row rather than V times the bf16 rounding error of its p).  Steps are fenced with scheduling barriers and
 // their results pinned, so the wave issues VALU work between its MFMAs
 // instead of in one block.
 template <int D>
 __device__ __forceinline__ void phase_a(f32x16 (&s_next)[2], const bf16x8 (&qf)[D / 16],
                                         uint32_t kaddr, const f32x16 (&s_cur)[2], float m,
-                                        float cs, uint32_t (&pk)[2][8], float &l)
+                                        float cs, uint32_t (&pk)[2][8], float &l, float &lp)
 {
     constexpr int KS = D / 16, NK = 2 * KS, KLA = 4;
     constexpr int EPS = 32 / NK;  // scores exponentiated per step
@@ -309,7 +296,8 @@ __device__ __forceinline__ void phase_a(f32x16 (&s_next)[2], const bf16x8 (&qf)[
             rs0 += p0;
             rs1 += p1;
             pk[blk][r >> 1] = pack_bf16x2(p0, p1);
-            asm volatile("" : "+v"(pk[blk][r >> 1]), "+v"(rs0), "+v"(rs1));
+            lp = add_bf16x2(pk[blk][r >> 1], lp);
+            asm volatile("" : "+v"(pk[blk][r >> 1]), "+v"(rs0), "+v"(rs1), "+v"(lp));
         });
     };
     static_for<0, KLA>([&](auto i) { kv[decltype(i)::value] = kread(i); });
@@ -435,6 +423,7 @@ __device__ __forceinline__ void attend_qtile(const PrefillArgs &a, unsigned char
         st.o[c] = f32x16{};
     st.m = -INFINITY;
     st.l = 0.f;
+    st.lp = 0.f;
     const float cs = a.scale * kLog2e;
 
     // Software pipeline: iteration t runs the QK MFMAs of tile t+1 next to
@@ -462,7 +451,8 @@ __device__ __forceinline__ void attend_qtile(const PrefillArgs &a, unsigned char
         // QK(t+1) also runs when this wave does not need tile t+1 (the result
         // is then dropped) so that phase A has no branch.
         uint32_t pk[2][8];
-        phase_a<D>(s_next, qf, lds_addr(kst(t + 1)) + off.k, s_cur, st.m, cs, pk, st.l);
+        phase_a<D>(s_next, qf, lds_addr(kst(t + 1)) + off.k, s_cur, st.m, cs, pk, st.l,
+                   st.lp);
         const bool more = t + 1 < ntw;
         if (more && needs_mask(t + 1))
             mask_tile<CAUSAL>(s_next, (t + 1) * kBN, N, g, my_q);
@@ -477,8 +467,9 @@ __device__ __forceinline__ void attend_qtile(const PrefillArgs &a, unsigned char
     }
 
     const float lt = sum_xor32(st.l);
+    const float ltp = sum_xor32(st.lp);
     if (my_q < N) {
-        const float inv = 1.f / lt;
+        const float inv = 1.f / ltp;
         if constexpr (OUT_F32) {
             float *orow = (float *)a.o + ((size_t)bh * N + my_q) * D;
 #pragma unroll
