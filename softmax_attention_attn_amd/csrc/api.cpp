@@ -179,7 +179,8 @@ attn_status attn_decode(const void *q, const void *k_cache, const void *v_cache,
         return fail(ATTN_ERR_UNSUPPORTED,
                     "query heads per kv head %d (supported: 1, 2, 4, 8, 16)", G);
     const long long splits = ((long long)N_max + split_tokens - 1) / split_tokens;
-    if (splits > 0x7fffffffLL || Hkv > 65535 || B > 65535)
+    // one wave per possible chunk (an int index) and one merge workgroup per (b, h)
+    if ((long long)B * Hkv * splits > 0x7fffff00LL || (long long)B * H > 0x7fffffffLL)
         return fail(ATTN_ERR_UNSUPPORTED, "problem too large for the grid mapping");
     const size_t need = attn_decode_workspace_size(B, H, N_max, d, split_tokens);
     if (!workspace || workspace_bytes < need)

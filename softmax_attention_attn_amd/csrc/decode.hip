@@ -27,6 +27,47 @@ __device__ __forceinline__ int clamp_len(const int32_t *seqlens, int b, int n_ma
     return L < 1 ? 1 : (L > n_max ? n_max : L);
 }
 
+// Work items are the non-empty chunks, ordered by sequence, then kv head,
+// then chunk, and item i goes to wave i of the grid.  Consecutive workgroups
+// land on consecutive XCDs, so every XCD gets an equal share of the chunks
+// whatever the length mix (a grid over (chunk, kv head, sequence) would give
+// the XCDs that own high chunk indices nothing to do on short sequences).
+// The wave maps its item to (b, kvh, split) with a wave-wide prefix sum of
+// the per-sequence item counts, 64 sequences at a time.
+__device__ __forceinline__ bool locate_item(const DecodeArgs &a, int item, int lane, int &b,
+                                            int &kvh, int &split, int &L)
+{
+    const int S = a.split_tokens;
+    int base = 0;  // items of the sequences before b0
+    for (int b0 = 0; b0 < a.B; b0 += 64) {
+        const int bb = b0 + lane;
+        const int nch = bb < a.B ? (clamp_len(a.seqlens, bb, a.N_max) + S - 1) / S : 0;
+        const int cnt = a.Hkv * nch;
+        int inc = cnt;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int t = __shfl_up(inc, off, 64);
+            if (lane >= off)
+                inc += t;
+        }
+        const int total = __shfl(inc, 63, 64);
+        if (item < base + total) {
+            const unsigned long long m = __ballot(base + inc > item);
+            const int l = __builtin_ctzll(m);  // first sequence whose items reach past item
+            const int excl = __shfl(inc - cnt, l, 64);
+            const int nch_l = __shfl(nch, l, 64);
+            b = b0 + l;
+            L = clamp_len(a.seqlens, b, a.N_max);
+            const int r = item - base - excl;
+            kvh = r / nch_l;
+            split = r - kvh * nch_l;
+            return true;
+        }
+        base += total;
+    }
+    return false;
+}
+
 // One 512-token (split_tokens) chunk per wave.  The wave streams its chunk
 // in sub-tiles of kSub keys: K straight into the registers of the MFMA A
 // operand, V into a 3-stage LDS ring of this wave through direct loads; both
@@ -60,13 +101,11 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void decode_split_kernel(DecodeAr
     __shared__ __attribute__((aligned(1024)))
     unsigned char vlds[kWavesPerWG][kVStages][DCfg<D>::kVBytes];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int kvh = blockIdx.y, b = blockIdx.z;
-    const int split = blockIdx.x * kWavesPerWG + wave;
-    const int L = clamp_len(a.seqlens, b, a.N_max);
     const int S = a.split_tokens;
+    int b, kvh, split, L;
+    if (!locate_item(a, (int)blockIdx.x * kWavesPerWG + wave, lane, b, kvh, split, L))
+        return;  // past the last chunk (no barrier follows)
     const int c0 = split * S;
-    if (split >= a.max_splits || c0 >= L)
-        return;  // this wave's chunk is empty (no barrier follows)
     const int n = min(S, L - c0);
     const int nsub = (n + kSub - 1) / kSub;
     const int col = lane & 15, G4 = lane >> 4;  // MFMA column (head) and lane group
@@ -263,7 +302,9 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a)
 template <int D, int G>
 hipError_t launch_split(const DecodeArgs &a, hipStream_t s)
 {
-    dim3 grid((a.max_splits + kWavesPerWG - 1) / kWavesPerWG, a.Hkv, a.B);
+    // one wave per possible chunk; waves past the last non-empty chunk exit
+    const long long items = (long long)a.B * a.Hkv * a.max_splits;
+    dim3 grid((unsigned)((items + kWavesPerWG - 1) / kWavesPerWG));
     ProfScope ps("decode_split", s);
     hipLaunchKernelGGL((decode_split_kernel<D, G>), grid, dim3(64 * kWavesPerWG), 0, s, a);
     return hipGetLastError();
