@@ -163,6 +163,31 @@ __device__ __forceinline__ void dma16(const void *gsrc, void *lds)
                                      0);
 }
 
+// Buffer resource for raw byte-addressed loads from [base, base + nbytes):
+// loads at offsets >= nbytes return zero without touching memory.  base and
+// nbytes must be wave-uniform (the resource lives in scalar registers).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void *base, uint32_t nbytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)nbytes,
+                                             0x00020000);
+}
+
+// 16-byte direct load through a buffer resource into LDS: lane l's bytes
+// [voff, voff + 16) land at lds + 16 * l (lds wave-uniform).
+__device__ __forceinline__ void dma16_rsrc(__amdgpu_buffer_rsrc_t r, uint32_t voff, void *lds)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16,
+                                             voff, 0, 0, 0);
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void vm_wait_n()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 __device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Global loads/stores of 16 bytes.

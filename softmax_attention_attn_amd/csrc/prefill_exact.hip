@@ -71,45 +71,75 @@ __device__ __forceinline__ int vswz(int row)
     return D >= 128 ? (row & 3) : ((row >> 1) & 1);
 }
 
-// Direct global->LDS loads of one K tile (padded rows): LDS slot p of the
-// tile (16 bytes) is row p / (C+1), chunk p % (C+1); the pad chunk re-reads
-// chunk 0.  Rows past the sequence end re-read the last valid row (finite
-// data; those keys are masked).  Waves take the 1 KB pieces round robin.
+// Direct global->LDS loads.  Each tile is split into 1 KB pieces that the
+// waves take round robin (piece p = wave + kWaves * i); lane l of piece p
+// fills LDS slot 64p + l (16 bytes).
+//  * K tile, padded rows: slot q is row q / (C+1), chunk q % (C+1); the pad
+//    chunk re-reads chunk 0.
+//  * V tile: slot q is row q / C, physical chunk q % C, which holds logical
+//    chunk (q % C) ^ (vswz(row) << 2).
+// A lane's source offset within the tile is the same for every tile, so it is
+// computed once (DmaLanes); a tile's loads go through a buffer resource whose
+// base is the tile and whose size stops at the sequence end, so on a ragged
+// last tile the rows past the end read as zero (those keys are masked).
 template <int D>
-__device__ __forceinline__ void issue_k(unsigned char *lds_tile, const uint16_t *src, int k0, int N,
-                                        int wave, int lane)
+struct DmaLanes {
+    static constexpr int kKMax = (Cfg<D>::kKPieces + kWaves - 1) / kWaves;
+    uint32_t k[kKMax];  // byte offset of the lane's 16 bytes within the K tile
+    uint32_t v;         // the same for V piece `wave` (piece wave + kWaves*i adds i * kWaves KB)
+};
+
+template <int D>
+__device__ __forceinline__ DmaLanes<D> dma_lanes(int wave, int lane)
 {
     constexpr int C = Cfg<D>::kChunks;
-    for (int piece = wave; piece < Cfg<D>::kKPieces; piece += kWaves) {
-        const int p = piece * 64 + lane;
-        const int row = p / (C + 1);
-        int c = p % (C + 1);
-        c = c == C ? 0 : c;
-        const int grow = min(k0 + row, N - 1);
-        __builtin_amdgcn_global_load_lds(
-            (const void *)(src + (size_t)grow * D + c * 8),
-            (__attribute__((address_space(3))) void *)(lds_tile + piece * 1024), 16, 0, 0);
+    DmaLanes<D> dl;
+#pragma unroll
+    for (int i = 0; i < DmaLanes<D>::kKMax; ++i) {
+        const int q = (wave + kWaves * i) * 64 + lane;
+        const int row = q / (C + 1), c = q % (C + 1);
+        dl.k[i] = row * (D * 2) + (c == C ? 0 : c) * 16;
+    }
+    // a V piece is 1 KB of whole rows, and vswz depends only on the row modulo
+    // 4 (a multiple of a piece's row count), so pieces differ by a constant
+    static_assert(64 % Cfg<D>::kChunks == 0 && (64 / Cfg<D>::kChunks) % 4 == 0, "V piece rows");
+    {
+        const int q = wave * 64 + lane;
+        const int row = q / C;
+        dl.v = row * (D * 2) + ((q % C) ^ (vswz<D>(row) << 2)) * 16;
+    }
+    return dl;
+}
+
+// the tile of kBN rows at key k0 (k0 < N), cut at the sequence end
+template <int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t *src, int k0, int N)
+{
+    return raw_rsrc(src + (size_t)k0 * D, (uint32_t)min(kBN, N - k0) * (D * 2));
+}
+
+// this wave's pieces of the K tile at key k0 (wave is wave-uniform)
+template <int D>
+__device__ __forceinline__ void issue_k(unsigned char *lds_tile, const uint16_t *src, int k0, int N,
+                                        int wave, const DmaLanes<D> &dl)
+{
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc<D>(src, k0, N);
+#pragma unroll
+    for (int i = 0; i < DmaLanes<D>::kKMax; ++i) {
+        const int piece = wave + kWaves * i;
+        if (piece < Cfg<D>::kKPieces)
+            dma16_rsrc(r, dl.k[i], lds_tile + piece * 1024);
     }
 }
 
-// Direct loads of one V tile: LDS slot p is row p / C, physical chunk p % C,
-// which holds logical chunk (p % C) ^ (vswz(row) << 2).
 template <int D>
 __device__ __forceinline__ void issue_v(unsigned char *lds_tile, const uint16_t *src, int k0, int N,
-                                        int wave, int lane)
+                                        int wave, const DmaLanes<D> &dl)
 {
-    constexpr int C = Cfg<D>::kChunks;
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc<D>(src, k0, N);
 #pragma unroll
-    for (int i = 0; i < Cfg<D>::kVPieces / kWaves; ++i) {
-        const int piece = wave + i * kWaves;
-        const int p = piece * 64 + lane;
-        const int row = p / C;
-        const int c = (p % C) ^ (vswz<D>(row) << 2);
-        const int grow = min(k0 + row, N - 1);
-        __builtin_amdgcn_global_load_lds(
-            (const void *)(src + (size_t)grow * D + c * 8),
-            (__attribute__((address_space(3))) void *)(lds_tile + piece * 1024), 16, 0, 0);
-    }
+    for (int i = 0; i < Cfg<D>::kVPieces / kWaves; ++i)
+        dma16_rsrc(r, dl.v + i * kWaves * 1024, lds_tile + (wave + kWaves * i) * 1024);
 }
 
 // Per-wave running state of the online softmax and the output accumulator.
@@ -119,6 +149,8 @@ struct WaveState {
     float m;           // reference max of score * scale * log2(e), raised lazily
     float l;           // this lane's part of the row sum (its 16 of every 32 keys)
     float lp;          // the same sum over the bf16-rounded P that enters the PV MFMA
+    float alpha;       // O rescale factor still to apply (see pending)
+    bool pending;      // an O rescale is pending (wave-uniform)
 };
 
 // Per-lane LDS offsets of the MFMA operand reads (independent of the stage).
@@ -176,42 +208,6 @@ __device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const bf16x8 (&qf)[D / 1
     });
 }
 
-// O^T += V^T P^T for one key tile: MFMA i = 4c + 2*blk + hh takes as B
-// operand registers 8*hh .. 8*hh+7 of s[blk], i.e. keys 32*blk + 16*hh +
-// 8*(e/4) + 4*g + e%4 for element e; its V^T operand is two transposing reads
-// of key rows 32*blk + 16*hh + 4g + 0..3 and +8..11.  Reads run two MFMAs
-// ahead.
-template <int D>
-__device__ __forceinline__ void pv_tile(f32x16 (&o)[D / 32], const uint32_t (&pk)[2][8],
-                                        uint32_t vaddr, const LaneOffsets<D> &off)
-{
-    constexpr int NV = 4 * (D / 32), VLA = 2;
-    u32x4 vw[VLA + 1];
-    auto read_v = [&](auto i) -> u32x4 {
-        constexpr int I = decltype(i)::value;
-        constexpr int c = I >> 2, blk = (I >> 1) & 1, hh = I & 1;
-        constexpr int row0 = 32 * blk + 16 * hh;
-        const uint32_t a = vaddr + off.v[c];
-        const u32x2 w0 = lds_read_tr16_b64<row0 * Cfg<D>::kVPitch>(a);
-        const u32x2 w1 = lds_read_tr16_b64<(row0 + 8) * Cfg<D>::kVPitch>(a);
-        return u32x4{w0[0], w0[1], w1[0], w1[1]};
-    };
-    static_for<0, VLA>([&](auto i) { vw[decltype(i)::value] = read_v(i); });
-    static_for<0, NV>([&](auto i) {
-        constexpr int I = decltype(i)::value;
-        if constexpr (I + VLA < NV) {
-            vw[(I + VLA) % (VLA + 1)] = read_v(std::integral_constant<int, I + VLA>{});
-            lgkm_wait<2 * VLA>(vw[I % (VLA + 1)]);
-        } else {
-            lgkm_wait<2 * (NV - 1 - I)>(vw[I % (VLA + 1)]);
-        }
-        constexpr int c = I >> 2, blk = (I >> 1) & 1, hh = I & 1;
-        const u32x4 pw = {pk[blk][4 * hh], pk[blk][4 * hh + 1], pk[blk][4 * hh + 2],
-                          pk[blk][4 * hh + 3]};
-        o[c] = mfma_bf16_32x32x16(as_bf16x8(vw[I % (VLA + 1)]), as_bf16x8(pw), o[c]);
-    });
-}
-
 __device__ __forceinline__ float tile_max(const f32x16 (&s)[2])
 {
     float mx = s[0][0];
@@ -236,150 +232,228 @@ __device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int k0, int N, int g, 
         }
 }
 
-// Raise the reference max when the tile max (log2 units) exceeds it by more
-// than 2^8 for some lane of the wave, rescaling O and l.  The first tile
-// always holds key 0, visible to every query, so m is finite from the first
-// tile on.
-template <int D>
-__device__ __forceinline__ void update_max(WaveState<D> &st, float mx)
+// p = 2^(s*cs - m) for one tile, rounded to bf16 for the PV product.  Two
+// row sums are kept: l over the unrounded values, for the LSE (a rounded sum
+// would carry up to 2^-9 relative error into the LSE of rows with few keys),
+// and lp over the rounded values, for normalising O (the weights applied to V
+// then sum to one, so a row dominated by one key returns that key's V row
+// rather than V times the bf16 rounding error of its p).
+__device__ __forceinline__ void softmax_tile(const f32x16 (&s)[2], float m, float cs,
+                                             uint32_t (&pk)[2][8], float &l, float &lp)
 {
-    if (__any(mx > st.m + kRescaleLog2)) {
-        const float m_new = mx > st.m + kRescaleLog2 ? mx : st.m;
-        const float alpha = fast_exp2(st.m - m_new);
-        st.l *= alpha;
-        st.lp *= alpha;
-#pragma unroll
-        for (int c = 0; c < D / 32; ++c)
-            st.o[c] *= alpha;
-        st.m = m_new;
-    }
-}
-
-// Phase A of the software pipeline: the QK MFMAs of the next tile, each
-// followed by a slice of the exponentials of the current tile.  The two
-// 32-key accumulators alternate so that consecutive MFMAs are independent.
-// Each step exponentiates two scores and folds the two of the previous step
-// into the row sums and the bf16 P fragment (the exp latency is then covered
-// by the MFMA in between).  p = 2^(s*cs - m) is rounded to bf16 for the PV
-// product, and two row sums are kept: l over the unrounded values, for the
-// LSE (a rounded sum would carry up to 2^-9 relative error into the LSE of
-// rows with few keys), and lp over the rounded values, for normalising O (the
-// weights applied to V then sum to one, so a row dominated by one key returns
-// that key's V row rather than V times the bf16 rounding error of its p).  Steps are fenced with scheduling barriers and
-// their results pinned, so the wave issues VALU work between its MFMAs
-// instead of in one block.
-template <int D>
-__device__ __forceinline__ void phase_a(f32x16 (&s_next)[2], const bf16x8 (&qf)[D / 16],
-                                        uint32_t kaddr, const f32x16 (&s_cur)[2], float m,
-                                        float cs, uint32_t (&pk)[2][8], float &l, float &lp)
-{
-    constexpr int KS = D / 16, NK = 2 * KS, KLA = 4;
-    constexpr int EPS = 32 / NK;  // scores exponentiated per step
-    static_assert(EPS == 2 || EPS == 4, "slice size");
-    u32x4 kv[KLA + 1];
-    s_next[0] = f32x16{};
-    s_next[1] = f32x16{};
     float rs0 = 0.f, rs1 = 0.f;
-    float pp[2][EPS];  // exponentials of the previous and the current step
-    // MFMA i: block i % 2, k-step i / 2
-    auto kread = [&](auto i) -> u32x4 {
-        constexpr int I = decltype(i)::value;
-        return lds_read_b128<(I % 2) * 32 * Cfg<D>::kKPitch + (I / 2) * 32>(kaddr);
-    };
-    auto fold = [&](auto i) {  // row sum and bf16 packing of step i's slice
-        constexpr int I = decltype(i)::value;
-        static_for<0, EPS / 2>([&](auto e) {
-            constexpr int R = I * EPS + 2 * decltype(e)::value;
-            constexpr int blk = R / 16, r = R % 16;
-            const float p0 = pp[I % 2][2 * decltype(e)::value];
-            const float p1 = pp[I % 2][2 * decltype(e)::value + 1];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+            const float p0 = fast_exp2(fmaf(s[blk][r], cs, -m));
+            const float p1 = fast_exp2(fmaf(s[blk][r + 1], cs, -m));
             rs0 += p0;
             rs1 += p1;
             pk[blk][r >> 1] = pack_bf16x2(p0, p1);
             lp = add_bf16x2(pk[blk][r >> 1], lp);
-            asm volatile("" : "+v"(pk[blk][r >> 1]), "+v"(rs0), "+v"(rs1), "+v"(lp));
-        });
-    };
-    static_for<0, KLA>([&](auto i) { kv[decltype(i)::value] = kread(i); });
-    static_for<0, NK>([&](auto i) {
-        constexpr int I = decltype(i)::value;
-        if constexpr (I + KLA < NK) {
-            kv[(I + KLA) % (KLA + 1)] = kread(std::integral_constant<int, I + KLA>{});
-            lgkm_wait<KLA>(kv[I % (KLA + 1)]);
-        } else {
-            lgkm_wait<NK - 1 - I>(kv[I % (KLA + 1)]);
         }
-        s_next[I % 2] =
-            mfma_bf16_32x32x16(as_bf16x8(kv[I % (KLA + 1)]), qf[I / 2], s_next[I % 2]);
-        static_for<0, EPS>([&](auto e) {
-            constexpr int R = I * EPS + decltype(e)::value;
-            pp[I % 2][decltype(e)::value] = fast_exp2(fmaf(s_cur[R / 16][R % 16], cs, -m));
-            asm volatile("" : "+v"(pp[I % 2][decltype(e)::value]));
-        });
-        if constexpr (I > 0)
-            fold(std::integral_constant<int, I - 1>{});
-        __builtin_amdgcn_sched_barrier(0);
-    });
-    fold(std::integral_constant<int, NK - 1>{});
     l += rs0 + rs1;
 }
 
-// Phase B: the PV MFMAs of the current tile, each followed by a slice of the
-// row max of the next tile; returns that max (this lane's keys only).
-// Consecutive MFMAs accumulate into different feature blocks.
+// Lazy max update with the tile max mx (log2 units, already reduced over the
+// two lane halves): the reference max of a row is raised only when mx
+// exceeds it by more than 2^8.  l and lp are rescaled at once; the O rescale
+// is left pending, to be applied once the PV product of the tile whose P was
+// computed against the old max has been issued.  At most one rescale is
+// pending at a time (it is applied one step after it is raised).
 template <int D>
-__device__ __forceinline__ float phase_b(f32x16 (&o)[D / 32], const uint32_t (&pk)[2][8],
-                                         uint32_t vaddr, const LaneOffsets<D> &off,
-                                         const f32x16 (&s_next)[2])
+__device__ __forceinline__ void raise_max(WaveState<D> &st, float mx)
 {
-    constexpr int NC = D / 32, NV = 4 * NC, VLA = 2;
-    constexpr int MPS = 32 / NV;  // scores reduced per step
-    u32x4 vw[VLA + 1];
-    // MFMA i: feature block i % NC, key quarter q = i / NC (blk = q / 2, hh = q % 2)
-    auto read_v = [&](auto i) -> u32x4 {
-        constexpr int I = decltype(i)::value;
-        constexpr int c = I % NC, q = I / NC, blk = q >> 1, hh = q & 1;
-        constexpr int row0 = 32 * blk + 16 * hh;
-        const uint32_t a = vaddr + off.v[c];
-        const u32x2 w0 = lds_read_tr16_b64<row0 * Cfg<D>::kVPitch>(a);
-        const u32x2 w1 = lds_read_tr16_b64<(row0 + 8) * Cfg<D>::kVPitch>(a);
-        return u32x4{w0[0], w0[1], w1[0], w1[1]};
-    };
-    float mx0 = -INFINITY, mx1 = -INFINITY;
-    static_for<0, VLA>([&](auto i) { vw[decltype(i)::value] = read_v(i); });
-    static_for<0, NV>([&](auto i) {
-        constexpr int I = decltype(i)::value;
-        if constexpr (I + VLA < NV) {
-            vw[(I + VLA) % (VLA + 1)] = read_v(std::integral_constant<int, I + VLA>{});
-            lgkm_wait<2 * VLA>(vw[I % (VLA + 1)]);
+    const bool need = mx > st.m + kRescaleLog2;
+    if (__any(need)) {
+        const float m_new = need ? mx : st.m;
+        const float alpha = fast_exp2(st.m - m_new);
+        st.l *= alpha;
+        st.lp *= alpha;
+        st.alpha = alpha;
+        st.pending = true;
+        st.m = m_new;
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void apply_pending(WaveState<D> &st)
+{
+    if (st.pending) {
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c)
+            st.o[c] *= st.alpha;
+        st.pending = false;
+    }
+}
+
+// Slot schedule of one pipeline step.  Step t issues NS MFMAs, one per slot:
+// slots 0 .. NQK-1 are the QK MFMAs of tile t+2 (slot i: key block i % 2,
+// k-step i / 2, so consecutive MFMAs accumulate into different blocks), the
+// remaining slots the PV MFMAs of tile t (slot NQK + j: feature block j % NC,
+// key quarter j / NC).  The VALU work of the step -- the exponentials, row
+// sums and bf16 packing of tile t+1 and the masking and max of tile t+2 --
+// is spread over the slots so that every MFMA has about the same amount of
+// independent VALU work issued behind it, and the operand reads from LDS run
+// RA slots ahead.
+template <int D>
+struct Sched {
+    static constexpr int NC = D / 32;
+    static constexpr int NQK = 2 * (D / 16);
+    static constexpr int NPV = 4 * NC;
+    static constexpr int NS = NQK + NPV;
+    static constexpr int RA = 3;
+    static constexpr int nops(int s) { return s < NQK ? 1 : 2; }  // LDS reads of slot s
+    // LDS reads issued after those of slot s by the time slot s's MFMA issues
+    static constexpr int after(int s)
+    {
+        int n = 0;
+        for (int j = s + 1; j <= s + RA && j < NS; ++j)
+            n += nops(j);
+        return n;
+    }
+    // scores first_score(s) .. first_score(s+1)-1 are exponentiated in slot s
+    static constexpr int first_score(int s) { return s >= NS ? 32 : (s * 32) / NS; }
+    // max3 k (k = 0..15, over scores 2k and 2k+1) runs in slot max_slot(k);
+    // the lane-half reduction of the max runs in slot NS - 2
+    static constexpr int max_slot(int k) { return NQK + 2 + (k * (NS - NQK - 4)) / 16; }
+    // direct-load instruction d of nd is issued in slot dma_slot(d, nd)
+    static constexpr int dma_slot(int d, int nd) { return 1 + (d * (NS - 2)) / nd; }
+};
+
+// One pipeline step t: PV(t) with P(t) (computed against the max of the
+// previous step), QK(t+2) into s_qk, and the exponentials of tile t+1 (s_exp,
+// against the current reference max) into p_next; returns the lane's max
+// over the masked s_qk, reduced over the two lane halves and in log2 units.
+// Every step runs the same code so that the score and
+// P buffers keep their registers from step to step: on the last two steps of
+// a wave the QK product and the exponentials run on whatever the stages hold
+// and their results are dropped -- the row sums are committed only when
+// commit_exp is set, and the caller raises the max only when tile t+2 exists.
+template <int D, bool CAUSAL, class Dma>
+__device__ __forceinline__ float pipe_step(WaveState<D> &st, const bf16x8 (&qf)[D / 16],
+                                           uint32_t kaddr, uint32_t vaddr,
+                                           const LaneOffsets<D> &off, const f32x16 (&s_exp)[2],
+                                           f32x16 (&s_qk)[2], const uint32_t (&p_cur)[2][8],
+                                           uint32_t (&p_next)[2][8], float cs, bool commit_exp,
+                                           bool mask_qk, int k0_qk, int N, int g, int my_q,
+                                           const Dma &dma)
+{
+    using SC = Sched<D>;
+    constexpr int NS = SC::NS, NQK = SC::NQK, NC = SC::NC, RA = SC::RA;
+    constexpr int S0 = 0;
+    constexpr bool DO_EXP = true, DO_QK = true;
+    u32x4 opb[RA + 1];
+    auto read_op = [&](auto sc) -> u32x4 {
+        constexpr int S = decltype(sc)::value;
+        if constexpr (S < NQK) {
+            return lds_read_b128<(S % 2) * 32 * Cfg<D>::kKPitch + (S / 2) * 32>(kaddr);
         } else {
-            lgkm_wait<2 * (NV - 1 - I)>(vw[I % (VLA + 1)]);
+            constexpr int j = S - NQK, c = j % NC, q = j / NC;
+            constexpr int row0 = 32 * (q >> 1) + 16 * (q & 1);
+            const uint32_t a = vaddr + off.v[c];
+            const u32x2 w0 = lds_read_tr16_b64<row0 * Cfg<D>::kVPitch>(a);
+            const u32x2 w1 = lds_read_tr16_b64<(row0 + 8) * Cfg<D>::kVPitch>(a);
+            return u32x4{w0[0], w0[1], w1[0], w1[1]};
         }
-        constexpr int c = I % NC, q = I / NC, blk = q >> 1, hh = q & 1;
-        const u32x4 pw = {pk[blk][4 * hh], pk[blk][4 * hh + 1], pk[blk][4 * hh + 2],
-                          pk[blk][4 * hh + 3]};
-        o[c] = mfma_bf16_32x32x16(as_bf16x8(vw[I % (VLA + 1)]), as_bf16x8(pw), o[c]);
-        static_for<0, MPS / 2>([&](auto e) {
-            constexpr int R = I * MPS + 2 * decltype(e)::value;
-            constexpr int sb = R / 16, r = R % 16;
-            if constexpr ((I * (MPS / 2) + decltype(e)::value) % 2 == 0)
-                mx0 = vmax3(mx0, s_next[sb][r], s_next[sb][r + 1]);
-            else
-                mx1 = vmax3(mx1, s_next[sb][r], s_next[sb][r + 1]);
-            asm volatile("" : "+v"(mx0), "+v"(mx1));
-        });
+    };
+    const float m = st.m;
+    float pv[32];
+    float rs0 = 0.f, rs1 = 0.f, lp = st.lp;
+    float mx0 = -INFINITY, mx1 = -INFINITY;
+    if constexpr (DO_QK) {
+        s_qk[0] = f32x16{};
+        s_qk[1] = f32x16{};
+    }
+    // fold score r (exponentiated in an earlier slot) into the sums and P
+    auto fold = [&](auto rc) {
+        constexpr int R = decltype(rc)::value;
+        if constexpr (R % 2 == 0) {
+            rs0 += pv[R];
+        } else {
+            rs1 += pv[R];
+            constexpr int blk = R / 16, r = R % 16;
+            p_next[blk][r >> 1] = pack_bf16x2(pv[R - 1], pv[R]);
+            lp = add_bf16x2(p_next[blk][r >> 1], lp);
+            asm volatile("" : "+v"(p_next[blk][r >> 1]), "+v"(lp));
+        }
+        asm volatile("" : "+v"(rs0), "+v"(rs1));
+    };
+    static_for<S0, (S0 + RA < NS ? S0 + RA : NS)>(
+        [&](auto i) { opb[decltype(i)::value % (RA + 1)] = read_op(i); });
+    static_for<S0, NS>([&](auto sc) {
+        constexpr int S = decltype(sc)::value;
+        if constexpr (S + RA < NS)
+            opb[(S + RA) % (RA + 1)] = read_op(std::integral_constant<int, S + RA>{});
+        lgkm_wait<SC::after(S)>(opb[S % (RA + 1)]);
+        if constexpr (S < NQK) {
+            s_qk[S % 2] = mfma_bf16_32x32x16(as_bf16x8(opb[S % (RA + 1)]), qf[S / 2], s_qk[S % 2]);
+        } else {
+            constexpr int j = S - NQK, c = j % NC, q = j / NC, blk = q >> 1, hh = q & 1;
+            const u32x4 pw = {p_cur[blk][4 * hh], p_cur[blk][4 * hh + 1], p_cur[blk][4 * hh + 2],
+                              p_cur[blk][4 * hh + 3]};
+            st.o[c] = mfma_bf16_32x32x16(as_bf16x8(opb[S % (RA + 1)]), as_bf16x8(pw), st.o[c]);
+        }
+        dma(sc);
+        if constexpr (DO_EXP) {
+            static_for<SC::first_score(S), SC::first_score(S + 1)>([&](auto rc) {
+                constexpr int R = decltype(rc)::value;
+                pv[R] = fast_exp2(fmaf(s_exp[R / 16][R % 16], cs, -m));
+                asm volatile("" : "+v"(pv[R]));
+            });
+            // fold the scores exponentiated two slots ago (covers the exp latency)
+            if constexpr (S > S0 + 1)
+                static_for<SC::first_score(S - 2), SC::first_score(S - 1)>(fold);
+        }
+        if constexpr (DO_QK) {
+            if constexpr (S == NQK + 1) {
+                if (mask_qk)
+                    mask_tile<CAUSAL>(s_qk, k0_qk, N, g, my_q);
+            }
+            static_for<0, 16>([&](auto kc) {
+                constexpr int k = decltype(kc)::value;
+                if constexpr (SC::max_slot(k) == S) {
+                    constexpr int R = 2 * k, blk = R / 16, r = R % 16;
+                    if constexpr (k % 2 == 0)
+                        mx0 = vmax3(mx0, s_qk[blk][r], s_qk[blk][r + 1]);
+                    else
+                        mx1 = vmax3(mx1, s_qk[blk][r], s_qk[blk][r + 1]);
+                    asm volatile("" : "+v"(mx0), "+v"(mx1));
+                }
+            });
+            if constexpr (S == NS - 2) {
+                mx0 = max_xor32(vmax3(mx0, mx1, mx1)) * cs;
+                asm volatile("" : "+v"(mx0));
+            }
+        }
         __builtin_amdgcn_sched_barrier(0);
     });
-    return vmax3(mx0, mx1, mx1);
+    static_for<SC::first_score(NS - 2), 32>(fold);
+    if (commit_exp) {
+        st.l += rs0 + rs1;
+        st.lp = lp;
+    }
+    // the PV MFMAs of this step used P computed against the max before the
+    // last raise: O can take that raise's factor now
+    apply_pending<D>(st);
+    return mx0;
 }
 
 // One query tile of one (batch, head): load its Q fragments, stream every
-// visible K/V tile through the LDS stages, write O and the LSE.
+// visible K/V tile through the LDS rings, write O and the LSE.
+//
+// LDS: 4-stage K and V rings (tile t in stage t % 4).  Step t reads K(t+2)
+// and V(t) and issues the loads of K(t+4) and V(t+2).  The workgroup
+// synchronises before every even step t: all loads issued by then (those of
+// the two previous steps, K(t+2), K(t+3), V(t), V(t+1)) are what steps t and
+// t+1 read, and the stages the two steps load into were last read before the
+// previous synchronisation.  The prologue loads K0..K3, V0 and V1.
 template <int D, bool CAUSAL, bool OUT_F32>
 __device__ __forceinline__ void attend_qtile(const PrefillArgs &a, unsigned char *smem, int bh,
                                              int qt, int wave, int lane)
 {
-    constexpr int kStage = Cfg<D>::kKBytes + Cfg<D>::kVBytes;
+    constexpr int kK = Cfg<D>::kKBytes, kV = Cfg<D>::kVBytes;
     const int g = lane >> 5, n = lane & 31;
     const int N = a.N;
     const int h = bh % a.H, b = bh / a.H;
@@ -395,19 +469,29 @@ __device__ __forceinline__ void attend_qtile(const PrefillArgs &a, unsigned char
     const int ntiles = (kend + kBN - 1) / kBN;
     // tiles this wave computes (the rest lie above its causal diagonal)
     const int ntw = CAUSAL ? min(ntiles, (qw0 + kQW - 1) / kBN + 1) : ntiles;
-    auto kst = [&](int t) { return smem + (t % 3) * kStage; };
-    auto vst = [&](int t) { return smem + (t % 3) * kStage + Cfg<D>::kKBytes; };
+    auto kst = [&](int t) { return smem + (t & 3) * kK; };
+    auto vst = [&](int t) { return smem + 4 * kK + (t & 3) * kV; };
     auto needs_mask = [&](int t) {
         const int k0 = t * kBN;
         return (CAUSAL && k0 + kBN - 1 > qw0) || k0 + kBN > N;
     };
+    // direct loads per wave for one K / V tile
+    const DmaLanes<D> dl = dma_lanes<D>(wave, lane);
+    auto load_k = [&](int t) {
+        if (t < ntiles)
+            issue_k<D>(kst(t), kb, t * kBN, N, wave, dl);
+    };
+    auto load_v = [&](int t) {
+        if (t < ntiles)
+            issue_v<D>(vst(t), vb, t * kBN, N, wave, dl);
+    };
 
-    issue_k<D>(kst(0), kb, 0, N, wave, lane);
-    issue_v<D>(vst(0), vb, 0, N, wave, lane);
-    if (ntiles > 1) {
-        issue_k<D>(kst(1), kb, kBN, N, wave, lane);
-        issue_v<D>(vst(1), vb, kBN, N, wave, lane);
-    }
+    load_k(0);
+    load_k(1);
+    load_k(2);
+    load_v(0);
+    load_k(3);
+    load_v(1);
 
     // Q^T fragments (B operand): lane holds Q[my_q][16*ks + 8*g .. +7].
     bf16x8 qf[D / 16];
@@ -421,50 +505,102 @@ __device__ __forceinline__ void attend_qtile(const PrefillArgs &a, unsigned char
 #pragma unroll
     for (int c = 0; c < D / 32; ++c)
         st.o[c] = f32x16{};
-    st.m = -INFINITY;
     st.l = 0.f;
     st.lp = 0.f;
+    st.alpha = 1.f;
+    st.pending = false;
     const float cs = a.scale * kLog2e;
 
-    // Software pipeline: iteration t runs the QK MFMAs of tile t+1 next to
-    // the exponentials of tile t, then the PV MFMAs of tile t next to the
-    // masking and max of tile t+1, so each wave has independent VALU work to
-    // issue between its MFMAs.  The loop is unrolled twice so that the two
-    // score buffers swap roles without register copies.
-    f32x16 sa[2], sb[2];
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    qk_tile<D>(sa, qf, lds_addr(kst(0)) + off.k);
-    if (needs_mask(0))
-        mask_tile<CAUSAL>(sa, 0, N, g, my_q);
-    update_max<D>(st, max_xor32(tile_max(sa)) * cs);
+    // S(j) lives in sA for even j, sB for odd j; P(j) likewise in pA / pB.
+    f32x16 sA[2], sB[2];
+    uint32_t pA[2][8], pB[2][8];
 
-    auto step = [&](int t, f32x16(&s_cur)[2], f32x16(&s_next)[2]) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (t + 2 < ntiles) {
-            issue_k<D>(kst(t + 2), kb, (t + 2) * kBN, N, wave, lane);
-            issue_v<D>(vst(t + 2), vb, (t + 2) * kBN, N, wave, lane);
+    // pre-step: S(0), S(1), the max of both and P(0)
+    vm_wait_n<0>();  // K0 K1 (the first loads take their full latency anyway)
+    __syncthreads();
+    if (0 < ntw) {
+        qk_tile<D>(sA, qf, lds_addr(kst(0)) + off.k);
+        if (ntw > 1)
+            qk_tile<D>(sB, qf, lds_addr(kst(1)) + off.k);
+        if (needs_mask(0))
+            mask_tile<CAUSAL>(sA, 0, N, g, my_q);
+        st.m = max_xor32(tile_max(sA)) * cs;
+        softmax_tile(sA, st.m, cs, pA, st.l, st.lp);
+        if (ntw > 1) {
+            if (needs_mask(1))
+                mask_tile<CAUSAL>(sB, kBN, N, g, my_q);
+            raise_max<D>(st, max_xor32(tile_max(sB)) * cs);
         }
-        if (t >= ntw)
-            return;
-        // QK(t+1) also runs when this wave does not need tile t+1 (the result
-        // is then dropped) so that phase A has no branch.
-        uint32_t pk[2][8];
-        phase_a<D>(s_next, qf, lds_addr(kst(t + 1)) + off.k, s_cur, st.m, cs, pk, st.l,
-                   st.lp);
-        const bool more = t + 1 < ntw;
-        if (more && needs_mask(t + 1))
-            mask_tile<CAUSAL>(s_next, (t + 1) * kBN, N, g, my_q);
-        const float mx = phase_b<D>(st.o, pk, lds_addr(vst(t)), off, s_next);
-        if (more)
-            update_max<D>(st, max_xor32(mx) * cs);
-    };
-    for (int t = 0; t < ntiles; t += 2) {
-        step(t, sa, sb);
-        if (t + 1 < ntiles)
-            step(t + 1, sb, sa);
     }
+
+    // Computed steps (t < ntw) first, then the steps of tiles above this
+    // wave's causal diagonal, in which it only keeps the workgroup's
+    // synchronisation and load cadence.  The workgroup synchronises before
+    // every even step (see above).
+    auto sync = [&](int t) {
+        if ((t & 1) == 0) {
+            vm_wait_n<0>();
+            __syncthreads();
+        }
+    };
+    auto step = [&](int t, auto par) {
+        constexpr int E = decltype(par)::value;  // t % 2
+        if constexpr (E == 0) {
+            vm_wait_n<0>();
+            __syncthreads();
+        }
+        // the loads of K(t+4) and V(t+2) go to stages no wave reads in this
+        // step; they are spread over the MFMA slots
+        const bool lk = t + 4 < ntiles, lv = t + 2 < ntiles;
+        const __amdgpu_buffer_rsrc_t rk = tile_rsrc<D>(kb, lk ? (t + 4) * kBN : 0, N);
+        const __amdgpu_buffer_rsrc_t rv = tile_rsrc<D>(vb, lv ? (t + 2) * kBN : 0, N);
+        unsigned char *const lk_st = kst(t + 4), *const lv_st = vst(t + 2);
+        auto dma = [&](auto sc) {
+            constexpr int S = decltype(sc)::value;
+            constexpr int NK = DmaLanes<D>::kKMax, NV = Cfg<D>::kVPieces / kWaves;
+            static_for<0, NK + NV>([&](auto dc) {
+                constexpr int d = decltype(dc)::value;
+                if constexpr (Sched<D>::dma_slot(d, NK + NV) == S) {
+                    if constexpr (d < NK) {
+                        const int piece = wave + kWaves * d;
+                        if (lk && piece < Cfg<D>::kKPieces)
+                            dma16_rsrc(rk, dl.k[d], lk_st + piece * 1024);
+                    } else {
+                        constexpr int i = d - NK;
+                        if (lv)
+                            dma16_rsrc(rv, dl.v + i * kWaves * 1024,
+                                       lv_st + (wave + kWaves * i) * 1024);
+                    }
+                }
+            });
+        };
+        const uint32_t kaddr = lds_addr(kst(t + 2)) + off.k;
+        const uint32_t vaddr = lds_addr(vst(t));
+        f32x16(&s_exp)[2] = E ? sA : sB;  // S(t+1)
+        f32x16(&s_qk)[2] = E ? sB : sA;   // S(t+2)
+        uint32_t(&pc)[2][8] = E ? pB : pA;  // P(t)
+        uint32_t(&pn)[2][8] = E ? pA : pB;  // P(t+1)
+        const float mx = pipe_step<D, CAUSAL>(st, qf, kaddr, vaddr, off, s_exp, s_qk, pc, pn, cs,
+                                              t + 1 < ntw, needs_mask(t + 2), (t + 2) * kBN, N,
+                                              g, my_q, dma);
+        if (t + 2 < ntw)
+            raise_max<D>(st, mx);
+    };
+    int t = 0;
+    for (; t + 1 < ntw; t += 2) {
+        step(t, std::integral_constant<int, 0>{});
+        step(t + 1, std::integral_constant<int, 1>{});
+    }
+    if (t < ntw) {
+        step(t, std::integral_constant<int, 0>{});
+        ++t;
+    }
+    for (; t < ntiles; ++t) {
+        sync(t);
+        load_k(t + 4);
+        load_v(t + 2);
+    }
+    apply_pending<D>(st);
 
     const float lt = sum_xor32(st.l);
     const float ltp = sum_xor32(st.lp);
@@ -503,9 +639,11 @@ template <int D, bool CAUSAL, bool OUT_F32>
 __global__ __launch_bounds__(kThreads) void prefill_exact_kernel(PrefillArgs a)
 {
     // three K/V stages: tile t+2 loads while tile t+1's K and tile t's V are read
-    constexpr int kStage = Cfg<D>::kKBytes + Cfg<D>::kVBytes;
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[3 * kStage];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // four K stages and four V stages (see attend_qtile)
+    __shared__ __attribute__((aligned(1024)))
+    unsigned char smem[4 * Cfg<D>::kKBytes + 4 * Cfg<D>::kVBytes];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int nqt = (a.N + kBM - 1) / kBM;
     // Causal: workgroup j of a head takes query tiles nqt-1-j and j, so every
     // workgroup streams the same number of key tiles (no long tail of heavy
