@@ -149,8 +149,6 @@ struct WaveState {
     float m;           // reference max of score * scale * log2(e), raised lazily
     float l;           // this lane's part of the row sum (its 16 of every 32 keys)
     float lp;          // the same sum over the bf16-rounded P that enters the PV MFMA
-    float alpha;       // O rescale factor still to apply (see pending)
-    bool pending;      // an O rescale is pending (wave-uniform)
 };
 
 // Per-lane LDS offsets of the MFMA operand reads (independent of the stage).
@@ -256,36 +254,30 @@ __device__ __forceinline__ void softmax_tile(const f32x16 (&s)[2], float m, floa
     l += rs0 + rs1;
 }
 
-// Lazy max update with the tile max mx (log2 units, already reduced over the
-// two lane halves): the reference max of a row is raised only when mx
-// exceeds it by more than 2^8.  l and lp are rescaled at once; the O rescale
-// is left pending, to be applied once the PV product of the tile whose P was
-// computed against the old max has been issued.  At most one rescale is
-// pending at a time (it is applied one step after it is raised).
-template <int D>
-__device__ __forceinline__ void raise_max(WaveState<D> &st, float mx)
-{
-    const bool need = mx > st.m + kRescaleLog2;
-    if (__any(need)) {
-        const float m_new = need ? mx : st.m;
-        const float alpha = fast_exp2(st.m - m_new);
-        st.l *= alpha;
-        st.lp *= alpha;
-        st.alpha = alpha;
-        st.pending = true;
-        st.m = m_new;
-    }
-}
+// The exponentials of a tile are taken against the current reference max m
+// of each row, without first reducing the tile's own max.  They are kept
+// only if every lane's share of the tile's row sum stays <= 2^8 (so every p
+// is <= 2^8 and finite); otherwise -- rarely, when a row's scores climb well
+// above its reference -- the tile is redone: m is raised to the exact running
+// max, the sums and O are rescaled, and the tile is exponentiated again.
+constexpr float kPSumMax = 256.f;
 
 template <int D>
-__device__ __forceinline__ void apply_pending(WaveState<D> &st)
+__device__ __forceinline__ void redo_tile(WaveState<D> &st, const f32x16 (&s)[2], float cs,
+                                          uint32_t (&pk)[2][8], float &rs, float &lp_tile)
 {
-    if (st.pending) {
+    const float mx = max_xor32(tile_max(s)) * cs;
+    const float m_new = mx > st.m ? mx : st.m;
+    const float alpha = fast_exp2(st.m - m_new);
+    st.l *= alpha;
+    st.lp *= alpha;
 #pragma unroll
-        for (int c = 0; c < D / 32; ++c)
-            st.o[c] *= st.alpha;
-        st.pending = false;
-    }
+    for (int c = 0; c < D / 32; ++c)
+        st.o[c] *= alpha;
+    st.m = m_new;
+    rs = 0.f;
+    lp_tile = 0.f;
+    softmax_tile(s, st.m, cs, pk, rs, lp_tile);
 }
 
 // Slot schedule of one pipeline step.  Step t issues NS MFMAs, one per slot:
@@ -315,29 +307,25 @@ struct Sched {
     }
     // scores first_score(s) .. first_score(s+1)-1 are exponentiated in slot s
     static constexpr int first_score(int s) { return s >= NS ? 32 : (s * 32) / NS; }
-    // max3 k (k = 0..15, over scores 2k and 2k+1) runs in slot max_slot(k);
-    // the lane-half reduction of the max runs in slot NS - 2
-    static constexpr int max_slot(int k) { return NQK + 2 + (k * (NS - NQK - 4)) / 16; }
     // direct-load instruction d of nd is issued in slot dma_slot(d, nd)
     static constexpr int dma_slot(int d, int nd) { return 1 + (d * (NS - 2)) / nd; }
 };
 
-// One pipeline step t: PV(t) with P(t) (computed against the max of the
-// previous step), QK(t+2) into s_qk, and the exponentials of tile t+1 (s_exp,
-// against the current reference max) into p_next; returns the lane's max
-// over the masked s_qk, reduced over the two lane halves and in log2 units.
-// Every step runs the same code so that the score and
-// P buffers keep their registers from step to step: on the last two steps of
-// a wave the QK product and the exponentials run on whatever the stages hold
-// and their results are dropped -- the row sums are committed only when
-// commit_exp is set, and the caller raises the max only when tile t+2 exists.
+// One pipeline step t: PV(t) with P(t), QK(t+2) into s_qk (masked), and the
+// exponentials of tile t+1 (s_exp, against the current reference max) into
+// p_next.  Returns this lane's share of tile t+1's row sum and (in lp_tile)
+// the same over the bf16-rounded values; the caller checks and commits them.
+// Every step runs the same code so that the score and P buffers keep their
+// registers from step to step: on the last two steps of a wave the QK
+// product and the exponentials run on whatever the stages hold and their
+// results are dropped.
 template <int D, bool CAUSAL, class Dma>
 __device__ __forceinline__ float pipe_step(WaveState<D> &st, const bf16x8 (&qf)[D / 16],
                                            uint32_t kaddr, uint32_t vaddr,
                                            const LaneOffsets<D> &off, const f32x16 (&s_exp)[2],
                                            f32x16 (&s_qk)[2], const uint32_t (&p_cur)[2][8],
-                                           uint32_t (&p_next)[2][8], float cs, bool commit_exp,
-                                           bool mask_qk, int k0_qk, int N, int g, int my_q,
+                                           uint32_t (&p_next)[2][8], float cs, bool mask_qk,
+                                           int k0_qk, int N, int g, int my_q, float &lp_tile,
                                            const Dma &dma)
 {
     using SC = Sched<D>;
@@ -360,8 +348,7 @@ __device__ __forceinline__ float pipe_step(WaveState<D> &st, const bf16x8 (&qf)[
     };
     const float m = st.m;
     float pv[32];
-    float rs0 = 0.f, rs1 = 0.f, lp = st.lp;
-    float mx0 = -INFINITY, mx1 = -INFINITY;
+    float rs0 = 0.f, rs1 = 0.f, lp = 0.f;
     if constexpr (DO_QK) {
         s_qk[0] = f32x16{};
         s_qk[1] = f32x16{};
@@ -411,33 +398,12 @@ __device__ __forceinline__ float pipe_step(WaveState<D> &st, const bf16x8 (&qf)[
                 if (mask_qk)
                     mask_tile<CAUSAL>(s_qk, k0_qk, N, g, my_q);
             }
-            static_for<0, 16>([&](auto kc) {
-                constexpr int k = decltype(kc)::value;
-                if constexpr (SC::max_slot(k) == S) {
-                    constexpr int R = 2 * k, blk = R / 16, r = R % 16;
-                    if constexpr (k % 2 == 0)
-                        mx0 = vmax3(mx0, s_qk[blk][r], s_qk[blk][r + 1]);
-                    else
-                        mx1 = vmax3(mx1, s_qk[blk][r], s_qk[blk][r + 1]);
-                    asm volatile("" : "+v"(mx0), "+v"(mx1));
-                }
-            });
-            if constexpr (S == NS - 2) {
-                mx0 = max_xor32(vmax3(mx0, mx1, mx1)) * cs;
-                asm volatile("" : "+v"(mx0));
-            }
         }
         __builtin_amdgcn_sched_barrier(0);
     });
     static_for<SC::first_score(NS - 2), 32>(fold);
-    if (commit_exp) {
-        st.l += rs0 + rs1;
-        st.lp = lp;
-    }
-    // the PV MFMAs of this step used P computed against the max before the
-    // last raise: O can take that raise's factor now
-    apply_pending<D>(st);
-    return mx0;
+    lp_tile = lp;
+    return rs0 + rs1;
 }
 
 // One query tile of one (batch, head): load its Q fragments, stream every
@@ -507,15 +473,13 @@ __device__ __forceinline__ void attend_qtile(const PrefillArgs &a, unsigned char
         st.o[c] = f32x16{};
     st.l = 0.f;
     st.lp = 0.f;
-    st.alpha = 1.f;
-    st.pending = false;
     const float cs = a.scale * kLog2e;
 
     // S(j) lives in sA for even j, sB for odd j; P(j) likewise in pA / pB.
     f32x16 sA[2], sB[2];
     uint32_t pA[2][8], pB[2][8];
 
-    // pre-step: S(0), S(1), the max of both and P(0)
+    // pre-step: S(0) and S(1); the reference max from S(0), and P(0)
     vm_wait_n<0>();  // K0 K1 (the first loads take their full latency anyway)
     __syncthreads();
     if (0 < ntw) {
@@ -526,11 +490,8 @@ __device__ __forceinline__ void attend_qtile(const PrefillArgs &a, unsigned char
             mask_tile<CAUSAL>(sA, 0, N, g, my_q);
         st.m = max_xor32(tile_max(sA)) * cs;
         softmax_tile(sA, st.m, cs, pA, st.l, st.lp);
-        if (ntw > 1) {
-            if (needs_mask(1))
-                mask_tile<CAUSAL>(sB, kBN, N, g, my_q);
-            raise_max<D>(st, max_xor32(tile_max(sB)) * cs);
-        }
+        if (ntw > 1 && needs_mask(1))
+            mask_tile<CAUSAL>(sB, kBN, N, g, my_q);
     }
 
     // Computed steps (t < ntw) first, then the steps of tiles above this
@@ -580,11 +541,17 @@ __device__ __forceinline__ void attend_qtile(const PrefillArgs &a, unsigned char
         f32x16(&s_qk)[2] = E ? sB : sA;   // S(t+2)
         uint32_t(&pc)[2][8] = E ? pB : pA;  // P(t)
         uint32_t(&pn)[2][8] = E ? pA : pB;  // P(t+1)
-        const float mx = pipe_step<D, CAUSAL>(st, qf, kaddr, vaddr, off, s_exp, s_qk, pc, pn, cs,
-                                              t + 1 < ntw, needs_mask(t + 2), (t + 2) * kBN, N,
-                                              g, my_q, dma);
-        if (t + 2 < ntw)
-            raise_max<D>(st, mx);
+        float lp_tile;
+        float rs = pipe_step<D, CAUSAL>(st, qf, kaddr, vaddr, off, s_exp, s_qk, pc, pn, cs,
+                                        needs_mask(t + 2), (t + 2) * kBN, N, g, my_q, lp_tile,
+                                        dma);
+        if (t + 1 < ntw) {
+            // !(rs <= max) also catches an overflow to inf or NaN
+            if (__any(!(rs <= kPSumMax)))
+                redo_tile<D>(st, s_exp, cs, pn, rs, lp_tile);
+            st.l += rs;
+            st.lp += lp_tile;
+        }
     };
     int t = 0;
     for (; t + 1 < ntw; t += 2) {
@@ -600,8 +567,6 @@ __device__ __forceinline__ void attend_qtile(const PrefillArgs &a, unsigned char
         load_k(t + 4);
         load_v(t + 2);
     }
-    apply_pending<D>(st);
-
     const float lt = sum_xor32(st.l);
     const float ltp = sum_xor32(st.lp);
     if (my_q < N) {
