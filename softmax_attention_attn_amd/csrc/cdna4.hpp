@@ -88,6 +88,14 @@ __device__ __forceinline__ float vmax3(float a, float b, float c)
 }
 
 // v_exp_f32: 2^x (exp2(-inf) == 0).
+// max of three signed ints (v_max3_i32)
+__device__ __forceinline__ int vmax3_i32(int a, int b, int c)
+{
+    int r;
+    asm("v_max3_i32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Value held by the lane 32 positions away (lanes l and l ^ 32 exchange).

@@ -375,14 +375,20 @@ __global__ __launch_bounds__(kAThreads) void sage_attn_kernel(PrefillArgs a, Sag
     for (int c = 0; c < D / 32; ++c)
         o[c] = f32x16{};
     float m = -INFINITY, l = 0.f;
+    // the K scale of tile t is read one tile ahead, before the next tile's
+    // direct loads are issued, so that waiting for it never waits for them
+    float kd_next = kdel[0];
 
     for (int t = 0; t < ntiles; ++t) {
         const int k0 = t * kBlk;
         unsigned char *stage = smem + (t & 1) * kStage;
         vm_wait_all();
         __syncthreads();
-        if (t + 1 < ntiles)
+        const float kd = kd_next;
+        if (t + 1 < ntiles) {
+            kd_next = kdel[t + 1];
             issue_tile<D>(smem + ((t + 1) & 1) * kStage, khat, vhatT, Npad, k0 + kBlk, wave, lane);
+        }
         if (CAUSAL && k0 > qw0 + kQW - 1)
             continue;
 
@@ -400,28 +406,31 @@ __global__ __launch_bounds__(kAThreads) void sage_attn_kernel(PrefillArgs a, Sag
             }
         }
 
-        // scores in log2 units: S * log2e = cq * dK * int
-        const float c = cq * kdel[t];
-        float f[2][16];
+        // scores in log2 units: S * log2e = c * int (c > 0).  The tile max is
+        // taken on the integers (masked keys as INT_MIN), the exponent
+        // 2^(c*int + log2(448) - m) with one FMA per score; on tiles that
+        // need the mask, masked keys get -inf (a key masked through INT_MIN
+        // alone would not vanish when c is tiny).
+        const float c = cq * kd;
         const bool need_mask = (CAUSAL && k0 + kBlk - 1 > qw0) || k0 + kBlk > N;
+        int imx = INT_MIN;
+        if (need_mask) {
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
+            for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                f[blk][r] = (float)s[blk][r] * c;
-                if (need_mask) {
+                for (int r = 0; r < 16; ++r) {
                     const int key = k0 + 32 * blk + 16 * g + r;
                     if (key >= N || (CAUSAL && key > my_q))
-                        f[blk][r] = -INFINITY;
+                        s[blk][r] = INT_MIN;
                 }
-            }
-        float mx = f[0][0];
+        }
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                mx = fmaxf(mx, f[blk][r]);
-        mx = max_xor32(mx);
+            for (int r = 0; r < 16; r += 2)
+                imx = vmax3_i32(imx, s[blk][r], s[blk][r + 1]);
+        // a row with every key of the tile masked contributes -inf
+        const float mx = max_xor32(imx == INT_MIN ? -INFINITY : (float)imx * c);
         // exact running max (P is quantised against it)
         if (__any(mx > m)) {
             const float m_new = fmaxf(m, mx);
@@ -432,19 +441,23 @@ __global__ __launch_bounds__(kAThreads) void sage_attn_kernel(PrefillArgs a, Sag
                 o[cc] *= alpha;
             m = m_new;
         }
-        // p = 448 * 2^(f - m) <= 448; E4M3 codes packed 4 per dword:
+        // p = 448 * 2^(c*int - m) <= 448; E4M3 codes packed 4 per dword:
         // byte 16*blk + r of the lane = key 32*blk + 16*g + r
         uint32_t pk[8];
         float rs0 = 0.f, rs1 = 0.f;
         const float bias = kLog2_448 - m;
+        auto expo = [&](int v) {
+            const float x = fmaf((float)v, c, bias);
+            return fast_exp2(need_mask && v == INT_MIN ? -INFINITY : x);
+        };
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
             for (int r = 0; r < 16; r += 4) {
-                const float p0 = fast_exp2(f[blk][r] + bias);
-                const float p1 = fast_exp2(f[blk][r + 1] + bias);
-                const float p2 = fast_exp2(f[blk][r + 2] + bias);
-                const float p3 = fast_exp2(f[blk][r + 3] + bias);
+                const float p0 = expo(s[blk][r]);
+                const float p1 = expo(s[blk][r + 1]);
+                const float p2 = expo(s[blk][r + 2]);
+                const float p3 = expo(s[blk][r + 3]);
                 rs0 += p0 + p2;
                 rs1 += p1 + p3;
                 int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
