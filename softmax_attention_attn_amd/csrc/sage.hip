@@ -289,13 +289,14 @@ constexpr int kBM = kQW * kWaves;
 
 template <int D>
 struct SCfg {
-    static constexpr int kKRow = D;                        // K^ row bytes
-    static constexpr int kKChunks = D / 16;
-    static constexpr int kKBytes = kBlk * D;               // K^ tile
-    static constexpr int kVBytes = D * kBlk;               // V^^T tile
-    static constexpr int kStage = kKBytes + kVBytes;
+    static constexpr int kKChunks = D / 16;       // 16-byte chunks of a K^ row
+    static constexpr int kKBytes = kBlk * D;      // K^ tile (int8)
+    static constexpr int kVBytes = D * kBlk;      // V^^T tile (e4m3, feature-major)
     static constexpr int kKPieces = kKBytes / 1024;
     static constexpr int kVPieces = kVBytes / 1024;
+    static constexpr int kNC = D / 32;            // 32-feature blocks of O (PV MFMAs per tile)
+    static constexpr int kNQK = 2 * (D / 32);     // QK MFMAs per tile
+    static_assert(kKPieces <= kWaves && kVPieces <= kWaves, "at most one direct load per wave");
 };
 
 // K^ tile: 16-byte chunk index XOR swizzle by row, so the 16 perm32 rows
@@ -308,54 +309,331 @@ __device__ __forceinline__ int kswz(int row)
 // V^^T tile (64-byte rows = 4 chunks): chunk XOR by feature row.
 __device__ __forceinline__ int vswz(int d) { return ((d >> 2) & 1) | (((d >> 4) & 1) << 1); }
 
+// Slot schedule of one pipeline step: slots 0 .. NQK-1 issue the INT8 QK
+// MFMAs of tile t+2 (slot i: key block i % 2, k-step i / 2), slots NQK ..
+// NS-1 the FP8 PV MFMAs of tile t (feature block c = slot - NQK).  A PV MFMA
+// takes twice as long as a QK MFMA, so it carries twice the VALU work: the
+// 32 scores of tile t+1 are spread by weight (1 per QK slot, 2 per PV slot).
+// The integer max of tile t+2 runs in the PV slots after the first.
 template <int D>
-__device__ __forceinline__ void issue_tile(unsigned char *stage, const int8_t *khat,
-                                           const uint8_t *vhatT, int Npad, int k0, int wave,
-                                           int lane)
+struct SSched {
+    static constexpr int NQK = SCfg<D>::kNQK, NS = NQK + SCfg<D>::kNC, RA = 2;
+    static constexpr int weight(int s) { return s < NQK ? 1 : 2; }
+    static constexpr int wsum(int s)
+    {
+        int w = 0;
+        for (int i = 0; i < s && i < NS; ++i)
+            w += weight(i);
+        return w;
+    }
+    static constexpr int first_score(int s) { return s >= NS ? 32 : wsum(s) * 32 / wsum(NS); }
+    static constexpr int nops(int s) { return s < NQK ? 1 : 2; }  // LDS reads of slot s
+    static constexpr int after(int s)
+    {
+        int n = 0;
+        for (int j = s + 1; j <= s + RA && j < NS; ++j)
+            n += nops(j);
+        return n;
+    }
+    static constexpr int max_slot(int k) { return NQK + 1 + k * (NS - NQK - 1) / 16; }
+    static constexpr int dma_slot(int d) { return 1 + d * (NS - 2) / 2; }  // d = 0: K, 1: V
+};
+
+// Per-lane LDS read offsets within a stage.
+template <int D>
+struct SLanes {
+    uint32_t k[D / 32];  // K^ operand of k-step ks: row perm32(n), chunk (2ks+g) ^ kswz
+    uint32_t vlo, vhi;   // V^^T operand: feature row perm32(n), chunks g ^ vswz and (2+g) ^ vswz
+};
+
+template <int D>
+__device__ __forceinline__ SLanes<D> s_lanes(int lane)
+{
+    const int g = lane >> 5, n = lane & 31;
+    const int row = perm32(n), sw = kswz<D>(row), vs = vswz(row);
+    SLanes<D> o;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks)
+        o.k[ks] = row * D + (((2 * ks + g) ^ sw) << 4);
+    o.vlo = row * kBlk + ((g ^ vs) << 4);
+    o.vhi = row * kBlk + (((2 + g) ^ vs) << 4);
+    return o;
+}
+
+// Per-lane global byte offsets of this wave's direct loads (one 1 KB piece
+// of the K^ tile and one of the V^^T tile per wave).
+template <int D>
+struct SDma {
+    uint32_t k, v;
+};
+
+template <int D>
+__device__ __forceinline__ SDma<D> s_dma(int wave, int lane, int Npad)
 {
     constexpr int C = SCfg<D>::kKChunks;
-    for (int piece = wave; piece < SCfg<D>::kKPieces; piece += kWaves) {
-        const int p = piece * 64 + lane, row = p / C;
-        const int c = (p % C) ^ kswz<D>(row);
-        dma16(khat + (size_t)(k0 + row) * D + c * 16, stage + piece * 1024);
+    const int q = wave * 64 + lane;
+    SDma<D> o;
+    {
+        const int row = q / C;
+        o.k = row * D + (((q % C) ^ kswz<D>(row)) << 4);
     }
-    for (int piece = wave; piece < SCfg<D>::kVPieces; piece += kWaves) {
-        const int p = piece * 64 + lane, d = p >> 2;
-        const int c = (p & 3) ^ vswz(d);
-        dma16(vhatT + (size_t)d * Npad + k0 + c * 16, stage + SCfg<D>::kKBytes + piece * 1024);
+    {
+        const int d = q >> 2;
+        o.v = d * Npad + (((q & 3) ^ vswz(d)) << 4);
+    }
+    return o;
+}
+
+// S^T = K^ Q^^T for one tile, unpipelined (the first two tiles of a query tile).
+template <int D>
+__device__ __forceinline__ void qk_tile_i8(i32x16 (&s)[2], const i32x4 (&qf)[D / 32], uint32_t kst,
+                                           const SLanes<D> &ln)
+{
+    s[0] = i32x16{};
+    s[1] = i32x16{};
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+        u32x4 a0 = lds_read_b128<0>(kst + ln.k[ks]);
+        u32x4 a1 = lds_read_b128<32 * D>(kst + ln.k[ks]);
+        lgkm_wait<1>(a0);
+        s[0] = mfma_i8_32x32x32(__builtin_bit_cast(i32x4, a0), qf[ks], s[0]);
+        lgkm_wait<0>(a1);
+        s[1] = mfma_i8_32x32x32(__builtin_bit_cast(i32x4, a1), qf[ks], s[1]);
     }
 }
 
-template <int D, bool CAUSAL, bool OUT_F32>
-__global__ __launch_bounds__(kAThreads) void sage_attn_kernel(PrefillArgs a, SageWs w)
+// Masked keys of a score tile (past the sequence end, or above the causal
+// diagonal) become INT_MIN; a real score is at most 128 * 127^2 in magnitude.
+template <bool CAUSAL>
+__device__ __forceinline__ void mask_i8(i32x16 (&s)[2], int k0, int N, int g, int my_q)
 {
-    constexpr int kStage = SCfg<D>::kStage;
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kStage];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = k0 + 32 * blk + 16 * g + r;
+            if (key >= N || (CAUSAL && key > my_q))
+                s[blk][r] = INT_MIN;
+        }
+}
+
+__device__ __forceinline__ int imax_tile(const i32x16 (&s)[2])
+{
+    int m = INT_MIN;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2)
+            m = vmax3_i32(m, s[blk][r], s[blk][r + 1]);
+    return m;
+}
+
+// Running state of one wave: O^T accumulators, the exact running max m (log2
+// units, the reference P is quantised against), the row sum l of the
+// unquantised 448-scaled probabilities, and a pending O rescale.
+template <int D>
+struct SState {
+    f32x16 o[D / 32];
+    float m, l, alpha;
+    bool pending;
+};
+
+// Raise m to include a tile whose lane-half max is mx (log2 units, -inf for a
+// fully masked row).  l is rescaled now; O only after the PV product of the
+// tile exponentiated against the old m (apply_pending, one step later).
+template <int D>
+__device__ __forceinline__ void s_raise(SState<D> &st, float mx)
+{
+    mx = max_xor32(mx);
+    if (__any(mx > st.m)) {
+        const float m_new = fmaxf(st.m, mx);
+        const float alpha = fast_exp2(st.m - m_new);
+        st.l *= alpha;
+        st.alpha = alpha;
+        st.pending = true;
+        st.m = m_new;
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void s_apply_pending(SState<D> &st)
+{
+    if (st.pending) {
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c)
+            st.o[c] *= st.alpha;
+        st.pending = false;
+    }
+}
+
+// p = 448 * 2^(c * s + log2(448) - m - log2(448)) for the whole tile, E4M3-packed
+// (byte 16*blk + r of the lane = score s[blk][r]); returns the lane's row sum.
+__device__ __forceinline__ float s_exp_tile(const i32x16 (&s)[2], float c, float bias, bool masked,
+                                            uint32_t (&pk)[8])
+{
+    float rs = 0.f;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int r = 0; r < 16; r += 4) {
+            float p[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int v = s[blk][r + e];
+                p[e] = fast_exp2(masked && v == INT_MIN ? -INFINITY : fmaf((float)v, c, bias));
+                rs += p[e];
+            }
+            int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+            wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wd, true);
+            pk[4 * blk + r / 4] = (uint32_t)wd;
+        }
+    return rs;
+}
+
+// One pipeline step t: PV(t) with P(t) (E4M3, computed against the running
+// max before the last raise), QK(t+2) into s_qk (masked when mask_qk), and
+// the exponentials of tile t+1 (s_exp, scale c_exp, against the current m)
+// into p_next, adding their row sum to l.  Returns the lane's integer max of
+// the masked s_qk.
+template <int D, bool CAUSAL, class Dma>
+__device__ __forceinline__ int s_step(SState<D> &st, const i32x4 (&qf)[D / 32], uint32_t kst,
+                                      uint32_t vst, const SLanes<D> &ln, const i32x16 (&s_exp)[2],
+                                      i32x16 (&s_qk)[2], const uint32_t (&p_cur)[8],
+                                      uint32_t (&p_next)[8], float c_exp, bool mask_exp,
+                                      bool mask_qk, int k0_qk, int N, int g, int my_q,
+                                      const Dma &dma)
+{
+    using SC = SSched<D>;
+    constexpr int NS = SC::NS, NQK = SC::NQK, RA = SC::RA;
+    const float bias = kLog2_448 - st.m;
+    // operand of slot S: u32x4 for QK, two of them for PV
+    u32x4 opa[RA + 1], opb[RA + 1];
+    auto read_op = [&](auto sc) {
+        constexpr int S = decltype(sc)::value;
+        if constexpr (S < NQK) {
+            constexpr int blk = S % 2, ks = S / 2;
+            opa[S % (RA + 1)] = lds_read_b128<blk * 32 * D>(kst + ln.k[ks]);
+        } else {
+            constexpr int c = S - NQK;
+            opa[S % (RA + 1)] = lds_read_b128<c * 32 * kBlk>(vst + ln.vlo);
+            opb[S % (RA + 1)] = lds_read_b128<c * 32 * kBlk>(vst + ln.vhi);
+        }
+    };
+    float p[32];
+    float rs0 = 0.f, rs1 = 0.f;
+    uint32_t wd = 0;
+    int imx0 = INT_MIN, imx1 = INT_MIN;
+    s_qk[0] = i32x16{};
+    s_qk[1] = i32x16{};
+    // fold score R (exponentiated in an earlier slot): row sum and E4M3 packing
+    auto fold = [&](auto rc) {
+        constexpr int R = decltype(rc)::value;
+        if constexpr (R % 2 == 0) {
+            rs0 += p[R];
+        } else {
+            rs1 += p[R];
+            constexpr int blk = R / 16, r = R % 16;
+            if constexpr ((r & 3) == 1) {
+                wd = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(p[R - 1], p[R], 0, false);
+            } else {
+                wd = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(p[R - 1], p[R], (int)wd, true);
+                p_next[4 * blk + r / 4] = wd;
+                asm volatile("" : "+v"(p_next[4 * blk + r / 4]));
+            }
+        }
+        asm volatile("" : "+v"(rs0), "+v"(rs1), "+v"(wd));
+    };
+    static_for<0, RA>([&](auto i) { read_op(i); });
+    static_for<0, NS>([&](auto sc) {
+        constexpr int S = decltype(sc)::value;
+        if constexpr (S + RA < NS)
+            read_op(std::integral_constant<int, S + RA>{});
+        if constexpr (S < NQK) {
+            lgkm_wait<SC::after(S)>(opa[S % (RA + 1)]);
+            s_qk[S % 2] = mfma_i8_32x32x32(__builtin_bit_cast(i32x4, opa[S % (RA + 1)]),
+                                           qf[S / 2], s_qk[S % 2]);
+        } else {
+            constexpr int c = S - NQK;
+            lgkm_wait<SC::after(S)>(opb[S % (RA + 1)]);
+            const u32x4 lo = opa[S % (RA + 1)], hi = opb[S % (RA + 1)];
+            const i32x8 va = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                              (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            const i32x8 pb = {(int)p_cur[0], (int)p_cur[1], (int)p_cur[2], (int)p_cur[3],
+                              (int)p_cur[4], (int)p_cur[5], (int)p_cur[6], (int)p_cur[7]};
+            st.o[c] = mfma_fp8_32x32x64(va, pb, st.o[c]);
+        }
+        dma(sc);
+        static_for<SC::first_score(S), SC::first_score(S + 1)>([&](auto rc) {
+            constexpr int R = decltype(rc)::value;
+            const int v = s_exp[R / 16][R % 16];
+            p[R] = fast_exp2(mask_exp && v == INT_MIN ? -INFINITY : fmaf((float)v, c_exp, bias));
+            asm volatile("" : "+v"(p[R]));
+        });
+        if constexpr (S > 0)
+            static_for<SC::first_score(S - 1), SC::first_score(S)>(fold);
+        if constexpr (S == NQK) {
+            if (mask_qk)
+                mask_i8<CAUSAL>(s_qk, k0_qk, N, g, my_q);
+        }
+        static_for<0, 16>([&](auto kc) {
+            constexpr int k = decltype(kc)::value;
+            if constexpr (SC::max_slot(k) == S) {
+                constexpr int R = 2 * k, blk = R / 16, r = R % 16;
+                if constexpr (k % 2 == 0)
+                    imx0 = vmax3_i32(imx0, s_qk[blk][r], s_qk[blk][r + 1]);
+                else
+                    imx1 = vmax3_i32(imx1, s_qk[blk][r], s_qk[blk][r + 1]);
+                asm volatile("" : "+v"(imx0), "+v"(imx1));
+            }
+        });
+        __builtin_amdgcn_sched_barrier(0);
+    });
+    static_for<SC::first_score(NS - 1), 32>(fold);
+    st.l += rs0 + rs1;
+    return imx0 > imx1 ? imx0 : imx1;
+}
+
+template <int D, bool CAUSAL, bool OUT_F32>
+__device__ __forceinline__ void sage_qtile(const PrefillArgs &a, const SageWs &w,
+                                           unsigned char *smem, int bh, int qt, int wave, int lane)
+{
+    constexpr int kK = SCfg<D>::kKBytes, kV = SCfg<D>::kVBytes;
     const int g = lane >> 5, n = lane & 31;
     const int N = a.N, nblk = (N + kBlk - 1) / kBlk, Npad = nblk * kBlk;
-    const int nqt = (N + kBM - 1) / kBM;
-    const int BH = a.B * a.H;
-    int bh, qi;
-    const int wg = blockIdx.x;
-    if ((BH & 7) == 0) {
-        const int xcd = wg & 7, slot = wg >> 3;
-        bh = xcd + 8 * (slot / nqt);
-        qi = slot % nqt;
-    } else {
-        bh = wg / nqt;
-        qi = wg % nqt;
-    }
-    const int qt = CAUSAL ? nqt - 1 - qi : qi;
     const int h = bh % a.H, b = bh / a.H;
     const int bg = b * a.Hkv + h / (a.H / a.Hkv);
     const int q0 = qt * kBM, qw0 = q0 + wave * kQW, my_q = qw0 + n;
     const int8_t *khat = w.khat + (size_t)bg * Npad * D;
     const uint8_t *vhatT = w.vhatT + (size_t)bg * D * Npad;
+    const float *kdel = w.kdelta + (size_t)bg * nblk;
     const int kend = CAUSAL ? min(N, q0 + kBM) : N;
     const int ntiles = (kend + kBlk - 1) / kBlk;
-
-    issue_tile<D>(smem, khat, vhatT, Npad, 0, wave, lane);
+    const int ntw = CAUSAL ? min(ntiles, (qw0 + kQW - 1) / kBlk + 1) : ntiles;
+    auto kst = [&](int t) { return smem + (t & 3) * kK; };
+    auto vst = [&](int t) { return smem + 4 * kK + (t & 3) * kV; };
+    auto needs_mask = [&](int t) {
+        const int k0 = t * kBlk;
+        return (CAUSAL && k0 + kBlk - 1 > qw0) || k0 + kBlk > N;
+    };
+    // direct loads: one 1 KB piece of each tile per wave (waves beyond the
+    // piece count load nothing); the V^^T tile's rows are Npad bytes apart
+    const SDma<D> dm = s_dma<D>(wave, lane, Npad);
+    const bool has_k = wave < SCfg<D>::kKPieces, has_v = wave < SCfg<D>::kVPieces;
+    auto load_k = [&](int t) {
+        if (t < ntiles && has_k)
+            dma16_rsrc(raw_rsrc(khat + (size_t)t * kBlk * D, kK), dm.k, kst(t) + wave * 1024);
+    };
+    auto load_v = [&](int t) {
+        if (t < ntiles && has_v)
+            dma16_rsrc(raw_rsrc(vhatT + (size_t)t * kBlk, (uint32_t)((D - 1) * Npad + kBlk)), dm.v,
+                       vst(t) + wave * 1024);
+    };
+    load_k(0);
+    load_k(1);
+    load_k(2);
+    load_v(0);
+    load_k(3);
+    load_v(1);
 
     // Q^^T fragments (B operand of the INT8 MFMA, K = 32 per step): lane holds
     // Q^[my_q][32*ks + 16*g .. +15].  Rows past N are zero in the workspace.
@@ -365,125 +643,115 @@ __global__ __launch_bounds__(kAThreads) void sage_attn_kernel(PrefillArgs a, Sag
     for (int ks = 0; ks < D / 32; ++ks)
         qf[ks] = __builtin_bit_cast(i32x4, ld16(qrow + ks * 32 + g * 16));
     // the 32 queries of a wave lie in one 64-token block
-    const float dq = w.qdelta[(size_t)bh * nblk + min(qw0, N - 1) / kBlk];
-    const float cq = a.scale * kLog2e * dq;
-    const float *kdel = w.kdelta + (size_t)bg * nblk;
+    const float cq = a.scale * kLog2e * w.qdelta[(size_t)bh * nblk + min(qw0, N - 1) / kBlk];
+    // per-tile score scales c(t) = cq * dK(t) for tiles t+1 .. t+5 of an even
+    // step t; those of tiles t+4, t+5 are loaded at step t and land by the
+    // synchronisation before step t+2
+    auto kd = [&](int t) { return t < ntiles ? kdel[t] : 1.f; };
+    float c1 = cq * kd(1), c2 = cq * kd(2), c3 = cq * kd(3), kd4 = 1.f, kd5 = 1.f;
+    const float c0 = cq * kd(0);
 
-    const int krow = perm32(n);  // K^ row of MFMA row n, + 32*blk
-    f32x16 o[D / 32];
+    const SLanes<D> ln = s_lanes<D>(lane);
+    SState<D> st;
 #pragma unroll
     for (int c = 0; c < D / 32; ++c)
-        o[c] = f32x16{};
-    float m = -INFINITY, l = 0.f;
-    // the K scale of tile t is read one tile ahead, before the next tile's
-    // direct loads are issued, so that waiting for it never waits for them
-    float kd_next = kdel[0];
+        st.o[c] = f32x16{};
+    st.l = 0.f;
+    st.alpha = 1.f;
+    st.pending = false;
 
-    for (int t = 0; t < ntiles; ++t) {
-        const int k0 = t * kBlk;
-        unsigned char *stage = smem + (t & 1) * kStage;
-        vm_wait_all();
-        __syncthreads();
-        const float kd = kd_next;
-        if (t + 1 < ntiles) {
-            kd_next = kdel[t + 1];
-            issue_tile<D>(smem + ((t + 1) & 1) * kStage, khat, vhatT, Npad, k0 + kBlk, wave, lane);
-        }
-        if (CAUSAL && k0 > qw0 + kQW - 1)
-            continue;
+    i32x16 sA[2], sB[2];   // S(j): sA for even j, sB for odd j
+    uint32_t pA[8], pB[8];  // P(j) likewise
 
-        // S^T = K^ Q^^T (exact int32)
-        i32x16 s[2] = {i32x16{}, i32x16{}};
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-            const int row = 32 * blk + krow;
-            const int sw = kswz<D>(row);
-#pragma unroll
-            for (int ks = 0; ks < D / 32; ++ks) {
-                const int chunk = (2 * ks + g) ^ sw;
-                const i32x4 ka = *(const i32x4 *)(stage + row * D + chunk * 16);
-                s[blk] = mfma_i8_32x32x32(ka, qf[ks], s[blk]);
-            }
-        }
-
-        // scores in log2 units: S * log2e = c * int (c > 0).  The tile max is
-        // taken on the integers (masked keys as INT_MIN), the exponent
-        // 2^(c*int + log2(448) - m) with one FMA per score; on tiles that
-        // need the mask, masked keys get -inf (a key masked through INT_MIN
-        // alone would not vanish when c is tiny).
-        const float c = cq * kd;
-        const bool need_mask = (CAUSAL && k0 + kBlk - 1 > qw0) || k0 + kBlk > N;
-        int imx = INT_MIN;
-        if (need_mask) {
-#pragma unroll
-            for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = k0 + 32 * blk + 16 * g + r;
-                    if (key >= N || (CAUSAL && key > my_q))
-                        s[blk][r] = INT_MIN;
-                }
-        }
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-            for (int r = 0; r < 16; r += 2)
-                imx = vmax3_i32(imx, s[blk][r], s[blk][r + 1]);
-        // a row with every key of the tile masked contributes -inf
-        const float mx = max_xor32(imx == INT_MIN ? -INFINITY : (float)imx * c);
-        // exact running max (P is quantised against it)
-        if (__any(mx > m)) {
-            const float m_new = fmaxf(m, mx);
-            const float alpha = fast_exp2(m - m_new);
-            l *= alpha;
-#pragma unroll
-            for (int cc = 0; cc < D / 32; ++cc)
-                o[cc] *= alpha;
-            m = m_new;
-        }
-        // p = 448 * 2^(c*int - m) <= 448; E4M3 codes packed 4 per dword:
-        // byte 16*blk + r of the lane = key 32*blk + 16*g + r
-        uint32_t pk[8];
-        float rs0 = 0.f, rs1 = 0.f;
-        const float bias = kLog2_448 - m;
-        auto expo = [&](int v) {
-            const float x = fmaf((float)v, c, bias);
-            return fast_exp2(need_mask && v == INT_MIN ? -INFINITY : x);
-        };
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-            for (int r = 0; r < 16; r += 4) {
-                const float p0 = expo(s[blk][r]);
-                const float p1 = expo(s[blk][r + 1]);
-                const float p2 = expo(s[blk][r + 2]);
-                const float p3 = expo(s[blk][r + 3]);
-                rs0 += p0 + p2;
-                rs1 += p1 + p3;
-                int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
-                wd = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wd, true);
-                pk[4 * blk + r / 4] = (uint32_t)wd;
-            }
-        l += rs0 + rs1;
-
-        // O^T += V^^T P^^T (FP8, K = 64 keys per MFMA)
-        const i32x8 pb = {(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3],
-                          (int)pk[4], (int)pk[5], (int)pk[6], (int)pk[7]};
-        const unsigned char *vt = stage + SCfg<D>::kKBytes;
-#pragma unroll
-        for (int cc = 0; cc < D / 32; ++cc) {
-            const int d = 32 * cc + perm32(n);
-            const int sw = vswz(d);
-            const u32x4 lo = *(const u32x4 *)(vt + d * kBlk + ((g ^ sw) << 4));
-            const u32x4 hi = *(const u32x4 *)(vt + d * kBlk + (((2 + g) ^ sw) << 4));
-            const i32x8 va = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                              (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-            o[cc] = mfma_fp8_32x32x64(va, pb, o[cc]);
+    // pre-step: S(0), S(1); m from S(0) (exact), P(0); raise for S(1)
+    vm_wait_n<0>();
+    __syncthreads();
+    if (0 < ntw) {
+        qk_tile_i8<D>(sA, qf, lds_addr(kst(0)), ln);
+        if (ntw > 1)
+            qk_tile_i8<D>(sB, qf, lds_addr(kst(1)), ln);
+        const bool m0 = needs_mask(0);
+        if (m0)
+            mask_i8<CAUSAL>(sA, 0, N, g, my_q);
+        const int i0 = imax_tile(sA);
+        st.m = max_xor32(i0 == INT_MIN ? -INFINITY : (float)i0 * c0);
+        st.l = s_exp_tile(sA, c0, kLog2_448 - st.m, m0, pA);
+        if (ntw > 1) {
+            if (needs_mask(1))
+                mask_i8<CAUSAL>(sB, kBlk, N, g, my_q);
+            const int i1 = imax_tile(sB);
+            s_raise<D>(st, i1 == INT_MIN ? -INFINITY : (float)i1 * c1);
         }
     }
 
+    // step t: as in the exact kernel, 4-stage rings, synchronisation before
+    // every even step, loads of K(t+4) and V(t+2) spread over the slots
+    auto step = [&](int t, auto par, float c_exp, float c_qk) {
+        constexpr int E = decltype(par)::value;
+        if constexpr (E == 0) {
+            vm_wait_n<0>();
+            __syncthreads();
+            if (t + 4 < ntiles)
+                kd4 = kdel[t + 4];
+            if (t + 5 < ntiles)
+                kd5 = kdel[t + 5];
+        }
+        const bool lk = t + 4 < ntiles && has_k, lv = t + 2 < ntiles && has_v;
+        const __amdgpu_buffer_rsrc_t rk = raw_rsrc(khat + (size_t)(lk ? t + 4 : 0) * kBlk * D, kK);
+        const __amdgpu_buffer_rsrc_t rv =
+            raw_rsrc(vhatT + (size_t)(lv ? t + 2 : 0) * kBlk, (uint32_t)((D - 1) * Npad + kBlk));
+        unsigned char *const k_st = kst(t + 4) + wave * 1024, *const v_st = vst(t + 2) + wave * 1024;
+        auto dma = [&](auto sc) {
+            constexpr int S = decltype(sc)::value;
+            if constexpr (S == SSched<D>::dma_slot(0)) {
+                if (lk)
+                    dma16_rsrc(rk, dm.k, k_st);
+            }
+            if constexpr (S == SSched<D>::dma_slot(1)) {
+                if (lv)
+                    dma16_rsrc(rv, dm.v, v_st);
+            }
+        };
+        i32x16(&s_exp)[2] = E ? sA : sB;  // S(t+1)
+        i32x16(&s_qk)[2] = E ? sB : sA;   // S(t+2)
+        uint32_t(&pc)[8] = E ? pB : pA;   // P(t)
+        uint32_t(&pn)[8] = E ? pA : pB;   // P(t+1)
+        const float l_before = st.l;
+        const int imx = s_step<D, CAUSAL>(st, qf, lds_addr(kst(t + 2)), lds_addr(vst(t)), ln,
+                                          s_exp, s_qk, pc, pn, c_exp, needs_mask(t + 1),
+                                          needs_mask(t + 2), (t + 2) * kBlk, N, g, my_q, dma);
+        if (t + 1 >= ntw)
+            st.l = l_before;  // tile t+1 does not exist for this wave
+        // PV(t) has been issued with P(t): O can take the factor of the raise
+        // that P(t+1) was computed after
+        s_apply_pending<D>(st);
+        if (t + 2 < ntw)
+            s_raise<D>(st, imx == INT_MIN ? -INFINITY : (float)imx * c_qk);
+    };
+    int t = 0;
+    for (; t + 1 < ntw; t += 2) {
+        step(t, std::integral_constant<int, 0>{}, c1, c2);
+        step(t + 1, std::integral_constant<int, 1>{}, c2, c3);
+        c1 = c3;
+        c2 = cq * kd4;
+        c3 = cq * kd5;
+    }
+    if (t < ntw) {
+        step(t, std::integral_constant<int, 0>{}, c1, c2);
+        ++t;
+    }
+    for (; t < ntiles; ++t) {
+        if ((t & 1) == 0) {
+            vm_wait_n<0>();
+            __syncthreads();
+        }
+        load_k(t + 4);
+        load_v(t + 2);
+    }
+    s_apply_pending<D>(st);
+
     // O = acc * delta_V / l448 ; lse = (m + log2 l448 - log2 448) ln2 + scale * q.kmean
-    const float lt = sum_xor32(l);
+    const float lt = sum_xor32(st.l);
     if (my_q < N) {
         const float inv = 1.f / lt;
         const float *vs = w.vscale + (size_t)bg * D;
@@ -492,7 +760,7 @@ __global__ __launch_bounds__(kAThreads) void sage_attn_kernel(PrefillArgs a, Sag
             float val[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                val[r] = o[cc][r] * vs[32 * cc + 16 * g + r] * inv;
+                val[r] = st.o[cc][r] * vs[32 * cc + 16 * g + r] * inv;
             if constexpr (OUT_F32) {
                 float *orow = (float *)a.o + ((size_t)bh * N + my_q) * D + 32 * cc + 16 * g;
 #pragma unroll
@@ -512,8 +780,40 @@ __global__ __launch_bounds__(kAThreads) void sage_attn_kernel(PrefillArgs a, Sag
             }
         }
         if (a.lse && g == 0)
-            a.lse[(size_t)bh * N + my_q] = (m + log2f(lt) - kLog2_448) * kLn2 +
+            a.lse[(size_t)bh * N + my_q] = (st.m + log2f(lt) - kLog2_448) * kLn2 +
                                            a.scale * w.qkdot[(size_t)bh * N + my_q];
+    }
+}
+
+template <int D, bool CAUSAL, bool OUT_F32>
+__global__ __launch_bounds__(kAThreads) void sage_attn_kernel(PrefillArgs a, SageWs w)
+{
+    __shared__ __attribute__((aligned(1024)))
+    unsigned char smem[4 * SCfg<D>::kKBytes + 4 * SCfg<D>::kVBytes];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nqt = (a.N + kBM - 1) / kBM;
+    // causal: workgroup j of a head takes query tiles nqt-1-j and j (equal work)
+    const int nw = CAUSAL ? (nqt + 1) / 2 : nqt;
+    const int BH = a.B * a.H;
+    int bh, j;
+    const int wg = blockIdx.x;
+    if ((BH & 7) == 0) {
+        const int xcd = wg & 7, slot = wg >> 3;
+        bh = xcd + 8 * (slot / nw);
+        j = slot % nw;
+    } else {
+        bh = wg / nw;
+        j = wg % nw;
+    }
+    if (CAUSAL) {
+        sage_qtile<D, CAUSAL, OUT_F32>(a, w, smem, bh, nqt - 1 - j, wave, lane);
+        if (j < nqt - 1 - j) {
+            __syncthreads();  // every wave is done with the LDS stages
+            sage_qtile<D, CAUSAL, OUT_F32>(a, w, smem, bh, j, wave, lane);
+        }
+    } else {
+        sage_qtile<D, CAUSAL, OUT_F32>(a, w, smem, bh, j, wave, lane);
     }
 }
 
@@ -548,7 +848,7 @@ hipError_t launch_d(const SageArgs &sa, hipStream_t s)
         return e;
     const int nqt = (a.N + kBM - 1) / kBM;
     ProfScope ps("sage_attn", s);
-    dim3 grid(BH * nqt), block(kAThreads);
+    dim3 grid(BH * (a.causal ? (nqt + 1) / 2 : nqt)), block(kAThreads);
     if (a.causal) {
         if (a.out_fp32)
             hipLaunchKernelGGL((sage_attn_kernel<D, true, true>), grid, block, 0, s, a, w);
