@@ -63,6 +63,24 @@ def test_small_decode(attn, case, out_dtype):
                 bf16_out=out_dtype == torch.bfloat16, what=str(case))
 
 
+def test_rising_scores_decode(attn):
+    """Scores rising from key to key move each chunk's running max on every
+    sub-tile (the decode kernel's rescale path)."""
+    from tests.test_gpu_prefill import _rising_keys
+    B, H, Hkv, N, d = 2, 8, 2, 1500, 128
+    qf, k, v = _rising_keys(B, H, Hkv, N, d, seed=5, top=40.0)
+    q = qf[:, :, 0].contiguous()
+    seqlens = torch.tensor((1500, 901), dtype=torch.int32)
+    k[1, :, 901:] = float("nan")
+    v[1, :, 901:] = float("nan")
+    o, lse = attn.decode(q.cuda(), k.cuda(), v.cuda(), seqlens.cuda(), split_tokens=256,
+                         out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = _oracle(q, k, v, seqlens, 1 / math.sqrt(d))
+    check_exact(o.float().cpu().numpy(), o_ref, lse.cpu().numpy(), lse_ref, bf16_out=False,
+                what="rising scores decode")
+
+
 def test_split_size_invariance(attn):
     B, H, Hkv, N, d = 2, 8, 2, 2000, 128
     q, k, v, seqlens = workloads.make_decode(B, H, Hkv, N, d, len_lo=1500, len_hi=2000, seed=9)

@@ -88,6 +88,35 @@ def test_large_scores_and_scale(attn):
         check_exact(o, o_ref, lse, lse_ref, bf16_out=False, what="large scores")
 
 
+def _rising_keys(B, H, Hkv, N, d, seed, top=40.0):
+    """q and k share one direction u, and the keys' component along it grows
+    with the key index: every row's score rises from key to key, so the running
+    max of the online softmax moves on (almost) every key tile, exercising the
+    kernels' rescaling paths (not just the first tile's max)."""
+    g = torch.Generator().manual_seed(seed)
+    u = torch.randn(d, generator=g)
+    u = u / u.norm()
+    q = torch.randn((B, H, N, d), generator=g) * 0.3 + u
+    ramp = torch.linspace(0.0, top, N)[None, None, :, None]
+    k = torch.randn((B, Hkv, N, d), generator=g) * 0.3 + ramp * u
+    v = torch.randn((B, Hkv, N, d), generator=g)
+    return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("shape", [(1, 2, 2, 700, 128), (1, 4, 2, 333, 64)],
+                         ids=lambda s: "B%dH%dKV%dN%dd%d" % s)
+def test_rising_scores(attn, shape, causal):
+    B, H, Hkv, N, d = shape
+    q, k, v = _rising_keys(B, H, Hkv, N, d, seed=N + d)
+    scale = 1 / math.sqrt(d)
+    for out_dtype in (torch.float32, torch.bfloat16):
+        o, lse = _run(attn, q, k, v, causal, out_dtype)
+        o_ref, lse_ref = _oracle_full(q, k, v, causal, scale)
+        check_exact(o, o_ref, lse, lse_ref, bf16_out=out_dtype == torch.bfloat16,
+                    what="rising scores %s" % (shape,))
+
+
 def test_closed_forms_on_device(attn):
     g = torch.Generator().manual_seed(22)
     B, H, N, d = 1, 2, 200, 128

@@ -77,6 +77,20 @@ def test_small_vs_emulator(attn, case):
     assert cos >= 0.999, (case, cos, rel)
 
 
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_rising_scores_vs_emulator(attn, causal):
+    """Scores that rise from key to key move the exact running max on almost
+    every tile (P is quantised against it): exercises the deferred O rescale."""
+    from tests.test_gpu_prefill import _rising_keys
+    B, H, N, d = 1, 2, 600, 128
+    q, k, v = _rising_keys(B, H, H, N, d, seed=77, top=25.0)
+    o, lse = _run(attn, q, k, v, causal)
+    qb, kb, vb = _bits(q, k, v)
+    o_emu, lse_emu = oracle.sage_rows(qb, kb, vb, causal=causal, scale=1 / math.sqrt(d),
+                                      tile_n=64, blk=64)
+    _check_vs_emulator(o, lse, o_emu, lse_emu, "rising scores causal=%s" % causal)
+
+
 def test_bf16_output_and_no_lse_bias(attn):
     """bf16 store path; K with a large shared bias exercises Smooth-K and the
     LSE correction (q . kmean is added back)."""
