@@ -8,9 +8,9 @@ own per-kernel HIP events (attn_profiler_*) time the dominant kernel inside
 the same timed region for the roofline figure.
 
 The same JSON line also carries the split-KV decode workload (HBM bound,
-GB/s) and, when built, the quantised prefill workload, each with its own
-roofline object, and the fp64 CPU oracle timed on a bounded sample of the
-headline workload.
+GB/s; contiguous caches, and the same caches spread over a pool of 16-row
+pages) and the quantised prefill workload, each with its own roofline object,
+and the fp64 CPU oracle timed on a bounded sample of the headline workload.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                   [--only prefill|decode|sage] [--calibrate-copy]
@@ -133,17 +133,41 @@ def bench_decode(args, stream):
     ms, per_kernel = time_calls(step, max(args.steps, 20), args.warmup, stream)
     # algorithmic bytes: every valid K and V row once, q, o (bf16) and lse (fp32)
     alg_bytes = sum_len * w.Hkv * w.d * 2 * 2 + w.B * w.H * w.d * 2 * 2 + w.B * w.H * 4
-    kms = per_kernel["decode_split"][0]
-    achieved = alg_bytes / (kms * 1e-3) / 1e9
-    return {
-        "workload": w.name, "value": alg_bytes / (ms * 1e-3) / 1e9, "unit": "GB/s",
-        "ms_per_step": ms, "sum_seqlen": sum_len, "algorithmic_bytes": alg_bytes,
-        "kernels_ms": {k_: t for k_, (t, _) in per_kernel.items()},
-        "roofline": {"bound": "hbm", "kernel": "decode_split", "achieved": achieved,
-                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
-                     "kernel_ms": kms,
-                     "traffic": measured_traffic("decode_split", ["decode.hip", "cdna4.hpp"])},
-    }
+
+    def result(ms, per_kernel, kernel, name, extra):
+        kms = per_kernel[kernel][0]
+        achieved = alg_bytes / (kms * 1e-3) / 1e9
+        r = {
+            "workload": name, "value": alg_bytes / (ms * 1e-3) / 1e9, "unit": "GB/s",
+            "ms_per_step": ms, "sum_seqlen": sum_len, "algorithmic_bytes": alg_bytes,
+            "kernels_ms": {k_: t for k_, (t, _) in per_kernel.items()},
+            "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved,
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": achieved / PEAK_HBM_GBS, "kernel_ms": kms,
+                         "traffic": measured_traffic(kernel, ["decode.hip", "cdna4.hpp"])},
+        }
+        r.update(extra)
+        return r
+
+    res = result(ms, per_kernel, "decode_split", w.name, {})
+    # the same caches spread over a pool of 16-row pages in a random order
+    ps = 16
+    table, num_pages = workloads.make_page_table(seqlens.cpu(), ps, seed=77, spare_pages=0,
+                                                 max_pages=w.N // ps)
+    kp = workloads.paginate(k, table, num_pages, ps)
+    vp = workloads.paginate(v, table, num_pages, ps)
+    del k, v
+    torch.cuda.empty_cache()
+    table = table.cuda()
+
+    def step_paged():
+        A.decode_paged(q, kp, vp, table, seqlens, split_tokens=w.split_tokens, o=o, lse=lse,
+                       workspace=ws, stream=stream)
+
+    ms_p, per_kernel_p = time_calls(step_paged, max(args.steps, 20), args.warmup, stream)
+    res["paged"] = result(ms_p, per_kernel_p, "decode_split_paged", w.name + "_paged16",
+                          {"page_size": ps, "num_pages": num_pages})
+    return res
 
 
 def bench_sage(args, stream):
@@ -245,7 +269,9 @@ def main():
     if args.only in (None, "decode"):
         log("decode: gqa_decode")
         dec = bench_decode(args, stream)
-        log("decode %.3f ms/step, %.1f GB/s" % (dec["ms_per_step"], dec["value"]))
+        log("decode %.3f ms/step, %.1f GB/s; paged (16-row pages) %.3f ms/step, %.1f GB/s" % (
+            dec["ms_per_step"], dec["value"], dec["paged"]["ms_per_step"],
+            dec["paged"]["value"]))
         out["decode"] = dec
         torch.cuda.empty_cache()
     if pre is None:

@@ -128,6 +128,40 @@ attn_status attn_decode(const void *q, const void *k_cache, const void *v_cache,
 /* Bytes of workspace attn_decode needs (0 for invalid sizes). */
 size_t attn_decode_workspace_size(int B, int H, int N_max, int d, int split_tokens);
 
+/*
+ * attn_decode over paged KV caches: the cache is a pool of fixed-size pages
+ * and a per-sequence page table names the page holding each run of
+ * page_size key positions (the non-contiguous KV layout of paged serving
+ * caches: "flashattention-kernels" page §3, a library interface covering
+ * paged KV; "GPU kernel overview" page, the open gaps on decode with paged,
+ * non-contiguous KV memory).  The computation, the chunking into
+ * split_tokens keys and the merge are those of attn_decode: for the same keys
+ * and values it returns bit-identical results.
+ *   k_pages, v_pages   device bf16 [num_pages, Hkv, page_size, d].
+ *   block_table  device int32 [B, max_pages]: key position n of sequence b
+ *              (0 <= n < seqlens[b]) is row n % page_size of page
+ *              block_table[b * max_pages + n / page_size].  Entries beyond a
+ *              sequence's last page are never read.  Entries must lie in
+ *              [0, num_pages); the kernels clamp others into that range
+ *              (the result is then unspecified, but no access leaves the pool).
+ *   seqlens    device int32 [B]; values are clamped to [1, max_pages * page_size].
+ *   page_size  a power of two, >= 16 and >= split_tokens / 64 (a chunk spans
+ *              at most 64 pages).
+ *   other arguments as for attn_decode (N_max = max_pages * page_size).
+ *   workspace  at least attn_decode_workspace_size(B, H, max_pages * page_size,
+ *              d, split_tokens) bytes.
+ * Errors: those of attn_decode; ATTN_ERR_INVALID_ARG for a null block_table,
+ * non-positive num_pages or max_pages, or a page_size that is not a power of
+ * two; ATTN_ERR_UNSUPPORTED for a page_size below the limits above or
+ * max_pages * page_size beyond 2^31 - 1.
+ */
+attn_status attn_decode_paged(const void *q, const void *k_pages, const void *v_pages,
+                              const int32_t *block_table, const int32_t *seqlens, void *o,
+                              float *lse, int B, int H, int Hkv, int num_pages, int page_size,
+                              int max_pages, int d, float scale, int mode, int o_dtype,
+                              int split_tokens, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
 /* Static description of a status code. */
 const char *attn_status_string(int status);
 

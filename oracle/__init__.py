@@ -24,6 +24,10 @@ What each routine follows:
   emulated step by step ("GPU kernel overview" page, SageAttention chain and
   its insight that QK suits INT8 while PV suits FP8).
 * ``e4m3_decode`` / ``e4m3_encode`` -- the OCP E4M3 ("fn") format.
+* ``gather_pages`` -- the paged KV layout (a pool of fixed-size pages named by
+  a per-sequence page table) turned back into contiguous caches, so that
+  paged decode is checked against ``attn_rows`` ("flashattention-kernels"
+  page, §3: paged KV among the layouts a decode library covers).
 """
 from __future__ import annotations
 
@@ -248,6 +252,30 @@ def quant_i8(x, delta) -> np.ndarray:
     x = np.asarray(x, dtype=np.float64)
     return np.array([lib.oracle_quant_i8(float(t), float(delta)) for t in x.ravel()],
                     dtype=np.int64).reshape(x.shape)
+
+
+def gather_pages(pages, block_table, seqlens, page_size: int):
+    """Contiguous caches from a paged pool, by the paged layout's definition.
+
+    pages [num_pages, Hkv, page_size, d] (any dtype); block_table [B, max_pages]
+    (int); seqlens [B].  Key position n of sequence b is row n % page_size of
+    page block_table[b, n // page_size] ("flashattention-kernels" page, §3:
+    the paged KV layouts a decode library covers).  Returns
+    [B, Hkv, max_pages * page_size, d] with positions >= seqlens[b] zero.
+    Plain loops over positions: this is the definition, not a fast path.
+    """
+    pages = np.asarray(pages)
+    block_table = np.asarray(block_table)
+    seqlens = np.asarray(seqlens)
+    P, Hkv, ps, d = pages.shape
+    if ps != page_size:
+        raise ValueError("page_size does not match the pool")
+    B, max_pages = block_table.shape
+    out = np.zeros((B, Hkv, max_pages * page_size, d), dtype=pages.dtype)
+    for b in range(B):
+        for n in range(int(seqlens[b])):
+            out[b, :, n, :] = pages[int(block_table[b, n // page_size]), :, n % page_size, :]
+    return out
 
 
 def num_threads() -> int:

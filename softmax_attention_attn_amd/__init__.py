@@ -8,7 +8,8 @@ the library's HIP kernels; there is no fallback.  Importing this package
 fails loudly when the library has not been built.
 
 The functions carry the C names (``attn_fwd``, ``attn_decode``, ...); the
-convenience wrappers ``fwd`` and ``decode`` allocate what the caller omits.
+convenience wrappers ``fwd``, ``decode`` and ``decode_paged`` allocate what the
+caller omits.
 """
 from __future__ import annotations
 
@@ -35,8 +36,8 @@ ATTN_OUT_FP32 = 1
 MODES = {"exact": ATTN_MODE_EXACT_BF16, "sage": ATTN_MODE_SAGE_QK_I8_BLK64_PV_FP8_E4M3}
 
 EXPORTS = ("attn_fwd", "attn_fwd_workspace_size", "attn_decode", "attn_decode_workspace_size",
-           "attn_status_string", "attn_last_error", "attn_profiler_enable",
-           "attn_profiler_read")
+           "attn_decode_paged", "attn_status_string", "attn_last_error",
+           "attn_profiler_enable", "attn_profiler_read")
 
 
 class AttnError(RuntimeError):
@@ -59,6 +60,9 @@ def _load():
     lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, sz, vp]
     lib.attn_decode_workspace_size.restype = sz
     lib.attn_decode_workspace_size.argtypes = [i, i, i, i, i]
+    lib.attn_decode_paged.restype = i
+    lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i,
+                                      i, vp, sz, vp]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_status_string.argtypes = [i]
     lib.attn_last_error.restype = ctypes.c_char_p
@@ -123,6 +127,14 @@ def attn_decode(q, k_cache, v_cache, seqlens, o, lse, B, H, Hkv, N_max, d, scale
     return int(_lib.attn_decode(q, k_cache, v_cache, seqlens, o, lse, B, H, Hkv, N_max, d,
                                 scale, mode, o_dtype, split_tokens, workspace,
                                 workspace_bytes, stream))
+
+
+def attn_decode_paged(q, k_pages, v_pages, block_table, seqlens, o, lse, B, H, Hkv, num_pages,
+                      page_size, max_pages, d, scale, mode, o_dtype, split_tokens, workspace,
+                      workspace_bytes, stream) -> int:
+    return int(_lib.attn_decode_paged(q, k_pages, v_pages, block_table, seqlens, o, lse, B, H,
+                                      Hkv, num_pages, page_size, max_pages, d, scale, mode,
+                                      o_dtype, split_tokens, workspace, workspace_bytes, stream))
 
 
 def attn_profiler_enable(enable: bool) -> None:
@@ -220,5 +232,43 @@ def decode(q, k_cache, v_cache, seqlens, *, scale: float | None = None,
                           _ptr(lse), B, H, Hkv, N_max, d, float(scale), ATTN_MODE_EXACT_BF16,
                           o_code, int(split_tokens), _ptr(workspace), workspace.numel(),
                           _stream(stream))
+    _check(st)
+    return o, lse
+
+
+def decode_paged(q, k_pages, v_pages, block_table, seqlens, *, scale: float | None = None,
+                 split_tokens: int = 512, out_dtype=torch.bfloat16, o=None, lse=None,
+                 with_lse: bool = True, workspace=None, stream=None):
+    """Split-KV decode over paged caches.  q [B,H,d]; k_pages/v_pages
+    [num_pages,Hkv,page_size,d] bf16; block_table int32 [B,max_pages];
+    seqlens int32 [B]."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_pages, "k_pages", torch.bfloat16, 4)
+    _need(v_pages, "v_pages", torch.bfloat16, 4)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(seqlens, "seqlens", torch.int32, 1)
+    B, H, d = q.shape
+    num_pages, Hkv, page_size, _ = k_pages.shape
+    if tuple(k_pages.shape) != (num_pages, Hkv, page_size, d) or \
+            tuple(v_pages.shape) != tuple(k_pages.shape):
+        raise ValueError("page pool shapes do not match q")
+    if block_table.shape[0] != B or seqlens.shape[0] != B:
+        raise ValueError("block_table and seqlens must have B rows")
+    max_pages = block_table.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o_code = {torch.bfloat16: ATTN_OUT_BF16, torch.float32: ATTN_OUT_FP32}[out_dtype]
+    if o is None:
+        o = torch.empty((B, H, d), dtype=out_dtype, device=q.device)
+    if lse is None and with_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    ws_bytes = attn_decode_workspace_size(B, H, max_pages * page_size, d, split_tokens)
+    if workspace is None:
+        workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=q.device)
+    st = _lib.attn_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
+                                _ptr(seqlens), _ptr(o), _ptr(lse), B, H, Hkv, num_pages,
+                                page_size, max_pages, d, float(scale), ATTN_MODE_EXACT_BF16,
+                                o_code, int(split_tokens), _ptr(workspace), workspace.numel(),
+                                _stream(stream))
     _check(st)
     return o, lse

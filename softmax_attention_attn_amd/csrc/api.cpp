@@ -78,6 +78,73 @@ void prof_end(hipStream_t s)
 
 }  // namespace attn
 
+namespace {
+
+// Checks shared by the contiguous and the paged decode; fills everything of
+// DecodeArgs but the cache layout.
+attn_status decode_common(const void *q, const void *k_cache, const void *v_cache,
+                          const int32_t *seqlens, void *o, float *lse, int B, int H, int Hkv,
+                          int N_max, int d, float scale, int mode, int o_dtype, int split_tokens,
+                          void *workspace, size_t workspace_bytes, attn::DecodeArgs &a)
+{
+    if (!q || !k_cache || !v_cache || !seqlens || !o)
+        return fail(ATTN_ERR_INVALID_ARG,
+                    "q, k_cache, v_cache, seqlens and o must be non-null device pointers");
+    if (B <= 0 || H <= 0 || Hkv <= 0 || N_max <= 0 || d <= 0)
+        return fail(ATTN_ERR_INVALID_ARG, "sizes must be positive (B=%d H=%d Hkv=%d N_max=%d d=%d)",
+                    B, H, Hkv, N_max, d);
+    if (H % Hkv != 0)
+        return fail(ATTN_ERR_INVALID_ARG, "H=%d is not a multiple of Hkv=%d", H, Hkv);
+    if (!valid_scale(scale))
+        return fail(ATTN_ERR_INVALID_ARG, "scale must be finite and > 0");
+    if (o_dtype != ATTN_OUT_BF16 && o_dtype != ATTN_OUT_FP32)
+        return fail(ATTN_ERR_INVALID_ARG, "unknown output dtype %d", o_dtype);
+    if (split_tokens <= 0 || split_tokens % 64 != 0)
+        return fail(ATTN_ERR_INVALID_ARG, "split_tokens=%d must be a positive multiple of 64",
+                    split_tokens);
+    if (mode != ATTN_MODE_EXACT_BF16)
+        return fail(mode == ATTN_MODE_SAGE_QK_I8_BLK64_PV_FP8_E4M3 ? ATTN_ERR_UNSUPPORTED
+                                                                   : ATTN_ERR_INVALID_ARG,
+                    "decode supports only the exact bf16 mode (mode=%d)", mode);
+    if (d != 64 && d != 128)
+        return fail(ATTN_ERR_UNSUPPORTED, "head dim d=%d (supported: 64, 128)", d);
+    const int G = H / Hkv;
+    if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
+        return fail(ATTN_ERR_UNSUPPORTED,
+                    "query heads per kv head %d (supported: 1, 2, 4, 8, 16)", G);
+    const long long splits = ((long long)N_max + split_tokens - 1) / split_tokens;
+    // one wave per possible chunk and one merge wave per (b, h), as int indices
+    if ((long long)B * Hkv * splits > 0x7fffff00LL || (long long)B * H > 0x7fffff00LL)
+        return fail(ATTN_ERR_UNSUPPORTED, "problem too large for the grid mapping");
+    const size_t need = attn_decode_workspace_size(B, H, N_max, d, split_tokens);
+    if (!workspace || workspace_bytes < need)
+        return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+
+    a = attn::DecodeArgs{};
+    a.q = q;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.seqlens = seqlens;
+    a.o = o;
+    a.lse = lse;
+    a.B = B;
+    a.H = H;
+    a.Hkv = Hkv;
+    a.N_max = N_max;
+    a.d = d;
+    a.scale = scale;
+    a.out_fp32 = o_dtype == ATTN_OUT_FP32;
+    a.split_tokens = split_tokens;
+    a.max_splits = (int)splits;
+    a.part_o = (float *)workspace;
+    a.part_lse = (float *)((char *)workspace +
+                           align_up(sizeof(float) * (size_t)B * H * splits * d, 256));
+    return ATTN_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char *attn_status_string(int status)
@@ -153,60 +220,47 @@ attn_status attn_decode(const void *q, const void *k_cache, const void *v_cache,
                         int N_max, int d, float scale, int mode, int o_dtype, int split_tokens,
                         void *workspace, size_t workspace_bytes, void *stream)
 {
-    if (!q || !k_cache || !v_cache || !seqlens || !o)
-        return fail(ATTN_ERR_INVALID_ARG,
-                    "q, k_cache, v_cache, seqlens and o must be non-null device pointers");
-    if (B <= 0 || H <= 0 || Hkv <= 0 || N_max <= 0 || d <= 0)
-        return fail(ATTN_ERR_INVALID_ARG, "sizes must be positive (B=%d H=%d Hkv=%d N_max=%d d=%d)",
-                    B, H, Hkv, N_max, d);
-    if (H % Hkv != 0)
-        return fail(ATTN_ERR_INVALID_ARG, "H=%d is not a multiple of Hkv=%d", H, Hkv);
-    if (!valid_scale(scale))
-        return fail(ATTN_ERR_INVALID_ARG, "scale must be finite and > 0");
-    if (o_dtype != ATTN_OUT_BF16 && o_dtype != ATTN_OUT_FP32)
-        return fail(ATTN_ERR_INVALID_ARG, "unknown output dtype %d", o_dtype);
-    if (split_tokens <= 0 || split_tokens % 64 != 0)
-        return fail(ATTN_ERR_INVALID_ARG, "split_tokens=%d must be a positive multiple of 64",
-                    split_tokens);
-    if (mode != ATTN_MODE_EXACT_BF16)
-        return fail(mode == ATTN_MODE_SAGE_QK_I8_BLK64_PV_FP8_E4M3 ? ATTN_ERR_UNSUPPORTED
-                                                                   : ATTN_ERR_INVALID_ARG,
-                    "decode supports only the exact bf16 mode (mode=%d)", mode);
-    if (d != 64 && d != 128)
-        return fail(ATTN_ERR_UNSUPPORTED, "head dim d=%d (supported: 64, 128)", d);
-    const int G = H / Hkv;
-    if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
-        return fail(ATTN_ERR_UNSUPPORTED,
-                    "query heads per kv head %d (supported: 1, 2, 4, 8, 16)", G);
-    const long long splits = ((long long)N_max + split_tokens - 1) / split_tokens;
-    // one wave per possible chunk (an int index) and one merge workgroup per (b, h)
-    if ((long long)B * Hkv * splits > 0x7fffff00LL || (long long)B * H > 0x7fffffffLL)
-        return fail(ATTN_ERR_UNSUPPORTED, "problem too large for the grid mapping");
-    const size_t need = attn_decode_workspace_size(B, H, N_max, d, split_tokens);
-    if (!workspace || workspace_bytes < need)
-        return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
-                    workspace ? workspace_bytes : (size_t)0);
-
-    attn::DecodeArgs a{};
-    a.q = q;
-    a.k = k_cache;
-    a.v = v_cache;
-    a.seqlens = seqlens;
-    a.o = o;
-    a.lse = lse;
-    a.B = B;
-    a.H = H;
-    a.Hkv = Hkv;
-    a.N_max = N_max;
-    a.d = d;
-    a.scale = scale;
-    a.out_fp32 = o_dtype == ATTN_OUT_FP32;
-    a.split_tokens = split_tokens;
-    a.max_splits = (int)splits;
-    a.part_o = (float *)workspace;
-    a.part_lse = (float *)((char *)workspace +
-                           align_up(sizeof(float) * (size_t)B * H * splits * d, 256));
+    attn::DecodeArgs a;
+    const attn_status st = decode_common(q, k_cache, v_cache, seqlens, o, lse, B, H, Hkv, N_max,
+                                         d, scale, mode, o_dtype, split_tokens, workspace,
+                                         workspace_bytes, a);
+    if (st != ATTN_OK)
+        return st;
     return from_hip(attn::launch_decode(a, (hipStream_t)stream), "decode launch");
+}
+
+attn_status attn_decode_paged(const void *q, const void *k_pages, const void *v_pages,
+                              const int32_t *block_table, const int32_t *seqlens, void *o,
+                              float *lse, int B, int H, int Hkv, int num_pages, int page_size,
+                              int max_pages, int d, float scale, int mode, int o_dtype,
+                              int split_tokens, void *workspace, size_t workspace_bytes,
+                              void *stream)
+{
+    if (!block_table)
+        return fail(ATTN_ERR_INVALID_ARG, "block_table must be a non-null device pointer");
+    if (num_pages <= 0 || max_pages <= 0)
+        return fail(ATTN_ERR_INVALID_ARG, "num_pages=%d and max_pages=%d must be positive",
+                    num_pages, max_pages);
+    if (page_size <= 0 || (page_size & (page_size - 1)) != 0)
+        return fail(ATTN_ERR_INVALID_ARG, "page_size=%d is not a power of two", page_size);
+    if (page_size < 16 || (split_tokens > 0 && (long long)page_size * 64 < split_tokens))
+        return fail(ATTN_ERR_UNSUPPORTED,
+                    "page_size=%d (supported: >= 16 and >= split_tokens/64 = %d)", page_size,
+                    split_tokens / 64);
+    const long long n_max = (long long)max_pages * page_size;
+    if (n_max > 0x7fffffffLL)
+        return fail(ATTN_ERR_UNSUPPORTED, "max_pages * page_size = %lld exceeds 2^31 - 1", n_max);
+    attn::DecodeArgs a;
+    const attn_status st = decode_common(q, k_pages, v_pages, seqlens, o, lse, B, H, Hkv,
+                                         (int)n_max, d, scale, mode, o_dtype, split_tokens,
+                                         workspace, workspace_bytes, a);
+    if (st != ATTN_OK)
+        return st;
+    a.block_table = block_table;
+    a.page_shift = __builtin_ctz((unsigned)page_size);
+    a.max_pages = max_pages;
+    a.num_pages = num_pages;
+    return from_hip(attn::launch_decode(a, (hipStream_t)stream), "paged decode launch");
 }
 
 attn_status attn_profiler_enable(int enable)

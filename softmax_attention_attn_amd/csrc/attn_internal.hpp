@@ -30,6 +30,12 @@ struct DecodeArgs {
     int max_splits;   // ceil(N_max / split_tokens)
     float *part_o;    // [B, H, max_splits, d]
     float *part_lse;  // [B, H, max_splits]
+    // Paged caches (block_table non-null): k and v are [num_pages, Hkv,
+    // page_size, d] with page_size = 1 << page_shift, and key position n of
+    // sequence b lives in page block_table[b * max_pages + (n >> page_shift)].
+    // N_max = max_pages * page_size.
+    const int32_t *block_table = nullptr;
+    int page_shift = 0, max_pages = 0, num_pages = 0;
 };
 
 struct SageArgs {
@@ -41,7 +47,7 @@ struct SageArgs {
 // Kernel launchers (defined in the .hip files).  They assume validated
 // arguments and return the launch status.
 hipError_t launch_prefill_exact(const PrefillArgs &a, hipStream_t s);
-hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);  // contiguous or paged caches
 hipError_t launch_sage(const SageArgs &a, hipStream_t s);
 size_t sage_workspace_bytes(int B, int H, int Hkv, int N, int d);
 

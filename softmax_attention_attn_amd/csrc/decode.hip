@@ -8,7 +8,13 @@
 // partial output O_s (normalised by the chunk's own row sum) and its log2
 // LSE.  Chunks starting at or beyond the sequence length do no work.
 //
-// decode_merge_kernel: one workgroup per (sequence, query head) combines the
+// The caches are either contiguous per sequence ([B, Hkv, N_max, d]) or a
+// pool of fixed-size pages named by a per-sequence page table (the paged KV
+// layout of serving caches, "flashattention-kernels" page §3).  A paged
+// wave reads its chunk's page numbers once, one per lane, and looks up the
+// page of each row it loads with a lane shuffle; everything else is shared.
+//
+// decode_merge_kernel: one wave per (sequence, query head) combines the
 // chunk partials with log-sum-exp weights into O and the natural-log LSE.
 //
 // The path is HBM bound (a few FLOPs per byte): the split kernel keeps two
@@ -95,7 +101,7 @@ __device__ __forceinline__ int dvswz(int r)
     return (2 * (r & 7)) & (DCfg<D>::kChunks - 1);
 }
 
-template <int D, int G>
+template <int D, int G, bool PAGED>
 __global__ __launch_bounds__(64 * kWavesPerWG) void decode_split_kernel(DecodeArgs a)
 {
     __shared__ __attribute__((aligned(1024)))
@@ -109,10 +115,34 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void decode_split_kernel(DecodeAr
     const int n = min(S, L - c0);
     const int nsub = (n + kSub - 1) / kSub;
     const int col = lane & 15, G4 = lane >> 4;  // MFMA column (head) and lane group
-    const size_t cache_off = ((size_t)(b * a.Hkv + kvh) * a.N_max + c0) * D;
-    const uint16_t *kb = (const uint16_t *)a.k + cache_off;
-    const uint16_t *vb = (const uint16_t *)a.v + cache_off;
     unsigned char *vst = &vlds[wave][0][0];
+    // Element offset of key row r (0 <= r < n) of the chunk in the K and V
+    // caches.  Paged: lane l holds the page of the chunk's l-th page slot
+    // (a chunk spans at most 64 pages; out-of-range page numbers are clamped
+    // into the pool), and a row's page is read from its lane.
+    size_t cache_off = 0;
+    int first_page = 0, my_page = 0;
+    if constexpr (PAGED) {
+        first_page = c0 >> a.page_shift;
+        const int npc = ((c0 + n - 1) >> a.page_shift) - first_page + 1;
+        if (lane < npc) {
+            const int pg = a.block_table[(size_t)b * a.max_pages + first_page + lane];
+            my_page = pg < 0 ? 0 : (pg >= a.num_pages ? a.num_pages - 1 : pg);
+        }
+    } else {
+        cache_off = ((size_t)(b * a.Hkv + kvh) * a.N_max + c0) * D;
+    }
+    auto row_off = [&](int r) -> size_t {
+        if constexpr (PAGED) {
+            const int pos = c0 + r;
+            const int pg = __shfl(my_page, (pos >> a.page_shift) - first_page, 64);
+            const int in_page = pos & ((1 << a.page_shift) - 1);
+            return ((((size_t)pg * a.Hkv + kvh) << a.page_shift) + in_page) * D;
+        } else {
+            return cache_off + (size_t)r * D;
+        }
+    };
+    const uint16_t *kc = (const uint16_t *)a.k, *vc = (const uint16_t *)a.v;
 
     // q^T fragments (B operand of QK): lane holds q[head col][32*ks + 8*G4 .. +7]
     bf16x8 qf[D / 32];
@@ -127,10 +157,10 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void decode_split_kernel(DecodeAr
     auto load_k = [&](int i, u32x4 (&kr)[2][D / 32]) {
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
-            const int row = min(i * kSub + 16 * blk + col, n - 1);
+            const uint16_t *krow = kc + row_off(min(i * kSub + 16 * blk + col, n - 1));
 #pragma unroll
             for (int ks = 0; ks < D / 32; ++ks)
-                kr[blk][ks] = ld16(kb + (size_t)row * D + 32 * ks + 8 * G4);
+                kr[blk][ks] = ld16(krow + 32 * ks + 8 * G4);
         }
     };
     // V sub-tile into LDS stage i % 3 (row-major rows of D bf16, swizzled)
@@ -142,8 +172,7 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void decode_split_kernel(DecodeAr
             const int p = piece * 64 + lane;
             const int r = p / C;
             const int c = (p % C) ^ dvswz<D>(r);
-            const int row = min(i * kSub + r, n - 1);
-            dma16(vb + (size_t)row * D + c * 8, dst + piece * 1024);
+            dma16(vc + row_off(min(i * kSub + r, n - 1)) + c * 8, dst + piece * 1024);
         }
     };
 
@@ -273,29 +302,87 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void decode_split_kernel(DecodeAr
     }
 }
 
+// One wave per (sequence, query head): lanes take the chunk LSEs 64 at a
+// time for the max and the weight sum, then each lane accumulates D/64
+// features over the chunks, sixteen chunk rows in flight.
+constexpr int kMergeWaves = 4;
+
 template <int D, bool OUT_F32>
-__global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a)
+__global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(DecodeArgs a)
 {
-    const int bh = blockIdx.x, b = bh / a.H, dd = threadIdx.x;
+    constexpr int F = D / 64;  // features per lane
+    const int lane = threadIdx.x & 63;
+    const int bh = (int)blockIdx.x * kMergeWaves + (int)(threadIdx.x >> 6);
+    if (bh >= a.B * a.H)
+        return;
+    const int b = bh / a.H;
     const int L = clamp_len(a.seqlens, b, a.N_max);
     const int ns = (L + a.split_tokens - 1) / a.split_tokens;
     const float *pl = a.part_lse + (size_t)bh * a.max_splits;
-    const float *po = a.part_o + (size_t)bh * a.max_splits * D;
+    const float *po = a.part_o + (size_t)bh * a.max_splits * D + F * lane;
     float M = -INFINITY;
-    for (int s = 0; s < ns; ++s)
+    for (int s = lane; s < ns; s += 64)
         M = fmaxf(M, pl[s]);
-    float wsum = 0.f, acc = 0.f;
-    for (int s = 0; s < ns; ++s) {
-        const float w = fast_exp2(pl[s] - M);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        M = fmaxf(M, __shfl_xor(M, off, 64));
+    float wsum = 0.f;
+    float acc[F] = {};
+    for (int s0 = 0; s0 < ns; s0 += 64) {
+        const float w = s0 + lane < ns ? fast_exp2(pl[s0 + lane] - M) : 0.f;
         wsum += w;
-        acc = fmaf(w, po[(size_t)s * D + dd], acc);
+        const int n = min(64, ns - s0);
+        int j = 0;
+        for (; j + 16 <= n; j += 16) {
+            float x[16][F];
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+#pragma unroll
+                for (int f = 0; f < F; ++f)
+                    x[u][f] = po[(size_t)(s0 + j + u) * D + f];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const float wu = __shfl(w, j + u, 64);
+#pragma unroll
+                for (int f = 0; f < F; ++f)
+                    acc[f] = fmaf(wu, x[u][f], acc[f]);
+            }
+        }
+        for (; j + 4 <= n; j += 4) {
+            float x[4][F];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int f = 0; f < F; ++f)
+                    x[u][f] = po[(size_t)(s0 + j + u) * D + f];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float wu = __shfl(w, j + u, 64);
+#pragma unroll
+                for (int f = 0; f < F; ++f)
+                    acc[f] = fmaf(wu, x[u][f], acc[f]);
+            }
+        }
+        for (; j < n; ++j) {
+            const float wu = __shfl(w, j, 64);
+#pragma unroll
+            for (int f = 0; f < F; ++f)
+                acc[f] = fmaf(wu, po[(size_t)(s0 + j) * D + f], acc[f]);
+        }
     }
-    const float out = acc / wsum;
-    if constexpr (OUT_F32)
-        ((float *)a.o)[(size_t)bh * D + dd] = out;
-    else
-        ((__bf16 *)a.o)[(size_t)bh * D + dd] = (__bf16)out;
-    if (a.lse && dd == 0)
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        wsum += __shfl_xor(wsum, off, 64);
+    const float inv = 1.f / wsum;
+#pragma unroll
+    for (int f = 0; f < F; ++f) {
+        const float out = acc[f] * inv;
+        if constexpr (OUT_F32)
+            ((float *)a.o)[(size_t)bh * D + F * lane + f] = out;
+        else
+            ((__bf16 *)a.o)[(size_t)bh * D + F * lane + f] = (__bf16)out;
+    }
+    if (a.lse && lane == 0)
         a.lse[bh] = (M + log2f(wsum)) * kLn2;
 }
 
@@ -305,8 +392,13 @@ hipError_t launch_split(const DecodeArgs &a, hipStream_t s)
     // one wave per possible chunk; waves past the last non-empty chunk exit
     const long long items = (long long)a.B * a.Hkv * a.max_splits;
     dim3 grid((unsigned)((items + kWavesPerWG - 1) / kWavesPerWG));
-    ProfScope ps("decode_split", s);
-    hipLaunchKernelGGL((decode_split_kernel<D, G>), grid, dim3(64 * kWavesPerWG), 0, s, a);
+    ProfScope ps(a.block_table ? "decode_split_paged" : "decode_split", s);
+    if (a.block_table)
+        hipLaunchKernelGGL((decode_split_kernel<D, G, true>), grid, dim3(64 * kWavesPerWG), 0, s,
+                           a);
+    else
+        hipLaunchKernelGGL((decode_split_kernel<D, G, false>), grid, dim3(64 * kWavesPerWG), 0, s,
+                           a);
     return hipGetLastError();
 }
 
@@ -324,10 +416,11 @@ hipError_t launch_d(const DecodeArgs &a, hipStream_t s)
     if (e != hipSuccess)
         return e;
     ProfScope ps("decode_merge", s);
+    const dim3 grid((unsigned)((a.B * a.H + kMergeWaves - 1) / kMergeWaves));
     if (a.out_fp32)
-        hipLaunchKernelGGL((decode_merge_kernel<D, true>), dim3(a.B * a.H), dim3(D), 0, s, a);
+        hipLaunchKernelGGL((decode_merge_kernel<D, true>), grid, dim3(64 * kMergeWaves), 0, s, a);
     else
-        hipLaunchKernelGGL((decode_merge_kernel<D, false>), dim3(a.B * a.H), dim3(D), 0, s, a);
+        hipLaunchKernelGGL((decode_merge_kernel<D, false>), grid, dim3(64 * kMergeWaves), 0, s, a);
     return hipGetLastError();
 }
 

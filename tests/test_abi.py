@@ -83,6 +83,35 @@ def test_decode_validation(A, kw, status):
     assert _dec(A, **kw) == status
 
 
+def _decp(A, **kw):
+    args = dict(q=P, k_pages=P, v_pages=P, block_table=P, seqlens=P, o=P, lse=None, B=2, H=8,
+                Hkv=2, num_pages=40, page_size=16, max_pages=64, d=128, scale=0.1, mode=0,
+                o_dtype=0, split_tokens=512, workspace=P, workspace_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return A.attn_decode_paged(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(block_table=None), -1), (dict(k_pages=None), -1), (dict(seqlens=None), -1),
+    (dict(num_pages=0), -1), (dict(max_pages=-1), -1),
+    (dict(page_size=0), -1), (dict(page_size=24), -1), (dict(page_size=-16), -1),
+    (dict(page_size=8), -2),                                   # below 16
+    (dict(page_size=16, split_tokens=2048), -2),               # a chunk would span 128 pages
+    (dict(page_size=1 << 20, max_pages=4096), -2),             # 2^32 positions
+    (dict(H=7), -1), (dict(split_tokens=100), -1), (dict(mode=1), -2), (dict(d=80), -2),
+    (dict(workspace=None), -3), (dict(workspace_bytes=1000), -3),
+])
+def test_decode_paged_validation(A, kw, status):
+    assert _decp(A, **kw) == status
+    assert A.attn_last_error() != ""
+
+
+def test_decode_paged_workspace_is_decode_workspace(A):
+    # the paged call needs exactly the contiguous call's workspace for N_max = max_pages * page_size
+    need = A.attn_decode_workspace_size(2, 8, 64 * 16, 128, 512)
+    assert _decp(A, workspace_bytes=need - 1) == -3
+
+
 def test_workspace_sizes(A):
     # partial O fp32 [B,H,splits,d] + partial lse fp32 [B,H,splits], each 256-B aligned
     B, H, N, d, s = 64, 32, 32768, 128, 512

@@ -247,6 +247,38 @@ def test_decode_kv_len_matches_brute(oracle_lib):
     np.testing.assert_allclose(lse, lseb, atol=1e-12)
 
 
+def test_gather_pages_worked_example():
+    # pool of 3 pages of 2 rows (1 kv head, d = 1); page p row j holds 10p + j.
+    # Sequence 0 (3 keys) uses pages 2 then 0, sequence 1 (4 keys) pages 1 then 2:
+    # its positions 0..3 are page 1 rows 0, 1 and page 2 rows 0, 1.
+    pages = np.array([[[[0], [1]]], [[[10], [11]]], [[[20], [21]]]], dtype=np.int64)
+    table = np.array([[2, 0], [1, 2]])
+    out = oracle.gather_pages(pages, table, np.array([3, 4]), 2)
+    assert out.shape == (2, 1, 4, 1)
+    assert out[:, 0, :, 0].tolist() == [[20, 21, 0, 0], [10, 11, 20, 21]]
+
+
+@pytest.mark.parametrize("page_size", [1, 4, 16])
+def test_gather_pages_inverts_a_scatter(page_size):
+    # scatter contiguous caches into a shuffled pool one whole page at a time
+    # (slices, not positions), then gather them back
+    rng = np.random.default_rng(page_size)
+    B, Hkv, d, max_pages = 3, 2, 5, 6
+    L = np.array([1, page_size * max_pages, page_size * 2 + 1])
+    cont = rng.standard_normal((B, Hkv, max_pages * page_size, d))
+    used = [(b, j) for b in range(B) for j in range((L[b] + page_size - 1) // page_size)]
+    perm = rng.permutation(len(used) + 3)  # 3 spare pages stay NaN
+    pool = np.full((len(used) + 3, Hkv, page_size, d), np.nan)
+    table = np.full((B, max_pages), -1)
+    for (b, j), p in zip(used, perm):
+        table[b, j] = p
+        pool[p] = cont[b, :, j * page_size:(j + 1) * page_size, :]
+    out = oracle.gather_pages(pool, table, L, page_size)
+    for b in range(B):
+        np.testing.assert_array_equal(out[b, :, :L[b]], cont[b, :, :L[b]])
+        assert (out[b, :, L[b]:] == 0).all()
+
+
 @pytest.mark.parametrize("cuts", [(0, 40), (0, 1, 40), (0, 8, 16, 24, 32, 40), (0, 13, 29, 40)])
 def test_split_and_merge_equals_unsplit(oracle_lib, cuts):
     g = torch.Generator().manual_seed(14)

@@ -17,7 +17,10 @@ Recipe (all draws from one ``torch.Generator`` on the CPU seeded with
 * decode draws the per-sequence lengths (uniform integers in [len_lo, len_hi]),
   then q [B, H, d], then the valid K rows batch by batch ([Hkv, L_b, d] each),
   then the valid V rows the same way; cache positions at or beyond L_b hold
-  bf16 NaN so that any over-read shows up in the output.
+  bf16 NaN so that any over-read shows up in the output;
+* paged decode takes those caches and spreads their pages over a pool in a
+  random order (its own generator, seeded separately); unused pool pages and
+  the rows of a last page past L_b hold NaN.
 """
 from __future__ import annotations
 
@@ -123,6 +126,44 @@ def make_decode(B, H, Hkv, N_max, d, *, len_lo, len_hi, seed=0):
             c[b, :, L:] = nan
         caches.append(c)
     return q, caches[0], caches[1], seqlens.to(torch.int32)
+
+
+def make_page_table(seqlens, page_size: int, *, seed=0, spare_pages=0, max_pages=None):
+    """A paged-cache page table: every page of every sequence gets a distinct
+    pool page, in a random order (``torch.randperm`` on a generator seeded with
+    ``seed``), and ``spare_pages`` pool pages stay unused.  Returns
+    (table int32 [B, max_pages] with -1 past each sequence's pages, num_pages).
+    """
+    seqlens = [int(x) for x in seqlens]
+    need = [(L + page_size - 1) // page_size for L in seqlens]
+    if max_pages is None:
+        max_pages = max(need)
+    total = sum(need)
+    num_pages = total + spare_pages
+    perm = torch.randperm(num_pages, generator=_gen(seed))[:total].to(torch.int32)
+    table = torch.full((len(seqlens), max_pages), -1, dtype=torch.int32)
+    i = 0
+    for b, n in enumerate(need):
+        table[b, :n] = perm[i:i + n]
+        i += n
+    return table, num_pages
+
+
+def paginate(cache, table, num_pages: int, page_size: int):
+    """Copy contiguous caches [B, Hkv, N_max, d] into a page pool
+    [num_pages, Hkv, page_size, d] laid out by ``table`` (unused pool pages
+    hold NaN).  Works on CPU or GPU tensors; N_max must be a multiple of
+    page_size and table must have N_max / page_size columns."""
+    B, Hkv, N_max, d = cache.shape
+    if N_max % page_size or table.shape != (B, N_max // page_size):
+        raise ValueError("cache length, page size and table do not agree")
+    pool = torch.full((num_pages, Hkv, page_size, d), float("nan"), dtype=cache.dtype,
+                      device=cache.device)
+    pages = cache.view(B, Hkv, N_max // page_size, page_size, d).transpose(1, 2)
+    t = table.to(cache.device, torch.int64)
+    used = t >= 0
+    pool[t[used]] = pages[used]
+    return pool
 
 
 def make(w: Workload):
