@@ -9,11 +9,12 @@ the same timed region for the roofline figure.
 
 The same JSON line also carries the split-KV decode workload (HBM bound,
 GB/s; contiguous caches, and the same caches spread over a pool of 16-row
-pages) and the quantised prefill workload, each with its own roofline object,
+pages), a packed batch of variable-length sequences, and the quantised
+prefill workload, each with its own roofline object,
 and the fp64 CPU oracle timed on a bounded sample of the headline workload.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                  [--only prefill|decode|sage] [--calibrate-copy]
+                  [--only prefill|varlen|decode|sage] [--calibrate-copy]
 """
 from __future__ import annotations
 
@@ -111,6 +112,34 @@ def bench_prefill(args, stream):
         "inputs": (inp["q"], inp["k"], inp["v"]),
     }
     return res
+
+
+def bench_varlen(args, stream):
+    import softmax_attention_attn_amd as A
+    w = workloads.WORKLOADS["varlen_prefill"]
+    inp = workloads.make(w)
+    q, k, v = inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda()
+    cu = inp["cu_seqlens"].cuda()
+    o = torch.empty_like(q)
+    lse = torch.empty((w.H, q.shape[0]), dtype=torch.float32, device="cuda")
+
+    def step():
+        A.fwd_varlen(q, k, v, cu, w.N, causal=w.causal, o=o, lse=lse, stream=stream)
+
+    ms, per_kernel = time_calls(step, args.steps, args.warmup, stream)
+    flops = w.flops(inp["seqlens"].numpy())
+    kms = per_kernel["prefill_exact_varlen"][0]
+    achieved = flops / (kms * 1e-3) / 1e12
+    return {
+        "workload": w.name, "value": flops / (ms * 1e-3) / 1e12, "unit": "TFLOP/s",
+        "ms_per_step": ms, "seqlens": inp["seqlens"].tolist(), "H": w.H, "Hkv": w.Hkv,
+        "d": w.d, "causal": w.causal,
+        "roofline": {"bound": "mfma", "kernel": "prefill_exact_varlen", "achieved": achieved,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "kernel_ms": kms,
+                     "traffic": measured_traffic("prefill_exact_varlen",
+                                                 ["prefill_exact.hip", "cdna4.hpp"])},
+    }
 
 
 def bench_decode(args, stream):
@@ -239,7 +268,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "sage"], default=None)
+    ap.add_argument("--only", choices=["prefill", "varlen", "decode", "sage"], default=None)
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -259,6 +288,11 @@ def main():
         log("prefill: llm_prefill")
         pre = bench_prefill(args, stream)
         log("prefill %.3f ms/step, %.1f TFLOP/s" % (pre["ms_per_step"], pre["value"]))
+    if args.only in (None, "varlen"):
+        log("varlen: varlen_prefill")
+        vl = bench_varlen(args, stream)
+        log("varlen %.3f ms/step, %.1f TFLOP/s" % (vl["ms_per_step"], vl["value"]))
+        out["varlen"] = vl
     if args.only in (None, "sage"):
         log("sage: sage_prefill")
         sg = bench_sage(args, stream)

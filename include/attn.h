@@ -98,6 +98,38 @@ attn_status attn_fwd(const void *q, const void *k, const void *v, void *o, float
 size_t attn_fwd_workspace_size(int B, int H, int Hkv, int N, int d, int mode);
 
 /*
+ * Attention forward over a packed batch of variable-length sequences (the
+ * exact mode only): each sequence attends to its own tokens, with the same
+ * computation as attn_fwd applied sequence by sequence.  Packing without
+ * padding is the shape/packing lever the "flashattention-kernels" page
+ * (recommendation table) puts before any specialised kernel, and the
+ * library interface of its §3 switches between prefill and decode over such
+ * batches.
+ *   q, o       device [total, H, d] (token-major: the H heads of a token are
+ *              adjacent); o has dtype o_dtype.
+ *   k, v       device bf16 [total, Hkv, d].
+ *   lse        device fp32 [H, total] or NULL.
+ *   cu_seqlens device int32 [B + 1]: sequence b holds tokens
+ *              [cu_seqlens[b], cu_seqlens[b+1]); cu_seqlens[0] = 0,
+ *              non-decreasing, cu_seqlens[B] = total.  Offsets outside
+ *              [0, total] are clamped into it, and a sequence longer than
+ *              max_seqlen is cut to its first max_seqlen queries and keys
+ *              (the result is then unspecified, but no access leaves the
+ *              tensors).  Empty sequences are allowed.
+ *   total      number of packed tokens (>= 1).
+ *   max_seqlen an upper bound of the sequence lengths (>= 1); it sizes the grid.
+ *   causal     0 = no mask, else the top-left causal mask inside each sequence.
+ *   mode       only ATTN_MODE_EXACT_BF16 (the quantised mode returns
+ *              ATTN_ERR_UNSUPPORTED).
+ * No workspace.  Errors as for attn_fwd, plus ATTN_ERR_INVALID_ARG for a null
+ * cu_seqlens or non-positive total or max_seqlen.
+ */
+attn_status attn_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *lse,
+                            const int32_t *cu_seqlens, int B, int H, int Hkv, int total,
+                            int max_seqlen, int d, int causal, float scale, int mode,
+                            int o_dtype, void *stream);
+
+/*
  * One-token decode against per-sequence KV caches with split-KV
  * (Flash-Decoding, "flashattention-kernels" page §3): the valid keys
  * [0, seqlens[b]) of each sequence are cut into chunks of split_tokens keys,

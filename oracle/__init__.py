@@ -16,6 +16,9 @@ What each routine follows:
   softmax preserve exact attention; "cuda-kernel-pretrain" page, §2).  Also the
   decode case (one query row, ``kv_len`` valid keys) and partial attention over
   a key range (Flash-Decoding's chunks, "flashattention-kernels" page, §3).
+* ``attn_varlen`` -- the same over a packed batch of variable-length
+  sequences, each attending only to its own tokens (packing without padding,
+  "flashattention-kernels" page, recommendation table and §3).
 * ``lse_merge`` -- the reduction that combines per-chunk partial results
   (same page, §3; the pages give no formula, the log-sum-exp weighting used
   here is the unique one that reproduces the unsplit softmax).
@@ -159,6 +162,32 @@ def attn_rows(q, k, v, *, causal: bool, scale: float, rows=None, kv_len=None,
         o = o.reshape(B, H, Nq, d)
         lse = lse.reshape(B, H, Nq)
     return o, lse, err
+
+
+def attn_varlen(q, k, v, cu_seqlens, *, causal: bool, scale: float,
+                threads: int | None = None):
+    """Exact attention over a packed batch: each sequence attends only to its
+    own tokens (sequence b holds tokens [cu_seqlens[b], cu_seqlens[b+1])).
+
+    q [total,H,d], k/v [total,Hkv,d] (uint16 bf16 bits), token-major.
+    Returns (o [total,H,d], lse [H,total]) in float64, computed sequence by
+    sequence with ``attn_rows``; empty sequences contribute nothing.
+    """
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    total, H, d = q.shape
+    cu = [int(x) for x in np.asarray(cu_seqlens)]
+    o = np.zeros((total, H, d), dtype=np.float64)
+    lse = np.zeros((H, total), dtype=np.float64)
+    for t0, t1 in zip(cu[:-1], cu[1:]):
+        if t1 <= t0:
+            continue
+        qs = np.ascontiguousarray(q[t0:t1].transpose(1, 0, 2))[None]
+        ks = np.ascontiguousarray(k[t0:t1].transpose(1, 0, 2))[None]
+        vs = np.ascontiguousarray(v[t0:t1].transpose(1, 0, 2))[None]
+        os_, ls, _ = attn_rows(qs, ks, vs, causal=causal, scale=scale, threads=threads)
+        o[t0:t1] = os_[0].transpose(1, 0, 2)
+        lse[:, t0:t1] = ls[0]
+    return o, lse
 
 
 def lse_merge(o_parts, lse_parts):

@@ -8,8 +8,8 @@ the library's HIP kernels; there is no fallback.  Importing this package
 fails loudly when the library has not been built.
 
 The functions carry the C names (``attn_fwd``, ``attn_decode``, ...); the
-convenience wrappers ``fwd``, ``decode`` and ``decode_paged`` allocate what the
-caller omits.
+convenience wrappers ``fwd``, ``fwd_varlen``, ``decode`` and ``decode_paged``
+allocate what the caller omits.
 """
 from __future__ import annotations
 
@@ -35,9 +35,9 @@ ATTN_OUT_FP32 = 1
 
 MODES = {"exact": ATTN_MODE_EXACT_BF16, "sage": ATTN_MODE_SAGE_QK_I8_BLK64_PV_FP8_E4M3}
 
-EXPORTS = ("attn_fwd", "attn_fwd_workspace_size", "attn_decode", "attn_decode_workspace_size",
-           "attn_decode_paged", "attn_status_string", "attn_last_error",
-           "attn_profiler_enable", "attn_profiler_read")
+EXPORTS = ("attn_fwd", "attn_fwd_workspace_size", "attn_fwd_varlen", "attn_decode",
+           "attn_decode_workspace_size", "attn_decode_paged", "attn_status_string",
+           "attn_last_error", "attn_profiler_enable", "attn_profiler_read")
 
 
 class AttnError(RuntimeError):
@@ -56,6 +56,8 @@ def _load():
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, sz, vp]
     lib.attn_fwd_workspace_size.restype = sz
     lib.attn_fwd_workspace_size.argtypes = [i, i, i, i, i, i]
+    lib.attn_fwd_varlen.restype = i
+    lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, vp]
     lib.attn_decode.restype = i
     lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, sz, vp]
     lib.attn_decode_workspace_size.restype = sz
@@ -120,6 +122,12 @@ def attn_fwd(q, k, v, o, lse, B, H, Hkv, N, d, causal, scale, mode, o_dtype, wor
     """Direct call of the C function with raw pointers (ints or None)."""
     return int(_lib.attn_fwd(q, k, v, o, lse, B, H, Hkv, N, d, causal, scale, mode, o_dtype,
                              workspace, workspace_bytes, stream))
+
+
+def attn_fwd_varlen(q, k, v, o, lse, cu_seqlens, B, H, Hkv, total, max_seqlen, d, causal, scale,
+                    mode, o_dtype, stream) -> int:
+    return int(_lib.attn_fwd_varlen(q, k, v, o, lse, cu_seqlens, B, H, Hkv, total, max_seqlen, d,
+                                    causal, scale, mode, o_dtype, stream))
 
 
 def attn_decode(q, k_cache, v_cache, seqlens, o, lse, B, H, Hkv, N_max, d, scale, mode,
@@ -200,6 +208,38 @@ def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, mode: str 
     st = _lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, N, d,
                        int(bool(causal)), float(scale), m, o_code, _ptr(workspace),
                        workspace.numel() if workspace is not None else 0, _stream(stream))
+    _check(st)
+    return o, lse
+
+
+def fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, *, causal: bool = False,
+               scale: float | None = None, out_dtype=torch.bfloat16, o=None, lse=None,
+               with_lse: bool = True, stream=None):
+    """Attention over a packed batch of variable-length sequences (exact mode).
+
+    q [total,H,d], k/v [total,Hkv,d] bf16; cu_seqlens int32 [B+1] on the GPU;
+    ``max_seqlen`` bounds the sequence lengths.  Returns (o [total,H,d] of
+    ``out_dtype``, lse fp32 [H,total] or None).
+    """
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k, "k", torch.bfloat16, 3)
+    _need(v, "v", torch.bfloat16, 3)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    total, H, d = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (total, Hkv, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k/v shape %s does not match q %s" % (tuple(k.shape), tuple(q.shape)))
+    B = cu_seqlens.shape[0] - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o_code = {torch.bfloat16: ATTN_OUT_BF16, torch.float32: ATTN_OUT_FP32}[out_dtype]
+    if o is None:
+        o = torch.empty((total, H, d), dtype=out_dtype, device=q.device)
+    if lse is None and with_lse:
+        lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
+    st = _lib.attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens),
+                              B, H, Hkv, total, int(max_seqlen), d, int(bool(causal)),
+                              float(scale), ATTN_MODE_EXACT_BF16, o_code, _stream(stream))
     _check(st)
     return o, lse
 

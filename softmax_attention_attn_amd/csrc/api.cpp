@@ -196,6 +196,9 @@ attn_status attn_fwd(const void *q, const void *k, const void *v, void *o, float
         return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                     workspace ? workspace_bytes : (size_t)0);
 
+    const long long nqt = ((long long)N + 255) / 256;
+    if ((long long)B * H * nqt > 0x7fffffffLL)
+        return fail(ATTN_ERR_UNSUPPORTED, "problem too large for the grid mapping");
     attn::PrefillArgs a{q, k, v, o, lse, B, H, Hkv, N, d, causal != 0, scale,
                         o_dtype == ATTN_OUT_FP32};
     hipStream_t s = (hipStream_t)stream;
@@ -203,6 +206,44 @@ attn_status attn_fwd(const void *q, const void *k, const void *v, void *o, float
         return from_hip(attn::launch_prefill_exact(a, s), "prefill launch");
     attn::SageArgs sa{a, workspace, workspace_bytes};
     return from_hip(attn::launch_sage(sa, s), "sage launch");
+}
+
+attn_status attn_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *lse,
+                            const int32_t *cu_seqlens, int B, int H, int Hkv, int total,
+                            int max_seqlen, int d, int causal, float scale, int mode,
+                            int o_dtype, void *stream)
+{
+    if (!q || !k || !v || !o || !cu_seqlens)
+        return fail(ATTN_ERR_INVALID_ARG,
+                    "q, k, v, o and cu_seqlens must be non-null device pointers");
+    if (B <= 0 || H <= 0 || Hkv <= 0 || d <= 0 || total <= 0 || max_seqlen <= 0)
+        return fail(ATTN_ERR_INVALID_ARG,
+                    "sizes must be positive (B=%d H=%d Hkv=%d d=%d total=%d max_seqlen=%d)", B,
+                    H, Hkv, d, total, max_seqlen);
+    if (H % Hkv != 0)
+        return fail(ATTN_ERR_INVALID_ARG, "H=%d is not a multiple of Hkv=%d", H, Hkv);
+    if (!valid_scale(scale))
+        return fail(ATTN_ERR_INVALID_ARG, "scale must be finite and > 0");
+    if (o_dtype != ATTN_OUT_BF16 && o_dtype != ATTN_OUT_FP32)
+        return fail(ATTN_ERR_INVALID_ARG, "unknown output dtype %d", o_dtype);
+    if (mode != ATTN_MODE_EXACT_BF16)
+        return fail(mode == ATTN_MODE_SAGE_QK_I8_BLK64_PV_FP8_E4M3 ? ATTN_ERR_UNSUPPORTED
+                                                                   : ATTN_ERR_INVALID_ARG,
+                    "the packed variable-length call supports only the exact mode (mode=%d)",
+                    mode);
+    if (d != 64 && d != 128)
+        return fail(ATTN_ERR_UNSUPPORTED, "head dim d=%d (supported: 64, 128)", d);
+    const long long nqt = ((long long)max_seqlen + 255) / 256;
+    // grid of B*H*(query tiles) workgroups; 64 key rows of one tile must stay
+    // within the 32-bit offsets of a buffer resource
+    if ((long long)B * H * nqt > 0x7fffffffLL || (long long)H * d > (1 << 20) ||
+        max_seqlen > (1 << 24))
+        return fail(ATTN_ERR_UNSUPPORTED, "problem too large for the grid mapping");
+    attn::PrefillArgs a{q, k, v, o, lse, B, H, Hkv, max_seqlen, d, causal != 0, scale,
+                        o_dtype == ATTN_OUT_FP32};
+    a.cu_seqlens = cu_seqlens;
+    a.total = total;
+    return from_hip(attn::launch_prefill_exact(a, (hipStream_t)stream), "varlen prefill launch");
 }
 
 size_t attn_decode_workspace_size(int B, int H, int N_max, int d, int split_tokens)

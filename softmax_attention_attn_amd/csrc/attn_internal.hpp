@@ -16,6 +16,11 @@ struct PrefillArgs {
     int causal;
     float scale;
     int out_fp32;  // 0: bf16 output, 1: fp32 output
+    // Packed variable-length batch (cu_seqlens non-null): sequence b holds
+    // tokens [cu_seqlens[b], cu_seqlens[b+1]) of q/o [total, H, d] and k/v
+    // [total, Hkv, d]; lse is [H, total]; N is then the longest sequence.
+    const int32_t *cu_seqlens = nullptr;
+    int total = 0;
 };
 
 struct DecodeArgs {

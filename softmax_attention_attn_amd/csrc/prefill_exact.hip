@@ -86,11 +86,14 @@ template <int D>
 struct DmaLanes {
     static constexpr int kKMax = (Cfg<D>::kKPieces + kWaves - 1) / kWaves;
     uint32_t k[kKMax];  // byte offset of the lane's 16 bytes within the K tile
-    uint32_t v;         // the same for V piece `wave` (piece wave + kWaves*i adds i * kWaves KB)
+    uint32_t v;         // the same for V piece `wave`
+    uint32_t v_step;    // piece wave + kWaves*i is i * v_step bytes further on
 };
 
+// row_bytes: distance between consecutive key rows in memory (2d for the
+// [B, H, N, d] layout, 2*Hkv*d for packed tokens)
 template <int D>
-__device__ __forceinline__ DmaLanes<D> dma_lanes(int wave, int lane)
+__device__ __forceinline__ DmaLanes<D> dma_lanes(int wave, int lane, uint32_t row_bytes)
 {
     constexpr int C = Cfg<D>::kChunks;
     DmaLanes<D> dl;
@@ -98,32 +101,36 @@ __device__ __forceinline__ DmaLanes<D> dma_lanes(int wave, int lane)
     for (int i = 0; i < DmaLanes<D>::kKMax; ++i) {
         const int q = (wave + kWaves * i) * 64 + lane;
         const int row = q / (C + 1), c = q % (C + 1);
-        dl.k[i] = row * (D * 2) + (c == C ? 0 : c) * 16;
+        dl.k[i] = row * row_bytes + (c == C ? 0 : c) * 16;
     }
-    // a V piece is 1 KB of whole rows, and vswz depends only on the row modulo
-    // 4 (a multiple of a piece's row count), so pieces differ by a constant
+    // a V piece is 64/C whole rows, and vswz depends only on the row modulo
+    // 4 (a divisor of a piece's row count), so pieces differ by whole rows
     static_assert(64 % Cfg<D>::kChunks == 0 && (64 / Cfg<D>::kChunks) % 4 == 0, "V piece rows");
     {
         const int q = wave * 64 + lane;
         const int row = q / C;
-        dl.v = row * (D * 2) + ((q % C) ^ (vswz<D>(row) << 2)) * 16;
+        dl.v = row * row_bytes + ((q % C) ^ (vswz<D>(row) << 2)) * 16;
+        dl.v_step = kWaves * (64 / C) * row_bytes;
     }
     return dl;
 }
 
-// the tile of kBN rows at key k0 (k0 < N), cut at the sequence end
+// the tile of kBN rows at key k0 (k0 < N), cut at the sequence end; rows are
+// `stride` elements apart
 template <int D>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t *src, int k0, int N)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t *src, int k0, int N,
+                                                            int stride)
 {
-    return raw_rsrc(src + (size_t)k0 * D, (uint32_t)min(kBN, N - k0) * (D * 2));
+    const uint32_t rows = (uint32_t)min(kBN, N - k0);
+    return raw_rsrc(src + (size_t)k0 * stride, ((rows - 1) * (uint32_t)stride + D) * 2);
 }
 
 // this wave's pieces of the K tile at key k0 (wave is wave-uniform)
 template <int D>
 __device__ __forceinline__ void issue_k(unsigned char *lds_tile, const uint16_t *src, int k0, int N,
-                                        int wave, const DmaLanes<D> &dl)
+                                        int stride, int wave, const DmaLanes<D> &dl)
 {
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc<D>(src, k0, N);
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc<D>(src, k0, N, stride);
 #pragma unroll
     for (int i = 0; i < DmaLanes<D>::kKMax; ++i) {
         const int piece = wave + kWaves * i;
@@ -134,12 +141,12 @@ __device__ __forceinline__ void issue_k(unsigned char *lds_tile, const uint16_t 
 
 template <int D>
 __device__ __forceinline__ void issue_v(unsigned char *lds_tile, const uint16_t *src, int k0, int N,
-                                        int wave, const DmaLanes<D> &dl)
+                                        int stride, int wave, const DmaLanes<D> &dl)
 {
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc<D>(src, k0, N);
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc<D>(src, k0, N, stride);
 #pragma unroll
     for (int i = 0; i < Cfg<D>::kVPieces / kWaves; ++i)
-        dma16_rsrc(r, dl.v + i * kWaves * 1024, lds_tile + (wave + kWaves * i) * 1024);
+        dma16_rsrc(r, dl.v + i * dl.v_step, lds_tile + (wave + kWaves * i) * 1024);
 }
 
 // Per-wave running state of the online softmax and the output accumulator.
@@ -406,6 +413,17 @@ __device__ __forceinline__ float pipe_step(WaveState<D> &st, const bf16x8 (&qf)[
     return rs0 + rs1;
 }
 
+// One (batch, head) as the kernel sees it: row 0 of its Q, K, V, O and LSE,
+// its length, and the distance between consecutive rows (in elements) of
+// Q/O and of K/V.
+struct SeqView {
+    const uint16_t *q, *k, *v;
+    void *o;
+    float *lse;  // may be null
+    int N;
+    int q_stride, kv_stride;
+};
+
 // One query tile of one (batch, head): load its Q fragments, stream every
 // visible K/V tile through the LDS rings, write O and the LSE.
 //
@@ -416,18 +434,15 @@ __device__ __forceinline__ float pipe_step(WaveState<D> &st, const bf16x8 (&qf)[
 // t+1 read, and the stages the two steps load into were last read before the
 // previous synchronisation.  The prologue loads K0..K3, V0 and V1.
 template <int D, bool CAUSAL, bool OUT_F32>
-__device__ __forceinline__ void attend_qtile(const PrefillArgs &a, unsigned char *smem, int bh,
-                                             int qt, int wave, int lane)
+__device__ __forceinline__ void attend_qtile(const PrefillArgs &a, unsigned char *smem,
+                                             const SeqView &sv, int qt, int wave, int lane)
 {
     constexpr int kK = Cfg<D>::kKBytes, kV = Cfg<D>::kVBytes;
     const int g = lane >> 5, n = lane & 31;
-    const int N = a.N;
-    const int h = bh % a.H, b = bh / a.H;
+    const int N = sv.N;
     const int q0 = qt * kBM;
-    const int kvh = h / (a.H / a.Hkv);
-    const uint16_t *qb = (const uint16_t *)a.q + (size_t)bh * N * D;
-    const uint16_t *kb = (const uint16_t *)a.k + (size_t)(b * a.Hkv + kvh) * N * D;
-    const uint16_t *vb = (const uint16_t *)a.v + (size_t)(b * a.Hkv + kvh) * N * D;
+    const uint16_t *qb = sv.q, *kb = sv.k, *vb = sv.v;
+    const int kvs = sv.kv_stride;
     const int qw0 = q0 + wave * kQW;
     const int my_q = qw0 + n;
 
@@ -442,14 +457,14 @@ __device__ __forceinline__ void attend_qtile(const PrefillArgs &a, unsigned char
         return (CAUSAL && k0 + kBN - 1 > qw0) || k0 + kBN > N;
     };
     // direct loads per wave for one K / V tile
-    const DmaLanes<D> dl = dma_lanes<D>(wave, lane);
+    const DmaLanes<D> dl = dma_lanes<D>(wave, lane, (uint32_t)kvs * 2);
     auto load_k = [&](int t) {
         if (t < ntiles)
-            issue_k<D>(kst(t), kb, t * kBN, N, wave, dl);
+            issue_k<D>(kst(t), kb, t * kBN, N, kvs, wave, dl);
     };
     auto load_v = [&](int t) {
         if (t < ntiles)
-            issue_v<D>(vst(t), vb, t * kBN, N, wave, dl);
+            issue_v<D>(vst(t), vb, t * kBN, N, kvs, wave, dl);
     };
 
     load_k(0);
@@ -463,7 +478,7 @@ __device__ __forceinline__ void attend_qtile(const PrefillArgs &a, unsigned char
     bf16x8 qf[D / 16];
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks)
-        qf[ks] = as_bf16x8(my_q < N ? ld16(qb + (size_t)my_q * D + ks * 16 + g * 8)
+        qf[ks] = as_bf16x8(my_q < N ? ld16(qb + (size_t)my_q * sv.q_stride + ks * 16 + g * 8)
                                     : u32x4{0, 0, 0, 0});
 
     const LaneOffsets<D> off = lane_offsets<D>(lane);
@@ -513,8 +528,8 @@ __device__ __forceinline__ void attend_qtile(const PrefillArgs &a, unsigned char
         // the loads of K(t+4) and V(t+2) go to stages no wave reads in this
         // step; they are spread over the MFMA slots
         const bool lk = t + 4 < ntiles, lv = t + 2 < ntiles;
-        const __amdgpu_buffer_rsrc_t rk = tile_rsrc<D>(kb, lk ? (t + 4) * kBN : 0, N);
-        const __amdgpu_buffer_rsrc_t rv = tile_rsrc<D>(vb, lv ? (t + 2) * kBN : 0, N);
+        const __amdgpu_buffer_rsrc_t rk = tile_rsrc<D>(kb, lk ? (t + 4) * kBN : 0, N, kvs);
+        const __amdgpu_buffer_rsrc_t rv = tile_rsrc<D>(vb, lv ? (t + 2) * kBN : 0, N, kvs);
         unsigned char *const lk_st = kst(t + 4), *const lv_st = vst(t + 2);
         auto dma = [&](auto sc) {
             constexpr int S = decltype(sc)::value;
@@ -529,7 +544,7 @@ __device__ __forceinline__ void attend_qtile(const PrefillArgs &a, unsigned char
                     } else {
                         constexpr int i = d - NK;
                         if (lv)
-                            dma16_rsrc(rv, dl.v + i * kWaves * 1024,
+                            dma16_rsrc(rv, dl.v + i * dl.v_step,
                                        lv_st + (wave + kWaves * i) * 1024);
                     }
                 }
@@ -572,7 +587,7 @@ __device__ __forceinline__ void attend_qtile(const PrefillArgs &a, unsigned char
     if (my_q < N) {
         const float inv = 1.f / ltp;
         if constexpr (OUT_F32) {
-            float *orow = (float *)a.o + ((size_t)bh * N + my_q) * D;
+            float *orow = (float *)sv.o + (size_t)my_q * sv.q_stride;
 #pragma unroll
             for (int c = 0; c < D / 32; ++c)
 #pragma unroll
@@ -582,7 +597,7 @@ __device__ __forceinline__ void attend_qtile(const PrefillArgs &a, unsigned char
                     *(f32x4 *)(orow + 32 * c + 16 * g + 4 * j) = w;
                 }
         } else {
-            uint16_t *orow = (uint16_t *)a.o + ((size_t)bh * N + my_q) * D;
+            uint16_t *orow = (uint16_t *)sv.o + (size_t)my_q * sv.q_stride;
 #pragma unroll
             for (int c = 0; c < D / 32; ++c)
 #pragma unroll
@@ -595,25 +610,26 @@ __device__ __forceinline__ void attend_qtile(const PrefillArgs &a, unsigned char
                     st16(orow + 32 * c + 16 * g + 8 * j, w);
                 }
         }
-        if (a.lse && g == 0)
-            a.lse[(size_t)bh * N + my_q] = (st.m + log2f(lt)) * kLn2;
+        if (sv.lse && g == 0)
+            sv.lse[my_q] = (st.m + log2f(lt)) * kLn2;
     }
 }
 
-template <int D, bool CAUSAL, bool OUT_F32>
+template <int D, bool CAUSAL, bool OUT_F32, bool VARLEN>
 __global__ __launch_bounds__(kThreads) void prefill_exact_kernel(PrefillArgs a)
 {
-    // three K/V stages: tile t+2 loads while tile t+1's K and tile t's V are read
     // four K stages and four V stages (see attend_qtile)
     __shared__ __attribute__((aligned(1024)))
     unsigned char smem[4 * Cfg<D>::kKBytes + 4 * Cfg<D>::kVBytes];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-    const int nqt = (a.N + kBM - 1) / kBM;
     // Causal: workgroup j of a head takes query tiles nqt-1-j and j, so every
     // workgroup streams the same number of key tiles (no long tail of heavy
-    // tiles started last).  Non-causal: one query tile per workgroup.
-    const int nw = CAUSAL ? (nqt + 1) / 2 : nqt;
+    // tiles started last).  Non-causal: one query tile per workgroup.  In a
+    // packed batch the grid is sized for the longest sequence (N) and the
+    // workgroups past a shorter sequence's tiles return at once.
+    const int nqt_grid = (a.N + kBM - 1) / kBM;
+    const int nw = CAUSAL ? (nqt_grid + 1) / 2 : nqt_grid;
     const int BH = a.B * a.H;
     int bh, j;
     const int wg = blockIdx.x;
@@ -626,14 +642,44 @@ __global__ __launch_bounds__(kThreads) void prefill_exact_kernel(PrefillArgs a)
         bh = wg / nw;
         j = wg % nw;
     }
+    const int h = bh % a.H, b = bh / a.H;
+    const int kvh = h / (a.H / a.Hkv);
+    SeqView sv;
+    if constexpr (VARLEN) {
+        // offsets are clamped into [0, total], so malformed offsets cannot
+        // move an access out of the tensors
+        const int t0 = min(max(a.cu_seqlens[b], 0), a.total);
+        const int t1 = min(max(a.cu_seqlens[b + 1], t0), a.total);
+        sv.N = min(t1 - t0, a.N);
+        sv.q = (const uint16_t *)a.q + ((size_t)t0 * a.H + h) * D;
+        sv.k = (const uint16_t *)a.k + ((size_t)t0 * a.Hkv + kvh) * D;
+        sv.v = (const uint16_t *)a.v + ((size_t)t0 * a.Hkv + kvh) * D;
+        sv.o = (char *)a.o + ((size_t)t0 * a.H + h) * D * (OUT_F32 ? 4 : 2);
+        sv.lse = a.lse ? a.lse + (size_t)h * a.total + t0 : nullptr;
+        sv.q_stride = a.H * D;
+        sv.kv_stride = a.Hkv * D;
+    } else {
+        const size_t N = a.N;
+        sv.N = a.N;
+        sv.q = (const uint16_t *)a.q + (size_t)bh * N * D;
+        sv.k = (const uint16_t *)a.k + (size_t)(b * a.Hkv + kvh) * N * D;
+        sv.v = (const uint16_t *)a.v + (size_t)(b * a.Hkv + kvh) * N * D;
+        sv.o = (char *)a.o + (size_t)bh * N * D * (OUT_F32 ? 4 : 2);
+        sv.lse = a.lse ? a.lse + (size_t)bh * N : nullptr;
+        sv.q_stride = D;
+        sv.kv_stride = D;
+    }
+    const int nqt = (sv.N + kBM - 1) / kBM;
+    if (j >= (CAUSAL ? (nqt + 1) / 2 : nqt))
+        return;  // past this sequence's tiles (no barrier has been reached)
     if (CAUSAL) {
-        attend_qtile<D, CAUSAL, OUT_F32>(a, smem, bh, nqt - 1 - j, wave, lane);
+        attend_qtile<D, CAUSAL, OUT_F32>(a, smem, sv, nqt - 1 - j, wave, lane);
         if (j < nqt - 1 - j) {
             __syncthreads();  // every wave is done with the LDS stages
-            attend_qtile<D, CAUSAL, OUT_F32>(a, smem, bh, j, wave, lane);
+            attend_qtile<D, CAUSAL, OUT_F32>(a, smem, sv, j, wave, lane);
         }
     } else {
-        attend_qtile<D, CAUSAL, OUT_F32>(a, smem, bh, j, wave, lane);
+        attend_qtile<D, CAUSAL, OUT_F32>(a, smem, sv, j, wave, lane);
     }
 }
 
@@ -642,8 +688,13 @@ hipError_t launch_t(const PrefillArgs &a, hipStream_t s)
 {
     const int nqt = (a.N + kBM - 1) / kBM;
     dim3 grid(a.B * a.H * (CAUSAL ? (nqt + 1) / 2 : nqt));
-    ProfScope ps("prefill_exact", s);
-    hipLaunchKernelGGL((prefill_exact_kernel<D, CAUSAL, OUT_F32>), grid, dim3(kThreads), 0, s, a);
+    ProfScope ps(a.cu_seqlens ? "prefill_exact_varlen" : "prefill_exact", s);
+    if (a.cu_seqlens)
+        hipLaunchKernelGGL((prefill_exact_kernel<D, CAUSAL, OUT_F32, true>), grid,
+                           dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((prefill_exact_kernel<D, CAUSAL, OUT_F32, false>), grid,
+                           dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 

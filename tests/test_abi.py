@@ -63,6 +63,25 @@ def test_fwd_sage_workspace_required(A):
     assert _fwd(A, mode=1, workspace=P, workspace_bytes=need - 1) == A.ATTN_ERR_WORKSPACE
 
 
+def _fwdv(A, **kw):
+    args = dict(q=P, k=P, v=P, o=P, lse=None, cu_seqlens=P, B=3, H=4, Hkv=2, total=100,
+                max_seqlen=64, d=128, causal=1, scale=0.1, mode=0, o_dtype=0, stream=None)
+    args.update(kw)
+    return A.attn_fwd_varlen(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cu_seqlens=None), -1), (dict(q=None), -1), (dict(o=None), -1), (dict(B=0), -1),
+    (dict(total=0), -1), (dict(max_seqlen=0), -1), (dict(H=3), -1), (dict(scale=0.0), -1),
+    (dict(o_dtype=2), -1), (dict(mode=7), -1),
+    (dict(mode=1), -2), (dict(d=96), -2), (dict(max_seqlen=1 << 25), -2),
+    (dict(B=1 << 20, H=1 << 10, Hkv=1 << 10, d=64, max_seqlen=4096), -2),
+])
+def test_fwd_varlen_validation(A, kw, status):
+    assert _fwdv(A, **kw) == status
+    assert A.attn_last_error() != ""
+
+
 def _dec(A, **kw):
     args = dict(q=P, k_cache=P, v_cache=P, seqlens=P, o=P, lse=None, B=2, H=8, Hkv=2,
                 N_max=1024, d=128, scale=0.1, mode=0, o_dtype=0, split_tokens=512,

@@ -247,6 +247,33 @@ def test_decode_kv_len_matches_brute(oracle_lib):
     np.testing.assert_allclose(lse, lseb, atol=1e-12)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_is_block_diagonal_attention(oracle_lib, causal):
+    """The packed batch against one softmax over all packed tokens whose mask
+    keeps only same-sequence (and, causal, earlier-or-equal) keys."""
+    g = torch.Generator().manual_seed(21)
+    lens = [5, 0, 1, 9, 3]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T, H, Hkv, d, scale = int(cu[-1]), 4, 2, 8, 0.3
+    q, k, v = _rand((T, H, d), g), _rand((T, Hkv, d), g), _rand((T, Hkv, d), g)
+    o, lse = oracle.attn_varlen(bf16_bits(q), bf16_bits(k), bf16_bits(v), cu, causal=causal,
+                                scale=scale)
+    seq = np.repeat(np.arange(len(lens)), lens)
+    pos = np.arange(T) - cu[seq]
+    mask = seq[:, None] == seq[None, :]
+    if causal:
+        mask &= pos[None, :] <= pos[:, None]
+    qd, kd, vd = (x.to(torch.float64).numpy() for x in (q, k, v))
+    for h in range(H):
+        gh = h // (H // Hkv)
+        S = np.where(mask, qd[:, h] @ kd[:, gh].T * scale, -np.inf)
+        m = S.max(axis=1, keepdims=True)
+        E = np.exp(S - m)
+        np.testing.assert_allclose(o[:, h], (E / E.sum(1, keepdims=True)) @ vd[:, gh],
+                                   atol=1e-12)
+        np.testing.assert_allclose(lse[h], m[:, 0] + np.log(E.sum(1)), atol=1e-12)
+
+
 def test_gather_pages_worked_example():
     # pool of 3 pages of 2 rows (1 kv head, d = 1); page p row j holds 10p + j.
     # Sequence 0 (3 keys) uses pages 2 then 0, sequence 1 (4 keys) pages 1 then 2:

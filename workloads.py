@@ -18,6 +18,10 @@ Recipe (all draws from one ``torch.Generator`` on the CPU seeded with
   then q [B, H, d], then the valid K rows batch by batch ([Hkv, L_b, d] each),
   then the valid V rows the same way; cache positions at or beyond L_b hold
   bf16 NaN so that any over-read shows up in the output;
+* a packed variable-length batch draws its lengths (uniform integers in
+  [len_lo, len_hi], generator seeded with ``seed``), then Q, K and V over all
+  packed tokens, token-major ([total, heads, d]), from a generator seeded with
+  ``seed + 1``;
 * paged decode takes those caches and spreads their pages over a pool in a
   random order (its own generator, seeded separately); unused pool pages and
   the rows of a last page past L_b hold NaN.
@@ -65,6 +69,10 @@ class Workload:
         if self.kind == "decode":
             total = int(np.sum(seqlens)) if seqlens is not None else self.B * self.N
             return 4.0 * self.H * self.d * total
+        if self.kind == "varlen":
+            sq = float(np.sum(np.asarray(seqlens, dtype=np.float64) ** 2))
+            f = 4.0 * self.H * sq * self.d
+            return f / 2 if self.causal else f
         f = 4.0 * self.B * self.H * self.N * self.N * self.d
         return f / 2 if self.causal else f
 
@@ -79,6 +87,9 @@ WORKLOADS = {
                            len_hi=32768, split_tokens=512),
     "long_prefill": Workload("long_prefill", "prefill", 1, 16, 16, 65536, 128, causal=True,
                              outlier_frac=0.001, outlier_mult=20.0),
+    # packed batch of 8 sequences, lengths uniform on [256, 4096] (N = the bound)
+    "varlen_prefill": Workload("varlen_prefill", "varlen", 8, 32, 32, 4096, 128, causal=True,
+                               len_lo=256, len_hi=4096),
 }
 
 
@@ -166,8 +177,26 @@ def paginate(cache, table, num_pages: int, page_size: int):
     return pool
 
 
+def make_varlen(lengths, H, Hkv, d, *, seed=0):
+    """A packed batch: q [total,H,d], k/v [total,Hkv,d] bf16 (token-major) and
+    cu_seqlens int32 [B+1], for the given sequence lengths; Q, then K, then V
+    ~ N(0, 1) over all packed tokens."""
+    lengths = [int(x) for x in lengths]
+    cu = torch.tensor([0] + list(np.cumsum(lengths)), dtype=torch.int32)
+    T = int(cu[-1])
+    g = _gen(seed)
+    q = torch.randn((T, H, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    k = torch.randn((T, Hkv, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    v = torch.randn((T, Hkv, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    return q, k, v, cu
+
+
 def make(w: Workload):
     """Inputs of a named workload (CPU tensors)."""
+    if w.kind == "varlen":
+        lengths = torch.randint(w.len_lo, w.len_hi + 1, (w.B,), generator=_gen(w.seed))
+        q, k, v, cu = make_varlen(lengths.tolist(), w.H, w.Hkv, w.d, seed=w.seed + 1)
+        return dict(q=q, k=k, v=v, cu_seqlens=cu, seqlens=lengths.to(torch.int32))
     if w.kind == "decode":
         q, k, v, seqlens = make_decode(w.B, w.H, w.Hkv, w.N, w.d, len_lo=w.len_lo,
                                        len_hi=w.len_hi, seed=w.seed)
