@@ -16,6 +16,10 @@ What each routine follows:
   softmax preserve exact attention; "cuda-kernel-pretrain" page, §2).  Also the
   decode case (one query row, ``kv_len`` valid keys) and partial attention over
   a key range (Flash-Decoding's chunks, "flashattention-kernels" page, §3).
+* ``attn_bwd`` -- the gradients of exact attention (dQ, dK, dV for an
+  upstream dO), by the chain rule through the explicit softmax row by row
+  (the backward pass the training kernels of the pages compute: "GPU kernel
+  overview" page, SageBwd; "flashattention-kernels" page §0, FA2/FA3).
 * ``attn_varlen`` -- the same over a packed batch of variable-length
   sequences, each attending only to its own tokens (packing without padding,
   "flashattention-kernels" page, recommendation table and §3).
@@ -75,6 +79,9 @@ def _load():
         _u16p, _u16p, _u16p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p, ctypes.c_int64, ctypes.c_int64,
         ctypes.c_double, _i64p, ctypes.c_int64, _f64p, _f64p, ctypes.c_int]
+    lib.oracle_attn_bwd.restype = ctypes.c_int
+    lib.oracle_attn_bwd.argtypes = [_u16p, _u16p, _u16p, _u16p] + [ctypes.c_int] * 6 + [
+        ctypes.c_double, _f64p, _f64p, _f64p, ctypes.c_int]
     lib.oracle_lse_merge.restype = None
     lib.oracle_lse_merge.argtypes = [_f64p, _f64p, ctypes.c_int, ctypes.c_int64,
                                      ctypes.c_int, _f64p, _f64p]
@@ -162,6 +169,30 @@ def attn_rows(q, k, v, *, causal: bool, scale: float, rows=None, kv_len=None,
         o = o.reshape(B, H, Nq, d)
         lse = lse.reshape(B, H, Nq)
     return o, lse, err
+
+
+def attn_bwd(q, k, v, dout, *, causal: bool, scale: float, threads: int | None = None):
+    """Gradients (dq, dk, dv) of exact attention for the upstream gradient
+    ``dout``, in fp64 (chain rule through the explicit softmax, row by row;
+    a kv head's gradients sum over its query heads).
+
+    q, dout [B,H,N,d]; k, v [B,Hkv,N,d] (uint16 bf16 bits).
+    """
+    q, k, v, dout = _u16(q), _u16(k), _u16(v), _u16(dout)
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, N, d) or v.shape != k.shape or dout.shape != q.shape:
+        raise ValueError("shape mismatch")
+    dq = np.empty((B, H, N, d), dtype=np.float64)
+    dk = np.empty((B, Hkv, N, d), dtype=np.float64)
+    dv = np.empty((B, Hkv, N, d), dtype=np.float64)
+    err = _load().oracle_attn_bwd(_ptr(q, _u16p), _ptr(k, _u16p), _ptr(v, _u16p),
+                                  _ptr(dout, _u16p), B, H, Hkv, N, d, int(bool(causal)),
+                                  float(scale), _ptr(dq, _f64p), _ptr(dk, _f64p), _ptr(dv, _f64p),
+                                  int(threads or default_threads()))
+    if err < 0:
+        raise ValueError("oracle_attn_bwd rejected its arguments")
+    return dq, dk, dv
 
 
 def attn_varlen(q, k, v, cu_seqlens, *, causal: bool, scale: float,

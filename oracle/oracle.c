@@ -247,6 +247,101 @@ double oracle_attn_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
 }
 
 /*
+ * Gradients of O = softmax(Q K^T * scale + mask) V with respect to Q, K and V
+ * for an upstream gradient dO (the backward pass of the attention forward;
+ * "GPU kernel overview" page, SageBwd / training gaps; "flashattention-
+ * kernels" page §0, FA2/FA3 as training kernels).  The pages print no
+ * formula; these are the chain rule through the definition, row by row:
+ *     P_i   = softmax over the visible keys of S_i,  S_ij = scale * Q_i . K_j
+ *     dP_ij = dO_i . V_j
+ *     D_i   = sum_j P_ij dP_ij
+ *     dS_ij = P_ij (dP_ij - D_i)
+ *     dQ_i  = scale * sum_j dS_ij K_j
+ *     dK_j += scale * dS_ij Q_i,   dV_j += P_ij dO_i
+ * A kv head's dK and dV sum over the query heads of its group.
+ * q, dout [B,H,N,d]; k, v [B,Hkv,N,d] (bf16 bits).  dq [B,H,N,d] and
+ * dk, dv [B,Hkv,N,d] are written in fp64.  Returns 0, or -1 on invalid
+ * arguments.
+ */
+int oracle_attn_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                    const uint16_t *dout, int B, int H, int Hkv, int N, int d, int causal,
+                    double scale, double *dq, double *dk, double *dv, int nthreads)
+{
+    if (B <= 0 || H <= 0 || Hkv <= 0 || H % Hkv != 0 || N <= 0 || d <= 0)
+        return -1;
+    const int G = H / Hkv;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    memset(dk, 0, sizeof(double) * (size_t)B * Hkv * N * d);
+    memset(dv, 0, sizeof(double) * (size_t)B * Hkv * N * d);
+    /* one (batch, kv head) per iteration: its dK and dV have one writer */
+#pragma omp parallel
+    {
+        double *S = (double *)malloc(sizeof(double) * (size_t)N);
+        double *P = (double *)malloc(sizeof(double) * (size_t)N);
+        double *dP = (double *)malloc(sizeof(double) * (size_t)N);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t bg = 0; bg < (int64_t)B * Hkv; ++bg) {
+            const int64_t b = bg / Hkv, g = bg % Hkv;
+            const uint16_t *kb = k + bg * (int64_t)N * d;
+            const uint16_t *vb = v + bg * (int64_t)N * d;
+            double *dkb = dk + bg * (int64_t)N * d;
+            double *dvb = dv + bg * (int64_t)N * d;
+            for (int64_t h = g * G; h < (g + 1) * G; ++h) {
+                const int64_t bh = b * H + h;
+                for (int64_t i = 0; i < N; ++i) {
+                    const uint16_t *qi = q + (bh * N + i) * d;
+                    const uint16_t *doi = dout + (bh * N + i) * d;
+                    double *dqi = dq + (bh * N + i) * d;
+                    const int64_t n = causal ? i + 1 : N;
+                    for (int64_t j = 0; j < n; ++j) {
+                        double dot = 0.0, dd = 0.0;
+                        for (int c = 0; c < d; ++c) {
+                            dot += bf16_to_f64(qi[c]) * bf16_to_f64(kb[j * d + c]);
+                            dd += bf16_to_f64(doi[c]) * bf16_to_f64(vb[j * d + c]);
+                        }
+                        S[j] = dot * scale;
+                        dP[j] = dd;
+                    }
+                    double m = S[0];
+                    for (int64_t j = 1; j < n; ++j)
+                        if (S[j] > m)
+                            m = S[j];
+                    double sum = 0.0;
+                    for (int64_t j = 0; j < n; ++j) {
+                        P[j] = exp(S[j] - m);
+                        sum += P[j];
+                    }
+                    double D = 0.0;
+                    for (int64_t j = 0; j < n; ++j) {
+                        P[j] /= sum;
+                        D += P[j] * dP[j];
+                    }
+                    for (int c = 0; c < d; ++c)
+                        dqi[c] = 0.0;
+                    for (int64_t j = 0; j < n; ++j) {
+                        const double ds = P[j] * (dP[j] - D);
+                        for (int c = 0; c < d; ++c) {
+                            dqi[c] += scale * ds * bf16_to_f64(kb[j * d + c]);
+                            dkb[j * d + c] += scale * ds * bf16_to_f64(qi[c]);
+                            dvb[j * d + c] += P[j] * bf16_to_f64(doi[c]);
+                        }
+                    }
+                }
+            }
+        }
+        free(S);
+        free(P);
+        free(dP);
+    }
+    return 0;
+}
+
+/*
  * Merge of partial results over disjoint key sets (the reduction step of
  * split-KV decoding): with M = max_s lse_s and w_s = exp(lse_s - M),
  * O = sum_s w_s O_s / sum_s w_s and lse = M + ln sum_s w_s.
