@@ -194,6 +194,33 @@ attn_status attn_decode_paged(const void *q, const void *k_pages, const void *v_
                               int split_tokens, void *workspace, size_t workspace_bytes,
                               void *stream);
 
+/*
+ * Backward pass of the exact mode: the gradients dQ, dK, dV of
+ * O = softmax(Q K^T * scale + mask) V for an upstream gradient dO, given the
+ * forward's O and LSE (the training side of the pages' kernels: "GPU kernel
+ * overview" page, SageBwd and the training gaps; "flashattention-kernels"
+ * page §0, FA2/FA3 as training kernels).  With P recomputed from the LSE:
+ *     dP = dO V^T,  D_i = dO_i . O_i,  dS = P * (dP - D),
+ *     dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO,
+ * and a kv head's dK/dV sum over the query heads of its group.  Deterministic
+ * (no atomics).
+ *   q, o, dout  device bf16 [B, H, N, d];  k, v  device bf16 [B, Hkv, N, d].
+ *   lse        device fp32 [B, H, N] as written by attn_fwd (natural log).
+ *   dq         device [B, H, N, d];  dk, dv  device [B, Hkv, N, d]; all of
+ *              dtype grad_dtype (attn_dtype).
+ *   workspace  at least attn_bwd_workspace_size() bytes (fp32 D and
+ *              lse*log2(e) per row); overwritten.
+ * Errors: as attn_fwd (d in {64, 128}); null lse or any null tensor is
+ * ATTN_ERR_INVALID_ARG; a missing or short workspace ATTN_ERR_WORKSPACE.
+ */
+attn_status attn_bwd(const void *q, const void *k, const void *v, const void *o,
+                     const float *lse, const void *dout, void *dq, void *dk, void *dv, int B,
+                     int H, int Hkv, int N, int d, int causal, float scale, int grad_dtype,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace attn_bwd needs (0 for invalid sizes). */
+size_t attn_bwd_workspace_size(int B, int H, int N);
+
 /* Static description of a status code. */
 const char *attn_status_string(int status);
 

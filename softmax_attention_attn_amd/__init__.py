@@ -8,8 +8,8 @@ the library's HIP kernels; there is no fallback.  Importing this package
 fails loudly when the library has not been built.
 
 The functions carry the C names (``attn_fwd``, ``attn_decode``, ...); the
-convenience wrappers ``fwd``, ``fwd_varlen``, ``decode`` and ``decode_paged``
-allocate what the caller omits.
+convenience wrappers ``fwd``, ``fwd_varlen``, ``bwd``, ``decode`` and
+``decode_paged`` allocate what the caller omits.
 """
 from __future__ import annotations
 
@@ -35,9 +35,10 @@ ATTN_OUT_FP32 = 1
 
 MODES = {"exact": ATTN_MODE_EXACT_BF16, "sage": ATTN_MODE_SAGE_QK_I8_BLK64_PV_FP8_E4M3}
 
-EXPORTS = ("attn_fwd", "attn_fwd_workspace_size", "attn_fwd_varlen", "attn_decode",
-           "attn_decode_workspace_size", "attn_decode_paged", "attn_status_string",
-           "attn_last_error", "attn_profiler_enable", "attn_profiler_read")
+EXPORTS = ("attn_fwd", "attn_fwd_workspace_size", "attn_fwd_varlen", "attn_bwd",
+           "attn_bwd_workspace_size", "attn_decode", "attn_decode_workspace_size",
+           "attn_decode_paged", "attn_status_string", "attn_last_error",
+           "attn_profiler_enable", "attn_profiler_read")
 
 
 class AttnError(RuntimeError):
@@ -56,6 +57,10 @@ def _load():
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, sz, vp]
     lib.attn_fwd_workspace_size.restype = sz
     lib.attn_fwd_workspace_size.argtypes = [i, i, i, i, i, i]
+    lib.attn_bwd.restype = i
+    lib.attn_bwd.argtypes = [vp] * 9 + [i, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.attn_bwd_workspace_size.restype = sz
+    lib.attn_bwd_workspace_size.argtypes = [i, i, i]
     lib.attn_fwd_varlen.restype = i
     lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, vp]
     lib.attn_decode.restype = i
@@ -128,6 +133,16 @@ def attn_fwd_varlen(q, k, v, o, lse, cu_seqlens, B, H, Hkv, total, max_seqlen, d
                     mode, o_dtype, stream) -> int:
     return int(_lib.attn_fwd_varlen(q, k, v, o, lse, cu_seqlens, B, H, Hkv, total, max_seqlen, d,
                                     causal, scale, mode, o_dtype, stream))
+
+
+def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Hkv, N, d, causal, scale, grad_dtype,
+             workspace, workspace_bytes, stream) -> int:
+    return int(_lib.attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Hkv, N, d, causal, scale,
+                             grad_dtype, workspace, workspace_bytes, stream))
+
+
+def attn_bwd_workspace_size(B, H, N) -> int:
+    return int(_lib.attn_bwd_workspace_size(B, H, N))
 
 
 def attn_decode(q, k_cache, v_cache, seqlens, o, lse, B, H, Hkv, N_max, d, scale, mode,
@@ -210,6 +225,40 @@ def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, mode: str 
                        workspace.numel() if workspace is not None else 0, _stream(stream))
     _check(st)
     return o, lse
+
+
+def bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: float | None = None,
+        grad_dtype=torch.bfloat16, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Gradients of the exact forward.  q/o/dout [B,H,N,d], k/v [B,Hkv,N,d] bf16,
+    lse fp32 [B,H,N] from ``fwd``.  Returns (dq, dk, dv) of ``grad_dtype``."""
+    for t, name in ((q, "q"), (o, "o"), (dout, "dout")):
+        _need(t, name, torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(v, "v", torch.bfloat16, 4)
+    _need(lse, "lse", torch.float32, 3)
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (B, Hkv, N, d) or tuple(v.shape) != tuple(k.shape) or \
+            tuple(o.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape) or \
+            tuple(lse.shape) != (B, H, N):
+        raise ValueError("shapes do not agree")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    g_code = {torch.bfloat16: ATTN_OUT_BF16, torch.float32: ATTN_OUT_FP32}[grad_dtype]
+    if dq is None:
+        dq = torch.empty((B, H, N, d), dtype=grad_dtype, device=q.device)
+    if dk is None:
+        dk = torch.empty((B, Hkv, N, d), dtype=grad_dtype, device=q.device)
+    if dv is None:
+        dv = torch.empty((B, Hkv, N, d), dtype=grad_dtype, device=q.device)
+    ws_bytes = attn_bwd_workspace_size(B, H, N)
+    if workspace is None:
+        workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=q.device)
+    st = _lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                       _ptr(dk), _ptr(dv), B, H, Hkv, N, d, int(bool(causal)), float(scale),
+                       g_code, _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st)
+    return dq, dk, dv
 
 
 def fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, *, causal: bool = False,

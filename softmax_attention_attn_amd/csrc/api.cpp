@@ -246,6 +246,63 @@ attn_status attn_fwd_varlen(const void *q, const void *k, const void *v, void *o
     return from_hip(attn::launch_prefill_exact(a, (hipStream_t)stream), "varlen prefill launch");
 }
 
+size_t attn_bwd_workspace_size(int B, int H, int N)
+{
+    if (B <= 0 || H <= 0 || N <= 0)
+        return 0;
+    return 2 * align_up(sizeof(float) * (size_t)B * H * N, 256);
+}
+
+attn_status attn_bwd(const void *q, const void *k, const void *v, const void *o,
+                     const float *lse, const void *dout, void *dq, void *dk, void *dv, int B,
+                     int H, int Hkv, int N, int d, int causal, float scale, int grad_dtype,
+                     void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
+        return fail(ATTN_ERR_INVALID_ARG,
+                    "q, k, v, o, lse, dout, dq, dk and dv must be non-null device pointers");
+    if (B <= 0 || H <= 0 || Hkv <= 0 || N <= 0 || d <= 0)
+        return fail(ATTN_ERR_INVALID_ARG, "sizes must be positive (B=%d H=%d Hkv=%d N=%d d=%d)",
+                    B, H, Hkv, N, d);
+    if (H % Hkv != 0)
+        return fail(ATTN_ERR_INVALID_ARG, "H=%d is not a multiple of Hkv=%d", H, Hkv);
+    if (!valid_scale(scale))
+        return fail(ATTN_ERR_INVALID_ARG, "scale must be finite and > 0");
+    if (grad_dtype != ATTN_OUT_BF16 && grad_dtype != ATTN_OUT_FP32)
+        return fail(ATTN_ERR_INVALID_ARG, "unknown gradient dtype %d", grad_dtype);
+    if (d != 64 && d != 128)
+        return fail(ATTN_ERR_UNSUPPORTED, "head dim d=%d (supported: 64, 128)", d);
+    const long long nt = ((long long)N + 127) / 128;
+    if ((long long)B * H * nt > 0x7fffffffLL || (long long)B * H * N > 0x7fffffffLL ||
+        N > (1 << 24))
+        return fail(ATTN_ERR_UNSUPPORTED, "problem too large for the grid mapping");
+    const size_t need = attn_bwd_workspace_size(B, H, N);
+    if (!workspace || workspace_bytes < need)
+        return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    attn::BwdArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.dout = dout;
+    a.lse = lse;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.B = B;
+    a.H = H;
+    a.Hkv = Hkv;
+    a.N = N;
+    a.d = d;
+    a.causal = causal != 0;
+    a.scale = scale;
+    a.out_fp32 = grad_dtype == ATTN_OUT_FP32;
+    a.delta = (float *)workspace;
+    a.lse2 = (float *)((char *)workspace + align_up(sizeof(float) * (size_t)B * H * N, 256));
+    return from_hip(attn::launch_bwd(a, (hipStream_t)stream), "backward launch");
+}
+
 size_t attn_decode_workspace_size(int B, int H, int N_max, int d, int split_tokens)
 {
     if (B <= 0 || H <= 0 || N_max <= 0 || d <= 0 || split_tokens <= 0)

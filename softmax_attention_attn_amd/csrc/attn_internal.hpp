@@ -43,6 +43,18 @@ struct DecodeArgs {
     int page_shift = 0, max_pages = 0, num_pages = 0;
 };
 
+struct BwdArgs {
+    const void *q, *k, *v, *o, *dout;  // bf16; q/o/dout [B,H,N,d], k/v [B,Hkv,N,d]
+    const float *lse;                  // [B,H,N], natural log, from the forward
+    void *dq, *dk, *dv;                // dq [B,H,N,d], dk/dv [B,Hkv,N,d]
+    int B, H, Hkv, N, d;
+    int causal;
+    float scale;
+    int out_fp32;  // gradients in fp32 (1) or bf16 (0)
+    float *delta;  // workspace [B,H,N]: dO . O per row
+    float *lse2;   // workspace [B,H,N]: lse * log2(e)
+};
+
 struct SageArgs {
     PrefillArgs p;
     void *workspace;
@@ -54,6 +66,7 @@ struct SageArgs {
 hipError_t launch_prefill_exact(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);  // contiguous or paged caches
 hipError_t launch_sage(const SageArgs &a, hipStream_t s);
+hipError_t launch_bwd(const BwdArgs &a, hipStream_t s);
 size_t sage_workspace_bytes(int B, int H, int Hkv, int N, int d);
 
 // Benchmark timing hooks (api.cpp): bracket one kernel launch with events when

@@ -1,0 +1,473 @@
+// Attention backward for gfx950: dQ, dK and dV of the exact forward
+// O = softmax(Q K^T * s + mask) V for an upstream gradient dO, with the
+// forward's LSE (the backward pass of the training kernels the pages discuss:
+// "GPU kernel overview" page, SageBwd and the training gaps;
+// "flashattention-kernels" page §0, FA2/FA3).  Per row i, with P recomputed
+// from the LSE:
+//     P_ij = exp(s Q_i.K_j - lse_i),  dP_ij = dO_i.V_j,  D_i = dO_i.O_i,
+//     dS_ij = P_ij (dP_ij - D_i),
+//     dQ_i = s sum_j dS_ij K_j,  dK_j = s sum_i dS_ij Q_i,  dV_j = sum_i P_ij dO_i,
+// and a kv head's dK/dV sum over the query heads of its group.
+//
+// Three kernels, no atomics (every output element has one writer, so the
+// result is deterministic):
+//  * bwd_delta: D_i = dO_i . O_i in fp32, and lse_i * log2(e), per row.
+//  * bwd_dq: query-stationary.  A workgroup owns 128 queries (4 waves x 32)
+//    of one head, keeps their Q and dO in registers and streams the K/V
+//    tiles (64 keys) through LDS: S^T = K Q^T and dP^T = V dO^T on the MFMA,
+//    dS^T in registers, dQ^T += K^T dS^T with K^T gathered by transposing
+//    LDS reads.
+//  * bwd_dkv: key-stationary.  A workgroup owns 128 keys (4 waves x 32) of
+//    one kv head, keeps their K and V in registers and streams, for every
+//    query head of the group, the Q/dO tiles (64 queries) through LDS:
+//    S = Q K^T, dP = dO V^T, dS, then dV^T += dO^T P and dK^T += Q^T dS with
+//    dO^T and Q^T gathered by transposing reads.
+// Products take bf16 operands (P and dS rounded to bf16) with fp32
+// accumulation; the outputs are bf16 or fp32.
+#include "attn_internal.hpp"
+#include "cdna4.hpp"
+
+namespace attn {
+namespace {
+
+constexpr int kBWaves = 4;
+constexpr int kBThreads = 64 * kBWaves;
+constexpr int kRows = 32 * kBWaves;  // queries (dq) or keys (dkv) per workgroup
+constexpr int kTile = 64;            // streamed rows per step
+
+// LDS tile of kTile rows of D bf16, rows padded by 16 bytes: a lane group
+// reading 16 bytes of 16 consecutive rows hits 16 distinct bank quads.
+template <int D>
+struct BCfg {
+    static constexpr int kChunks = D / 8;             // 16-byte chunks per row
+    static constexpr int kPitch = D * 2 + 16;         // bytes per LDS row
+    static constexpr int kPieces = kTile * (kChunks + 1) / 64;  // 1 KB direct loads
+    static constexpr int kBytes = kPieces * 1024;
+    static constexpr int kPerWave = (kPieces + kBWaves - 1) / kBWaves;
+    static_assert(kPieces * 64 == kTile * (kChunks + 1), "tile split");
+};
+
+// Direct loads of one padded tile: piece p = wave + 4i of the tile's pieces,
+// lane l fills LDS slot 64p + l = row (64p+l)/(C+1), chunk (64p+l)%(C+1) (the
+// pad chunk re-reads chunk 0).  Rows at or past `rows` read as zero (the
+// buffer resource ends there).
+template <int D>
+struct TileLanes {
+    uint32_t off[BCfg<D>::kPerWave];  // source byte offset within the tile
+};
+
+template <int D>
+__device__ __forceinline__ TileLanes<D> tile_lanes(int wave, int lane)
+{
+    constexpr int C = BCfg<D>::kChunks;
+    TileLanes<D> t;
+#pragma unroll
+    for (int i = 0; i < BCfg<D>::kPerWave; ++i) {
+        const int q = (wave + kBWaves * i) * 64 + lane;
+        const int row = q / (C + 1), c = q % (C + 1);
+        t.off[i] = row * (D * 2) + (c == C ? 0 : c) * 16;
+    }
+    return t;
+}
+
+template <int D>
+__device__ __forceinline__ void load_tile(unsigned char *lds, const uint16_t *src, int r0, int N,
+                                          int wave, const TileLanes<D> &tl)
+{
+    const int rows = min(kTile, N - r0);
+    const __amdgpu_buffer_rsrc_t r = raw_rsrc(src + (size_t)r0 * D, (uint32_t)rows * D * 2);
+#pragma unroll
+    for (int i = 0; i < BCfg<D>::kPerWave; ++i) {
+        const int piece = wave + kBWaves * i;
+        if (piece < BCfg<D>::kPieces)
+            dma16_rsrc(r, tl.off[i], lds + piece * 1024);
+    }
+}
+
+// A operand read straight from a padded tile: lane (n, g) takes row
+// row0 + n, bf16 columns 16*ks + 8g .. +7.
+template <int D>
+__device__ __forceinline__ uint32_t direct_addr(uint32_t tile, int row0, int lane)
+{
+    return tile + (row0 + (lane & 31)) * BCfg<D>::kPitch + (lane >> 5) * 16;
+}
+
+// A operand X^T read from a padded tile of X (rows = the contraction index):
+// for the 16 contraction rows base .. base+15 and the 32 columns 32c ..
+// 32c+31, lane l (half h = l/32) gets column 32c + l%32 at rows
+// base + 4h + 0..3 and base + 8 + 4h + 0..3, the order in which an MFMA
+// accumulator of S (rows 8(r/4) + 4g + r%4) hands its registers 8u .. 8u+7 to
+// the B operand.  Two transposing reads: in each 16-lane group lane 4j + q
+// points at row (base + 4h + j), columns 32c + 16(G&1) + 4q .. +3, and lane i
+// of the group receives column 32c + 16(G&1) + i of the four rows.
+template <int D>
+__device__ __forceinline__ uint32_t trans_addr(uint32_t tile, int lane)
+{
+    const int G = lane >> 4, L = lane & 15, j = L >> 2, q = L & 3, h = G >> 1;
+    return tile + (4 * h + j) * BCfg<D>::kPitch + (16 * (G & 1) + 4 * q) * 2;
+}
+
+// the 16 contraction rows starting at ROW0 and the column block C of the
+// tile (both compile-time, folded into the read offsets)
+template <int D, int ROW0, int C>
+__device__ __forceinline__ u32x4 trans_read(uint32_t addr)
+{
+    constexpr int off = ROW0 * BCfg<D>::kPitch + C * 64;
+    const u32x2 a = lds_read_tr16_b64<off>(addr);
+    const u32x2 b = lds_read_tr16_b64<off + 8 * BCfg<D>::kPitch>(addr);
+    return u32x4{a[0], a[1], b[0], b[1]};
+}
+
+// The 16 bf16 of an MFMA accumulator, rounded and packed in register order.
+__device__ __forceinline__ void pack16(const float (&x)[16], uint32_t (&w)[8])
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        w[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+}
+
+// Store a transposed accumulator: acc[c] holds rows 32c + 8(r/4) + 4g + r%4
+// (feature index) of column `row` (the lane's query or key); four
+// consecutive features per (c, r/4).
+template <int D, bool OUT_F32>
+__device__ __forceinline__ void store_rows(void *base, size_t row, int g, const f32x16 (&acc)[D / 32],
+                                           float mul)
+{
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+        for (int R = 0; R < 4; ++R) {
+            const int col = 32 * c + 8 * R + 4 * g;
+            const float x0 = acc[c][4 * R] * mul, x1 = acc[c][4 * R + 1] * mul,
+                        x2 = acc[c][4 * R + 2] * mul, x3 = acc[c][4 * R + 3] * mul;
+            if constexpr (OUT_F32) {
+                *(f32x4 *)((float *)base + row * D + col) = f32x4{x0, x1, x2, x3};
+            } else {
+                *(u32x2 *)((uint16_t *)base + row * D + col) =
+                    u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+            }
+        }
+}
+
+// Workgroup -> (outer index, tile) with the outer index's tiles kept on one
+// XCD (workgroup i runs on XCD i % 8) when the outer count is a multiple of 8.
+__device__ __forceinline__ void bwd_task(int wg, int ntile, int nouter, int &outer, int &tile)
+{
+    if ((nouter & 7) == 0) {
+        const int xcd = wg & 7, slot = wg >> 3;
+        outer = xcd + 8 * (slot / ntile);
+        tile = slot % ntile;
+    } else {
+        outer = wg / ntile;
+        tile = wg % ntile;
+    }
+}
+
+// ---------------------------------------------------------------- D, lse2
+// One 16-lane group per row: D = dO . O (fp32), lse2 = lse * log2(e).
+template <int D>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a)
+{
+    constexpr int LPR = D / 8;  // lanes per row (16 bytes each)
+    const int rows_per_block = 256 / LPR;
+    const long long row = (long long)blockIdx.x * rows_per_block + threadIdx.x / LPR;
+    const int sub = threadIdx.x % LPR;
+    const long long nrows = (long long)a.B * a.H * a.N;
+    float dot = 0.f;
+    if (row < nrows) {
+        const u32x4 x = ld16((const uint16_t *)a.dout + row * D + sub * 8);
+        const u32x4 y = ld16((const uint16_t *)a.o + row * D + sub * 8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            dot += bf16_lo(x[e]) * bf16_lo(y[e]) + bf16_hi(x[e]) * bf16_hi(y[e]);
+    }
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1)
+        dot += __shfl_xor(dot, off, LPR);
+    if (row < nrows && sub == 0) {
+        a.delta[row] = dot;
+        a.lse2[row] = a.lse[row] * kLog2e;
+    }
+}
+
+// ---------------------------------------------------------------- dQ
+// Workgroup: 128 queries of one (b, h); wave w owns queries q0 + 32w .. +31
+// (lane n = l % 32 is query q0 + 32w + n).  Key tiles of 64 stream through a
+// 2-stage LDS ring (K and V, padded rows), loaded by direct loads one step
+// ahead; the workgroup synchronises once per step.
+template <int D, bool CAUSAL, bool OUT_F32>
+__global__ __launch_bounds__(kBThreads) void bwd_dq_kernel(BwdArgs a)
+{
+    constexpr int KB = BCfg<D>::kBytes, KS = D / 16, NC = D / 32;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * KB];
+    const int lane = threadIdx.x & 63, g = lane >> 5, n = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int N = a.N;
+    const int nqt = (N + kRows - 1) / kRows;
+    int bh, qt;
+    bwd_task(blockIdx.x, nqt, a.B * a.H, bh, qt);
+    const int h = bh % a.H, b = bh / a.H, kvh = h / (a.H / a.Hkv);
+    const int q0 = qt * kRows, qw0 = q0 + 32 * wave, my_q = qw0 + n;
+    const uint16_t *kb = (const uint16_t *)a.k + (size_t)(b * a.Hkv + kvh) * N * D;
+    const uint16_t *vb = (const uint16_t *)a.v + (size_t)(b * a.Hkv + kvh) * N * D;
+    const size_t qrow = (size_t)bh * N + my_q;
+
+    const int kend = CAUSAL ? min(N, q0 + kRows) : N;
+    const int ntiles = (kend + kTile - 1) / kTile;
+    const int ntw = CAUSAL ? min(ntiles, (qw0 + 31) / kTile + 1) : ntiles;  // this wave's tiles
+
+    const TileLanes<D> tl = tile_lanes<D>(wave, lane);
+    auto kst = [&](int t) { return smem + (t & 1) * 2 * KB; };
+    auto vst = [&](int t) { return smem + (t & 1) * 2 * KB + KB; };
+    load_tile<D>(kst(0), kb, 0, N, wave, tl);
+    load_tile<D>(vst(0), vb, 0, N, wave, tl);
+
+    // Q^T and dO^T fragments (B operands): lane holds row my_q, columns 16ks + 8g .. +7
+    bf16x8 qf[KS], df[KS];
+    const bool valid_q = my_q < N;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        qf[ks] = as_bf16x8(valid_q ? ld16((const uint16_t *)a.q + qrow * D + 16 * ks + 8 * g)
+                                   : u32x4{0, 0, 0, 0});
+        df[ks] = as_bf16x8(valid_q ? ld16((const uint16_t *)a.dout + qrow * D + 16 * ks + 8 * g)
+                                   : u32x4{0, 0, 0, 0});
+    }
+    const float lse2 = valid_q ? a.lse2[qrow] : 0.f;
+    const float dlt = valid_q ? a.delta[qrow] : 0.f;
+    const float cs = a.scale * kLog2e;
+
+    f32x16 acc[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+        acc[c] = f32x16{};
+
+    for (int t = 0; t < ntiles; ++t) {
+        vm_wait_n<0>();
+        __syncthreads();  // tile t landed; stage (t+1)&1 no longer read
+        if (t + 1 < ntiles) {
+            load_tile<D>(kst(t + 1), kb, (t + 1) * kTile, N, wave, tl);
+            load_tile<D>(vst(t + 1), vb, (t + 1) * kTile, N, wave, tl);
+        }
+        if (t >= ntw)
+            continue;
+        const uint32_t ka = lds_addr(kst(t)), va = lds_addr(vst(t));
+        const uint32_t kd = direct_addr<D>(ka, 0, lane), vd = direct_addr<D>(va, 0, lane);
+        // S^T = K Q^T and dP^T = V dO^T: rows = keys 32 blk + 8(r/4) + 4g + r%4
+        f32x16 s[2], dp[2];
+        static_for<0, 2>([&](auto bc) {
+            constexpr int blk = decltype(bc)::value;
+            s[blk] = f32x16{};
+            dp[blk] = f32x16{};
+            static_for<0, KS>([&](auto kc) {
+                constexpr int ks = decltype(kc)::value;
+                constexpr int off = 32 * blk * BCfg<D>::kPitch + 32 * ks;
+                u32x4 x = lds_read_b128<off>(kd);
+                u32x4 y = lds_read_b128<off>(vd);
+                lgkm_wait<0>(x);
+                lgkm_wait<0>(y);
+                s[blk] = mfma_bf16_32x32x16(as_bf16x8(x), qf[ks], s[blk]);
+                dp[blk] = mfma_bf16_32x32x16(as_bf16x8(y), df[ks], dp[blk]);
+            });
+        });
+        // dS^T = P^T (dP^T - D), P^T = 2^(s cs - lse2), masked keys give 0
+        uint32_t dsw[2][8];
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            float ds[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = t * kTile + 32 * blk + 8 * (r >> 2) + 4 * g + (r & 3);
+                const bool ok = valid_q && key < N && (!CAUSAL || key <= my_q);
+                const float p = ok ? fast_exp2(s[blk][r] * cs - lse2) : 0.f;
+                ds[r] = p * (dp[blk][r] - dlt);
+            }
+            pack16(ds, dsw[blk]);
+        }
+        // dQ^T += K^T dS^T: contraction over the tile's keys, 16 per MFMA
+        const uint32_t kt = trans_addr<D>(ka, lane);
+        static_for<0, NC>([&](auto cc) {
+            constexpr int c = decltype(cc)::value;
+            static_for<0, 4>([&](auto uc) {
+                constexpr int u = decltype(uc)::value;  // keys 16u .. 16u+15
+                u32x4 x = trans_read<D, 16 * u, c>(kt);
+                lgkm_wait<0>(x);
+                const u32x4 w = {dsw[u >> 1][4 * (u & 1)], dsw[u >> 1][4 * (u & 1) + 1],
+                                 dsw[u >> 1][4 * (u & 1) + 2], dsw[u >> 1][4 * (u & 1) + 3]};
+                acc[c] = mfma_bf16_32x32x16(as_bf16x8(x), as_bf16x8(w), acc[c]);
+            });
+        });
+    }
+    if (valid_q)
+        store_rows<D, OUT_F32>(a.dq, qrow, g, acc, a.scale);
+}
+
+// ---------------------------------------------------------------- dK, dV
+// Workgroup: 128 keys of one (b, kv head); wave w owns keys k0 + 32w .. +31
+// (lane n is key k0 + 32w + n).  For each query head of the group, query
+// tiles of 64 (with their lse2 and D rows) stream through a 2-stage LDS ring.
+template <int D, bool CAUSAL, bool OUT_F32>
+__global__ __launch_bounds__(kBThreads) void bwd_dkv_kernel(BwdArgs a)
+{
+    constexpr int KB = BCfg<D>::kBytes, KS = D / 16, NC = D / 32;
+    constexpr int STAGE = 2 * KB + 2 * kTile * 4;  // Q, dO, lse2, D
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
+    const int lane = threadIdx.x & 63, g = lane >> 5, n = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int N = a.N;
+    const int G = a.H / a.Hkv;
+    const int nkt = (N + kRows - 1) / kRows;
+    int bg, kt;
+    bwd_task(blockIdx.x, nkt, a.B * a.Hkv, bg, kt);
+    const int b = bg / a.Hkv, g_kv = bg % a.Hkv;
+    const int k0 = kt * kRows, kw0 = k0 + 32 * wave, my_k = kw0 + n;
+    const bool valid_k = my_k < N;
+    const size_t krow = (size_t)bg * N + my_k;
+
+    // K and V fragments (B operands): lane holds row my_k, columns 16ks + 8g .. +7
+    bf16x8 kf[KS], vf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        kf[ks] = as_bf16x8(valid_k ? ld16((const uint16_t *)a.k + krow * D + 16 * ks + 8 * g)
+                                   : u32x4{0, 0, 0, 0});
+        vf[ks] = as_bf16x8(valid_k ? ld16((const uint16_t *)a.v + krow * D + 16 * ks + 8 * g)
+                                   : u32x4{0, 0, 0, 0});
+    }
+    const float cs = a.scale * kLog2e;
+    f32x16 dk[NC], dv[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        dk[c] = f32x16{};
+        dv[c] = f32x16{};
+    }
+
+    // the (head, query tile) sequence: for a causal mask the query tiles
+    // start at the tile holding this workgroup's first key
+    const int t0 = CAUSAL ? k0 / kTile : 0;
+    const int nqt = (N + kTile - 1) / kTile;
+    const int per_head = nqt - t0;
+    const int nsteps = G * per_head;
+    const TileLanes<D> tl = tile_lanes<D>(wave, lane);
+    auto stage = [&](int i) { return smem + (i & 1) * STAGE; };
+    auto load_step = [&](int i) {
+        const int hh = b * a.H + g_kv * G + i / per_head;
+        const int q0 = (t0 + i % per_head) * kTile;
+        unsigned char *st = stage(i);
+        load_tile<D>(st, (const uint16_t *)a.q + (size_t)hh * N * D, q0, N, wave, tl);
+        load_tile<D>(st + KB, (const uint16_t *)a.dout + (size_t)hh * N * D, q0, N, wave, tl);
+        const int rows = min(kTile, N - q0);
+        if (wave == 0)
+            dma4_rsrc(raw_rsrc(a.lse2 + (size_t)hh * N + q0, rows * 4), lane * 4, st + 2 * KB);
+        else if (wave == 1)
+            dma4_rsrc(raw_rsrc(a.delta + (size_t)hh * N + q0, rows * 4), lane * 4,
+                      st + 2 * KB + kTile * 4);
+    };
+    if (nsteps > 0)
+        load_step(0);
+    for (int i = 0; i < nsteps; ++i) {
+        vm_wait_n<0>();
+        __syncthreads();  // step i landed; stage (i+1)&1 no longer read
+        if (i + 1 < nsteps)
+            load_step(i + 1);
+        const int q0 = (t0 + i % per_head) * kTile;
+        unsigned char *st = stage(i);
+        const uint32_t qa = lds_addr(st), da = lds_addr(st + KB);
+        const float *lse_s = (const float *)(st + 2 * KB);
+        const float *dl_s = lse_s + kTile;
+        const uint32_t qt_a = trans_addr<D>(qa, lane), dt_a = trans_addr<D>(da, lane);
+        static_for<0, 2>([&](auto qc) {
+            constexpr int qs = decltype(qc)::value;  // queries q0 + 32 qs .. +31
+            // causal: skip when every query of the step precedes every key of the wave
+            if (CAUSAL && q0 + 32 * qs + 31 < kw0)
+                return;
+            // S = Q K^T and dP = dO V^T: rows = queries 32 qs + 8(r/4) + 4g + r%4
+            f32x16 s = f32x16{}, dp = f32x16{};
+            const uint32_t qd = direct_addr<D>(qa, 32 * qs, lane);
+            const uint32_t dd = direct_addr<D>(da, 32 * qs, lane);
+            static_for<0, KS>([&](auto kc) {
+                constexpr int ks = decltype(kc)::value;
+                u32x4 x = lds_read_b128<32 * ks>(qd);
+                u32x4 y = lds_read_b128<32 * ks>(dd);
+                lgkm_wait<0>(x);
+                lgkm_wait<0>(y);
+                s = mfma_bf16_32x32x16(as_bf16x8(x), kf[ks], s);
+                dp = mfma_bf16_32x32x16(as_bf16x8(y), vf[ks], dp);
+            });
+            float p[16], ds[16];
+#pragma unroll
+            for (int R = 0; R < 4; ++R) {
+                const int r0 = 32 * qs + 8 * R + 4 * g;
+                const f32x4 l4 = *(const f32x4 *)(lse_s + r0);
+                const f32x4 d4 = *(const f32x4 *)(dl_s + r0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * R + e, q = q0 + r0 + e;
+                    const bool ok = valid_k && q < N && (!CAUSAL || my_k <= q);
+                    p[r] = ok ? fast_exp2(s[r] * cs - l4[e]) : 0.f;
+                    ds[r] = p[r] * (dp[r] - d4[e]);
+                }
+            }
+            uint32_t pw[8], dsw[8];
+            pack16(p, pw);
+            pack16(ds, dsw);
+            // dV^T += dO^T P and dK^T += Q^T dS: contraction over the step's queries
+            static_for<0, NC>([&](auto cc) {
+                constexpr int c = decltype(cc)::value;
+                static_for<0, 2>([&](auto uc) {
+                    constexpr int u = decltype(uc)::value;
+                    u32x4 x = trans_read<D, 32 * qs + 16 * u, c>(dt_a);
+                    u32x4 y = trans_read<D, 32 * qs + 16 * u, c>(qt_a);
+                    lgkm_wait<0>(x);
+                    lgkm_wait<0>(y);
+                    const u32x4 wp = {pw[4 * u], pw[4 * u + 1], pw[4 * u + 2], pw[4 * u + 3]};
+                    const u32x4 wd = {dsw[4 * u], dsw[4 * u + 1], dsw[4 * u + 2], dsw[4 * u + 3]};
+                    dv[c] = mfma_bf16_32x32x16(as_bf16x8(x), as_bf16x8(wp), dv[c]);
+                    dk[c] = mfma_bf16_32x32x16(as_bf16x8(y), as_bf16x8(wd), dk[c]);
+                });
+            });
+        });
+    }
+    if (valid_k) {
+        store_rows<D, OUT_F32>(a.dk, krow, g, dk, a.scale);
+        store_rows<D, OUT_F32>(a.dv, krow, g, dv, 1.f);
+    }
+}
+
+template <int D, bool CAUSAL, bool OUT_F32>
+hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s)
+{
+    {
+        constexpr int rows_per_block = 256 / (D / 8);
+        const long long nrows = (long long)a.B * a.H * a.N;
+        ProfScope ps("bwd_delta", s);
+        hipLaunchKernelGGL((bwd_delta_kernel<D>),
+                           dim3((unsigned)((nrows + rows_per_block - 1) / rows_per_block)),
+                           dim3(256), 0, s, a);
+    }
+    const int nt = (a.N + kRows - 1) / kRows;
+    {
+        ProfScope ps("bwd_dq", s);
+        hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, OUT_F32>), dim3(a.B * a.H * nt),
+                           dim3(kBThreads), 0, s, a);
+    }
+    ProfScope ps("bwd_dkv", s);
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, CAUSAL, OUT_F32>), dim3(a.B * a.Hkv * nt),
+                       dim3(kBThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_bwd_d(const BwdArgs &a, hipStream_t s)
+{
+    if (a.causal)
+        return a.out_fp32 ? launch_bwd_t<D, true, true>(a, s) : launch_bwd_t<D, true, false>(a, s);
+    return a.out_fp32 ? launch_bwd_t<D, false, true>(a, s) : launch_bwd_t<D, false, false>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdArgs &a, hipStream_t s)
+{
+    return a.d == 64 ? launch_bwd_d<64>(a, s) : launch_bwd_d<128>(a, s);
+}
+
+}  // namespace attn

@@ -188,6 +188,14 @@ __device__ __forceinline__ void dma16_rsrc(__amdgpu_buffer_rsrc_t r, uint32_t vo
                                              voff, 0, 0, 0);
 }
 
+// 4-byte direct load through a buffer resource into LDS: lane l's bytes
+// [voff, voff + 4) land at lds + 4 * l (lds wave-uniform).
+__device__ __forceinline__ void dma4_rsrc(__amdgpu_buffer_rsrc_t r, uint32_t voff, void *lds)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 4,
+                                             voff, 0, 0, 0);
+}
+
 // Wait until at most N vector-memory operations of this wave are outstanding.
 template <int N>
 __device__ __forceinline__ void vm_wait_n()

@@ -82,6 +82,29 @@ def test_fwd_varlen_validation(A, kw, status):
     assert A.attn_last_error() != ""
 
 
+def _bwd(A, **kw):
+    args = dict(q=P, k=P, v=P, o=P, lse=P, dout=P, dq=P, dk=P, dv=P, B=1, H=4, Hkv=2, N=16,
+                d=128, causal=1, scale=0.1, grad_dtype=0, workspace=P, workspace_bytes=1 << 20,
+                stream=None)
+    args.update(kw)
+    return A.attn_bwd(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(lse=None), -1), (dict(dout=None), -1), (dict(dk=None), -1), (dict(B=0), -1),
+    (dict(N=0), -1), (dict(H=3), -1), (dict(scale=-2.0), -1), (dict(grad_dtype=5), -1),
+    (dict(d=32), -2), (dict(workspace=None), -3), (dict(workspace_bytes=10), -3),
+])
+def test_bwd_validation(A, kw, status):
+    assert _bwd(A, **kw) == status
+    assert A.attn_last_error() != ""
+
+
+def test_bwd_workspace_size(A):
+    assert A.attn_bwd_workspace_size(2, 4, 100) == 2 * (((4 * 2 * 4 * 100) + 255) // 256 * 256)
+    assert A.attn_bwd_workspace_size(0, 4, 100) == 0
+
+
 def _dec(A, **kw):
     args = dict(q=P, k_cache=P, v_cache=P, seqlens=P, o=P, lse=None, B=2, H=8, Hkv=2,
                 N_max=1024, d=128, scale=0.1, mode=0, o_dtype=0, split_tokens=512,
