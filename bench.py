@@ -9,12 +9,12 @@ the same timed region for the roofline figure.
 
 The same JSON line also carries the split-KV decode workload (HBM bound,
 GB/s; contiguous caches, and the same caches spread over a pool of 16-row
-pages), a packed batch of variable-length sequences, and the quantised
-prefill workload, each with its own roofline object,
+pages), the backward of the headline workload, a packed batch of
+variable-length sequences, and the quantised prefill workload, each with its own roofline object,
 and the fp64 CPU oracle timed on a bounded sample of the headline workload.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                  [--only prefill|varlen|decode|sage] [--calibrate-copy]
+                  [--only prefill|bwd|varlen|decode|sage] [--calibrate-copy]
 """
 from __future__ import annotations
 
@@ -112,6 +112,42 @@ def bench_prefill(args, stream):
         "inputs": (inp["q"], inp["k"], inp["v"]),
     }
     return res
+
+
+def bench_bwd(args, stream):
+    """Backward of the headline workload: dQ, dK, dV for a random dO, with O
+    and LSE from the forward (outside the timed region)."""
+    import softmax_attention_attn_amd as A
+    w = workloads.WORKLOADS["llm_prefill"]
+    inp = workloads.make(w)
+    q, k, v = inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda()
+    do = workloads.make_prefill(w.B, w.H, w.Hkv, w.N, w.d, seed=1)[0].cuda()
+    o, lse = A.fwd(q, k, v, causal=w.causal)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    ws = torch.empty((A.attn_bwd_workspace_size(w.B, w.H, w.N),), dtype=torch.uint8,
+                     device="cuda")
+
+    def step():
+        A.bwd(q, k, v, o, lse, do, causal=w.causal, dq=dq, dk=dk, dv=dv, workspace=ws,
+              stream=stream)
+
+    ms, per_kernel = time_calls(step, args.steps, args.warmup, stream)
+    # five products of the forward's size (S, dP, dV, dK, dQ): 2.5x the
+    # forward's FLOPs; the recomputation of S and dP in the dQ kernel is not
+    # counted
+    flops = 2.5 * w.flops()
+    kms = sum(t for t, _ in per_kernel.values())
+    achieved = flops / (kms * 1e-3) / 1e12
+    return {
+        "workload": w.name + "_bwd", "value": flops / (ms * 1e-3) / 1e12, "unit": "TFLOP/s",
+        "ms_per_step": ms, "flops": flops,
+        "kernels_ms": {k_: t for k_, (t, _) in per_kernel.items()},
+        "roofline": {"bound": "mfma", "kernel": "bwd_delta + bwd_dq + bwd_dkv",
+                     "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "kernel_ms": kms, "traffic": None},
+    }
 
 
 def bench_varlen(args, stream):
@@ -268,7 +304,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "varlen", "decode", "sage"], default=None)
+    ap.add_argument("--only", choices=["prefill", "bwd", "varlen", "decode", "sage"],
+                    default=None)
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -288,6 +325,12 @@ def main():
         log("prefill: llm_prefill")
         pre = bench_prefill(args, stream)
         log("prefill %.3f ms/step, %.1f TFLOP/s" % (pre["ms_per_step"], pre["value"]))
+    if args.only in (None, "bwd"):
+        log("bwd: llm_prefill backward")
+        bw = bench_bwd(args, stream)
+        log("bwd %.3f ms/step, %.1f TFLOP/s" % (bw["ms_per_step"], bw["value"]))
+        out["bwd"] = bw
+        torch.cuda.empty_cache()
     if args.only in (None, "varlen"):
         log("varlen: varlen_prefill")
         vl = bench_varlen(args, stream)

@@ -163,6 +163,32 @@ __device__ __forceinline__ void bwd_task(int wg, int ntile, int nouter, int &out
     }
 }
 
+// N products, each taking two LDS operands read by rd(i) (OPS read
+// instructions in all); the reads run RA products ahead of the MFMAs.
+template <int N, int RA, int OPS, class Rd, class Use>
+__device__ __forceinline__ void operand_stream(Rd &&rd, Use &&use)
+{
+    static_assert(OPS * RA <= 15, "lgkmcnt field");
+    u32x4 x[RA + 1], y[RA + 1];
+    static_for<0, (RA < N ? RA : N)>([&](auto i) {
+        constexpr int I = decltype(i)::value;
+        rd(i, x[I % (RA + 1)], y[I % (RA + 1)]);
+    });
+    static_for<0, N>([&](auto i) {
+        constexpr int I = decltype(i)::value, B = I % (RA + 1);
+        if constexpr (I + RA < N) {
+            rd(std::integral_constant<int, I + RA>{}, x[(I + RA) % (RA + 1)],
+               y[(I + RA) % (RA + 1)]);
+            lgkm_wait<OPS * RA>(x[B]);
+            lgkm_wait<OPS * RA>(y[B]);
+        } else {
+            lgkm_wait<OPS * (N - 1 - I)>(x[B]);
+            lgkm_wait<OPS * (N - 1 - I)>(y[B]);
+        }
+        use(i, x[B], y[B]);
+    });
+}
+
 // ---------------------------------------------------------------- D, lse2
 // One 16-lane group per row: D = dO . O (fp32), lse2 = lse * log2(e).
 template <int D>
@@ -253,22 +279,21 @@ __global__ __launch_bounds__(kBThreads) void bwd_dq_kernel(BwdArgs a)
         const uint32_t ka = lds_addr(kst(t)), va = lds_addr(vst(t));
         const uint32_t kd = direct_addr<D>(ka, 0, lane), vd = direct_addr<D>(va, 0, lane);
         // S^T = K Q^T and dP^T = V dO^T: rows = keys 32 blk + 8(r/4) + 4g + r%4
-        f32x16 s[2], dp[2];
-        static_for<0, 2>([&](auto bc) {
-            constexpr int blk = decltype(bc)::value;
-            s[blk] = f32x16{};
-            dp[blk] = f32x16{};
-            static_for<0, KS>([&](auto kc) {
-                constexpr int ks = decltype(kc)::value;
-                constexpr int off = 32 * blk * BCfg<D>::kPitch + 32 * ks;
-                u32x4 x = lds_read_b128<off>(kd);
-                u32x4 y = lds_read_b128<off>(vd);
-                lgkm_wait<0>(x);
-                lgkm_wait<0>(y);
-                s[blk] = mfma_bf16_32x32x16(as_bf16x8(x), qf[ks], s[blk]);
-                dp[blk] = mfma_bf16_32x32x16(as_bf16x8(y), df[ks], dp[blk]);
+        f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+        // product i: block i % 2 (alternating accumulators), k-step i / 2;
+        // two products of read-ahead keep two waves per SIMD within 256 registers
+        operand_stream<2 * KS, 2, 2>(
+            [&](auto i, u32x4 &x, u32x4 &y) {
+                constexpr int I = decltype(i)::value;
+                constexpr int off = 32 * (I % 2) * BCfg<D>::kPitch + 32 * (I / 2);
+                x = lds_read_b128<off>(kd);
+                y = lds_read_b128<off>(vd);
+            },
+            [&](auto i, const u32x4 &x, const u32x4 &y) {
+                constexpr int I = decltype(i)::value;
+                s[I % 2] = mfma_bf16_32x32x16(as_bf16x8(x), qf[I / 2], s[I % 2]);
+                dp[I % 2] = mfma_bf16_32x32x16(as_bf16x8(y), df[I / 2], dp[I % 2]);
             });
-        });
         // dS^T = P^T (dP^T - D), P^T = 2^(s cs - lse2), masked keys give 0
         uint32_t dsw[2][8];
 #pragma unroll
@@ -285,17 +310,22 @@ __global__ __launch_bounds__(kBThreads) void bwd_dq_kernel(BwdArgs a)
         }
         // dQ^T += K^T dS^T: contraction over the tile's keys, 16 per MFMA
         const uint32_t kt = trans_addr<D>(ka, lane);
-        static_for<0, NC>([&](auto cc) {
-            constexpr int c = decltype(cc)::value;
-            static_for<0, 4>([&](auto uc) {
-                constexpr int u = decltype(uc)::value;  // keys 16u .. 16u+15
-                u32x4 x = trans_read<D, 16 * u, c>(kt);
-                lgkm_wait<0>(x);
+        // product pair i: keys 16u .. 16u+15 (u = i / (NC/2)) into the
+        // feature blocks c0 = 2(i % (NC/2)) and c0 + 1, so that consecutive
+        // MFMAs accumulate into different blocks
+        operand_stream<2 * NC, 2, 4>(
+            [&](auto i, u32x4 &x, u32x4 &y) {
+                constexpr int I = decltype(i)::value, u = I / (NC / 2), c0 = 2 * (I % (NC / 2));
+                x = trans_read<D, 16 * u, c0>(kt);
+                y = trans_read<D, 16 * u, c0 + 1>(kt);
+            },
+            [&](auto i, const u32x4 &x, const u32x4 &y) {
+                constexpr int I = decltype(i)::value, u = I / (NC / 2), c0 = 2 * (I % (NC / 2));
                 const u32x4 w = {dsw[u >> 1][4 * (u & 1)], dsw[u >> 1][4 * (u & 1) + 1],
                                  dsw[u >> 1][4 * (u & 1) + 2], dsw[u >> 1][4 * (u & 1) + 3]};
-                acc[c] = mfma_bf16_32x32x16(as_bf16x8(x), as_bf16x8(w), acc[c]);
+                acc[c0] = mfma_bf16_32x32x16(as_bf16x8(x), as_bf16x8(w), acc[c0]);
+                acc[c0 + 1] = mfma_bf16_32x32x16(as_bf16x8(y), as_bf16x8(w), acc[c0 + 1]);
             });
-        });
     }
     if (valid_q)
         store_rows<D, OUT_F32>(a.dq, qrow, g, acc, a.scale);
@@ -383,15 +413,17 @@ __global__ __launch_bounds__(kBThreads) void bwd_dkv_kernel(BwdArgs a)
             f32x16 s = f32x16{}, dp = f32x16{};
             const uint32_t qd = direct_addr<D>(qa, 32 * qs, lane);
             const uint32_t dd = direct_addr<D>(da, 32 * qs, lane);
-            static_for<0, KS>([&](auto kc) {
-                constexpr int ks = decltype(kc)::value;
-                u32x4 x = lds_read_b128<32 * ks>(qd);
-                u32x4 y = lds_read_b128<32 * ks>(dd);
-                lgkm_wait<0>(x);
-                lgkm_wait<0>(y);
-                s = mfma_bf16_32x32x16(as_bf16x8(x), kf[ks], s);
-                dp = mfma_bf16_32x32x16(as_bf16x8(y), vf[ks], dp);
-            });
+            operand_stream<KS, 3, 2>(
+                [&](auto i, u32x4 &x, u32x4 &y) {
+                    constexpr int ks = decltype(i)::value;
+                    x = lds_read_b128<32 * ks>(qd);
+                    y = lds_read_b128<32 * ks>(dd);
+                },
+                [&](auto i, const u32x4 &x, const u32x4 &y) {
+                    constexpr int ks = decltype(i)::value;
+                    s = mfma_bf16_32x32x16(as_bf16x8(x), kf[ks], s);
+                    dp = mfma_bf16_32x32x16(as_bf16x8(y), vf[ks], dp);
+                });
             float p[16], ds[16];
 #pragma unroll
             for (int R = 0; R < 4; ++R) {
@@ -410,20 +442,22 @@ __global__ __launch_bounds__(kBThreads) void bwd_dkv_kernel(BwdArgs a)
             pack16(p, pw);
             pack16(ds, dsw);
             // dV^T += dO^T P and dK^T += Q^T dS: contraction over the step's queries
-            static_for<0, NC>([&](auto cc) {
-                constexpr int c = decltype(cc)::value;
-                static_for<0, 2>([&](auto uc) {
-                    constexpr int u = decltype(uc)::value;
-                    u32x4 x = trans_read<D, 32 * qs + 16 * u, c>(dt_a);
-                    u32x4 y = trans_read<D, 32 * qs + 16 * u, c>(qt_a);
-                    lgkm_wait<0>(x);
-                    lgkm_wait<0>(y);
+            // product pair i: queries 16u .. 16u+15 of the step (u = i / NC),
+            // feature block c = i % NC (consecutive pairs use different blocks)
+            operand_stream<2 * NC, 3, 4>(
+                [&](auto i, u32x4 &x, u32x4 &y) {
+                    constexpr int I = decltype(i)::value, c = I % NC, u = I / NC;
+                    x = trans_read<D, 32 * qs + 16 * u, c>(dt_a);
+                    y = trans_read<D, 32 * qs + 16 * u, c>(qt_a);
+                },
+                [&](auto i, const u32x4 &x, const u32x4 &y) {
+                    constexpr int I = decltype(i)::value, c = I % NC, u = I / NC;
                     const u32x4 wp = {pw[4 * u], pw[4 * u + 1], pw[4 * u + 2], pw[4 * u + 3]};
-                    const u32x4 wd = {dsw[4 * u], dsw[4 * u + 1], dsw[4 * u + 2], dsw[4 * u + 3]};
+                    const u32x4 wd = {dsw[4 * u], dsw[4 * u + 1], dsw[4 * u + 2],
+                                      dsw[4 * u + 3]};
                     dv[c] = mfma_bf16_32x32x16(as_bf16x8(x), as_bf16x8(wp), dv[c]);
                     dk[c] = mfma_bf16_32x32x16(as_bf16x8(y), as_bf16x8(wd), dk[c]);
                 });
-            });
         });
     }
     if (valid_k) {
