@@ -304,7 +304,7 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void decode_split_kernel(DecodeAr
 
 // One wave per (sequence, query head): lanes take the chunk LSEs 64 at a
 // time for the max and the weight sum, then each lane accumulates D/64
-// features over the chunks, sixteen chunk rows in flight.
+// features over the chunks, with the rows of 64 chunks in flight at once.
 constexpr int kMergeWaves = 4;
 
 template <int D, bool OUT_F32>
@@ -332,42 +332,20 @@ __global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(DecodeAr
         const float w = s0 + lane < ns ? fast_exp2(pl[s0 + lane] - M) : 0.f;
         wsum += w;
         const int n = min(64, ns - s0);
-        int j = 0;
-        for (; j + 16 <= n; j += 16) {
-            float x[16][F];
+        // all 64 chunk rows of the batch in flight at once (rows past the
+        // last chunk re-read it and carry weight 0)
+        float x[64][F];
 #pragma unroll
-            for (int u = 0; u < 16; ++u)
-#pragma unroll
-                for (int f = 0; f < F; ++f)
-                    x[u][f] = po[(size_t)(s0 + j + u) * D + f];
-#pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                const float wu = __shfl(w, j + u, 64);
-#pragma unroll
-                for (int f = 0; f < F; ++f)
-                    acc[f] = fmaf(wu, x[u][f], acc[f]);
-            }
-        }
-        for (; j + 4 <= n; j += 4) {
-            float x[4][F];
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-                for (int f = 0; f < F; ++f)
-                    x[u][f] = po[(size_t)(s0 + j + u) * D + f];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float wu = __shfl(w, j + u, 64);
-#pragma unroll
-                for (int f = 0; f < F; ++f)
-                    acc[f] = fmaf(wu, x[u][f], acc[f]);
-            }
-        }
-        for (; j < n; ++j) {
-            const float wu = __shfl(w, j, 64);
+        for (int j = 0; j < 64; ++j)
 #pragma unroll
             for (int f = 0; f < F; ++f)
-                acc[f] = fmaf(wu, po[(size_t)(s0 + j) * D + f], acc[f]);
+                x[j][f] = po[(size_t)(s0 + min(j, n - 1)) * D + f];
+#pragma unroll
+        for (int j = 0; j < 64; ++j) {
+            const float wj = __shfl(w, j, 64);
+#pragma unroll
+            for (int f = 0; f < F; ++f)
+                acc[f] = fmaf(wj, x[j][f], acc[f]);
         }
     }
 #pragma unroll
