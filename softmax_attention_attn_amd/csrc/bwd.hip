@@ -335,8 +335,13 @@ __global__ __launch_bounds__(kBThreads) void bwd_dq_kernel(BwdArgs a)
 // Workgroup: 128 keys of one (b, kv head); wave w owns keys k0 + 32w .. +31
 // (lane n is key k0 + 32w + n).  For each query head of the group, query
 // tiles of 64 (with their lse2 and D rows) stream through a 2-stage LDS ring.
+// Two waves per SIMD (two workgroups per CU; 70 KB of LDS each): the
+// register budget of 256 then holds the dK/dV accumulators (128), the K/V
+// fragments (64) and one product of operand read-ahead, with a few values
+// spilled outside the inner loop; the second wave hides the LDS latency and
+// the score arithmetic, which the read-ahead of a single wave did not.
 template <int D, bool CAUSAL, bool OUT_F32>
-__global__ __launch_bounds__(kBThreads) void bwd_dkv_kernel(BwdArgs a)
+__global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkv_kernel(BwdArgs a)
 {
     constexpr int KB = BCfg<D>::kBytes, KS = D / 16, NC = D / 32;
     constexpr int STAGE = 2 * KB + 2 * kTile * 4;  // Q, dO, lse2, D
@@ -413,7 +418,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_dkv_kernel(BwdArgs a)
             f32x16 s = f32x16{}, dp = f32x16{};
             const uint32_t qd = direct_addr<D>(qa, 32 * qs, lane);
             const uint32_t dd = direct_addr<D>(da, 32 * qs, lane);
-            operand_stream<KS, 3, 2>(
+            operand_stream<KS, 1, 2>(
                 [&](auto i, u32x4 &x, u32x4 &y) {
                     constexpr int ks = decltype(i)::value;
                     x = lds_read_b128<32 * ks>(qd);
@@ -444,7 +449,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_dkv_kernel(BwdArgs a)
             // dV^T += dO^T P and dK^T += Q^T dS: contraction over the step's queries
             // product pair i: queries 16u .. 16u+15 of the step (u = i / NC),
             // feature block c = i % NC (consecutive pairs use different blocks)
-            operand_stream<2 * NC, 3, 4>(
+            operand_stream<2 * NC, 1, 4>(
                 [&](auto i, u32x4 &x, u32x4 &y) {
                     constexpr int I = decltype(i)::value, c = I % NC, u = I / NC;
                     x = trans_read<D, 32 * qs + 16 * u, c>(dt_a);
