@@ -593,7 +593,10 @@ __device__ __forceinline__ int s_step(SState<D> &st, const i32x4 (&qf)[D / 32], 
     return imx0 > imx1 ? imx0 : imx1;
 }
 
-template <int D, bool CAUSAL, bool OUT_F32>
+// TAIL: some key tile runs past N (N not a multiple of 64); without it and
+// without a causal mask no tile is masked, and the per-score mask tests of
+// the exponentials compile away.
+template <int D, bool CAUSAL, bool OUT_F32, bool TAIL>
 __device__ __forceinline__ void sage_qtile(const PrefillArgs &a, const SageWs &w,
                                            unsigned char *smem, int bh, int qt, int wave, int lane)
 {
@@ -613,7 +616,7 @@ __device__ __forceinline__ void sage_qtile(const PrefillArgs &a, const SageWs &w
     auto vst = [&](int t) { return smem + 4 * kK + (t & 3) * kV; };
     auto needs_mask = [&](int t) {
         const int k0 = t * kBlk;
-        return (CAUSAL && k0 + kBlk - 1 > qw0) || k0 + kBlk > N;
+        return (CAUSAL && k0 + kBlk - 1 > qw0) || (TAIL && k0 + kBlk > N);
     };
     // direct loads: one 1 KB piece of each tile per wave (waves beyond the
     // piece count load nothing); the V^^T tile's rows are Npad bytes apart
@@ -785,7 +788,7 @@ __device__ __forceinline__ void sage_qtile(const PrefillArgs &a, const SageWs &w
     }
 }
 
-template <int D, bool CAUSAL, bool OUT_F32>
+template <int D, bool CAUSAL, bool OUT_F32, bool TAIL>
 __global__ __launch_bounds__(kAThreads) void sage_attn_kernel(PrefillArgs a, SageWs w)
 {
     __shared__ __attribute__((aligned(1024)))
@@ -807,13 +810,13 @@ __global__ __launch_bounds__(kAThreads) void sage_attn_kernel(PrefillArgs a, Sag
         j = wg % nw;
     }
     if (CAUSAL) {
-        sage_qtile<D, CAUSAL, OUT_F32>(a, w, smem, bh, nqt - 1 - j, wave, lane);
+        sage_qtile<D, CAUSAL, OUT_F32, TAIL>(a, w, smem, bh, nqt - 1 - j, wave, lane);
         if (j < nqt - 1 - j) {
             __syncthreads();  // every wave is done with the LDS stages
-            sage_qtile<D, CAUSAL, OUT_F32>(a, w, smem, bh, j, wave, lane);
+            sage_qtile<D, CAUSAL, OUT_F32, TAIL>(a, w, smem, bh, j, wave, lane);
         }
     } else {
-        sage_qtile<D, CAUSAL, OUT_F32>(a, w, smem, bh, j, wave, lane);
+        sage_qtile<D, CAUSAL, OUT_F32, TAIL>(a, w, smem, bh, j, wave, lane);
     }
 }
 
@@ -849,16 +852,23 @@ hipError_t launch_d(const SageArgs &sa, hipStream_t s)
     const int nqt = (a.N + kBM - 1) / kBM;
     ProfScope ps("sage_attn", s);
     dim3 grid(BH * (a.causal ? (nqt + 1) / 2 : nqt)), block(kAThreads);
+    const bool tail = a.N % kBlk != 0;
     if (a.causal) {
         if (a.out_fp32)
-            hipLaunchKernelGGL((sage_attn_kernel<D, true, true>), grid, block, 0, s, a, w);
+            hipLaunchKernelGGL((sage_attn_kernel<D, true, true, true>), grid, block, 0, s, a, w);
         else
-            hipLaunchKernelGGL((sage_attn_kernel<D, true, false>), grid, block, 0, s, a, w);
+            hipLaunchKernelGGL((sage_attn_kernel<D, true, false, true>), grid, block, 0, s, a, w);
+    } else if (tail) {
+        if (a.out_fp32)
+            hipLaunchKernelGGL((sage_attn_kernel<D, false, true, true>), grid, block, 0, s, a, w);
+        else
+            hipLaunchKernelGGL((sage_attn_kernel<D, false, false, true>), grid, block, 0, s, a, w);
     } else {
         if (a.out_fp32)
-            hipLaunchKernelGGL((sage_attn_kernel<D, false, true>), grid, block, 0, s, a, w);
+            hipLaunchKernelGGL((sage_attn_kernel<D, false, true, false>), grid, block, 0, s, a, w);
         else
-            hipLaunchKernelGGL((sage_attn_kernel<D, false, false>), grid, block, 0, s, a, w);
+            hipLaunchKernelGGL((sage_attn_kernel<D, false, false, false>), grid, block, 0, s, a,
+                               w);
     }
     return hipGetLastError();
 }

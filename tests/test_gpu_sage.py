@@ -55,6 +55,7 @@ def _check_vs_emulator(o, lse, o_emu, lse_emu, what):
 CASES = [
     # B, H, Hkv, N, d, causal
     (1, 2, 2, 64, 128, False),
+    (1, 4, 2, 384, 64, False),   # N a multiple of the key tile: the no-mask instantiation
     (1, 2, 1, 200, 128, False),
     (2, 4, 2, 300, 64, False),
     (1, 2, 2, 257, 128, True),
