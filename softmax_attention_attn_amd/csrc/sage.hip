@@ -521,7 +521,6 @@ __device__ __forceinline__ int s_step(SState<D> &st, const i32x4 (&qf)[D / 32], 
     };
     float p[32];
     float rs0 = 0.f, rs1 = 0.f;
-    uint32_t wd = 0;
     int imx0 = INT_MIN, imx1 = INT_MIN;
     s_qk[0] = i32x16{};
     s_qk[1] = i32x16{};
@@ -532,16 +531,17 @@ __device__ __forceinline__ int s_step(SState<D> &st, const i32x4 (&qf)[D / 32], 
             rs0 += p[R];
         } else {
             rs1 += p[R];
-            constexpr int blk = R / 16, r = R % 16;
+            constexpr int blk = R / 16, r = R % 16, w = 4 * blk + r / 4;
+            // the pair goes straight into its word of P: low half, then high half
             if constexpr ((r & 3) == 1) {
-                wd = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(p[R - 1], p[R], 0, false);
+                p_next[w] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(p[R - 1], p[R], 0, false);
             } else {
-                wd = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(p[R - 1], p[R], (int)wd, true);
-                p_next[4 * blk + r / 4] = wd;
-                asm volatile("" : "+v"(p_next[4 * blk + r / 4]));
+                p_next[w] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(p[R - 1], p[R],
+                                                                      (int)p_next[w], true);
             }
+            asm volatile("" : "+v"(p_next[w]));
         }
-        asm volatile("" : "+v"(rs0), "+v"(rs1), "+v"(wd));
+        asm volatile("" : "+v"(rs0), "+v"(rs1));
     };
     static_for<0, RA>([&](auto i) { read_op(i); });
     static_for<0, NS>([&](auto sc) {
