@@ -221,8 +221,11 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a)
 // (lane n = l % 32 is query q0 + 32w + n).  Key tiles of 64 stream through a
 // 2-stage LDS ring (K and V, padded rows), loaded by direct loads one step
 // ahead; the workgroup synchronises once per step.
+// Compiled for two waves per SIMD: without the bound the compiler kept the
+// dQ accumulators in AGPRs and copied them to VGPRs and back around every
+// tile (128 extra VALU moves per tile).
 template <int D, bool CAUSAL, bool OUT_F32>
-__global__ __launch_bounds__(kBThreads) void bwd_dq_kernel(BwdArgs a)
+__global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(BwdArgs a)
 {
     constexpr int KB = BCfg<D>::kBytes, KS = D / 16, NC = D / 32;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * KB];
