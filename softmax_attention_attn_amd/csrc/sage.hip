@@ -43,6 +43,41 @@ constexpr int kNCh = 16;   // sequence chunks of the statistics pass
 constexpr int kThreads = 256;
 constexpr float kLog2_448 = 8.807354922057604f;
 
+// Biased integer scores.  Every QK accumulator starts at the bit pattern of
+// the float 1.5 * 2^23 instead of zero.  A score is at most 128 * 127^2 <
+// 2^22 in magnitude, so the int32 result stays inside that float's binade and
+// its bits read as the float 1.5 * 2^23 + s exactly: the scaled exponent
+// c * s + bias is then one FMA on the raw bits, c * bits + (bias - 1.5 * 2^23
+// * c), with no int-to-float conversion.  Signed integer order of the biased
+// scores is still score order (all of them are positive ints).  A masked score
+// is set to the bits of -inf, a negative int below every real score, and its
+// exponent c * (-inf) + bias' is -inf, so p = 0 with no per-score test.
+constexpr int kSBias = 0x4B400000;       // bits of 12582912.0f = 1.5 * 2^23
+constexpr float kSBiasF = 12582912.f;
+constexpr int kSMasked = (int)0xFF800000u;  // bits of -inf
+
+// The bias block is built once per query tile and kept in registers (the
+// empty asm hides its value), so the first MFMA of every score block reads it
+// as its accumulator input instead of a fresh copy being made each tile.
+__device__ __forceinline__ i32x16 sbias16()
+{
+    i32x16 v;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        v[r] = kSBias;
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+// the lane's biased integer max in log2 units (-inf when every key is masked)
+__device__ __forceinline__ float smax_log2(int imx, float c)
+{
+    return imx < 0 ? -INFINITY : (__int_as_float(imx) - kSBiasF) * c;
+}
+
+// the per-tile constant of the exponent for biased scores
+__device__ __forceinline__ float sbias_exp(float bias, float c) { return fmaf(-kSBiasF, c, bias); }
+
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 struct SageWs {
@@ -387,23 +422,21 @@ __device__ __forceinline__ SDma<D> s_dma(int wave, int lane, int Npad)
 // S^T = K^ Q^^T for one tile, unpipelined (the first two tiles of a query tile).
 template <int D>
 __device__ __forceinline__ void qk_tile_i8(i32x16 (&s)[2], const i32x4 (&qf)[D / 32], uint32_t kst,
-                                           const SLanes<D> &ln)
+                                           const SLanes<D> &ln, const i32x16 &sbias)
 {
-    s[0] = i32x16{};
-    s[1] = i32x16{};
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
         u32x4 a0 = lds_read_b128<0>(kst + ln.k[ks]);
         u32x4 a1 = lds_read_b128<32 * D>(kst + ln.k[ks]);
         lgkm_wait<1>(a0);
-        s[0] = mfma_i8_32x32x32(__builtin_bit_cast(i32x4, a0), qf[ks], s[0]);
+        s[0] = mfma_i8_32x32x32(__builtin_bit_cast(i32x4, a0), qf[ks], ks ? s[0] : sbias);
         lgkm_wait<0>(a1);
-        s[1] = mfma_i8_32x32x32(__builtin_bit_cast(i32x4, a1), qf[ks], s[1]);
+        s[1] = mfma_i8_32x32x32(__builtin_bit_cast(i32x4, a1), qf[ks], ks ? s[1] : sbias);
     }
 }
 
 // Masked keys of a score tile (past the sequence end, or above the causal
-// diagonal) become INT_MIN; a real score is at most 128 * 127^2 in magnitude.
+// diagonal) become kSMasked.
 template <bool CAUSAL>
 __device__ __forceinline__ void mask_i8(i32x16 (&s)[2], int k0, int N, int g, int my_q)
 {
@@ -413,7 +446,7 @@ __device__ __forceinline__ void mask_i8(i32x16 (&s)[2], int k0, int N, int g, in
         for (int r = 0; r < 16; ++r) {
             const int key = k0 + 32 * blk + 16 * g + r;
             if (key >= N || (CAUSAL && key > my_q))
-                s[blk][r] = INT_MIN;
+                s[blk][r] = kSMasked;
         }
 }
 
@@ -468,9 +501,10 @@ __device__ __forceinline__ void s_apply_pending(SState<D> &st)
 
 // p = 448 * 2^(c * s + log2(448) - m - log2(448)) for the whole tile, E4M3-packed
 // (byte 16*blk + r of the lane = score s[blk][r]); returns the lane's row sum.
-__device__ __forceinline__ float s_exp_tile(const i32x16 (&s)[2], float c, float bias, bool masked,
+__device__ __forceinline__ float s_exp_tile(const i32x16 (&s)[2], float c, float bias,
                                             uint32_t (&pk)[8])
 {
+    const float b = sbias_exp(bias, c);
     float rs = 0.f;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
@@ -479,8 +513,10 @@ __device__ __forceinline__ float s_exp_tile(const i32x16 (&s)[2], float c, float
             float p[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
+                // (the element goes through a scalar: a bit cast of a vector
+                // element itself compiles to a read of element 0)
                 const int v = s[blk][r + e];
-                p[e] = fast_exp2(masked && v == INT_MIN ? -INFINITY : fmaf((float)v, c, bias));
+                p[e] = fast_exp2(fmaf(__int_as_float(v), c, b));
                 rs += p[e];
             }
             int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
@@ -499,13 +535,13 @@ template <int D, bool CAUSAL, class Dma>
 __device__ __forceinline__ int s_step(SState<D> &st, const i32x4 (&qf)[D / 32], uint32_t kst,
                                       uint32_t vst, const SLanes<D> &ln, const i32x16 (&s_exp)[2],
                                       i32x16 (&s_qk)[2], const uint32_t (&p_cur)[8],
-                                      uint32_t (&p_next)[8], float c_exp, bool mask_exp,
-                                      bool mask_qk, int k0_qk, int N, int g, int my_q,
+                                      uint32_t (&p_next)[8], float c_exp, bool mask_qk, int k0_qk,
+                                      int N, int g, int my_q, const i32x16 &sbias,
                                       const Dma &dma)
 {
     using SC = SSched<D>;
     constexpr int NS = SC::NS, NQK = SC::NQK, RA = SC::RA;
-    const float bias = kLog2_448 - st.m;
+    const float bexp = sbias_exp(kLog2_448 - st.m, c_exp);
     // operand of slot S: u32x4 for QK, two of them for PV
     u32x4 opa[RA + 1], opb[RA + 1];
     auto read_op = [&](auto sc) {
@@ -522,8 +558,6 @@ __device__ __forceinline__ int s_step(SState<D> &st, const i32x4 (&qf)[D / 32], 
     float p[32];
     float rs0 = 0.f, rs1 = 0.f;
     int imx0 = INT_MIN, imx1 = INT_MIN;
-    s_qk[0] = i32x16{};
-    s_qk[1] = i32x16{};
     // fold score R (exponentiated in an earlier slot): row sum and E4M3 packing
     auto fold = [&](auto rc) {
         constexpr int R = decltype(rc)::value;
@@ -551,7 +585,7 @@ __device__ __forceinline__ int s_step(SState<D> &st, const i32x4 (&qf)[D / 32], 
         if constexpr (S < NQK) {
             lgkm_wait<SC::after(S)>(opa[S % (RA + 1)]);
             s_qk[S % 2] = mfma_i8_32x32x32(__builtin_bit_cast(i32x4, opa[S % (RA + 1)]),
-                                           qf[S / 2], s_qk[S % 2]);
+                                           qf[S / 2], S < 2 ? sbias : s_qk[S % 2]);
         } else {
             constexpr int c = S - NQK;
             lgkm_wait<SC::after(S)>(opb[S % (RA + 1)]);
@@ -566,7 +600,7 @@ __device__ __forceinline__ int s_step(SState<D> &st, const i32x4 (&qf)[D / 32], 
         static_for<SC::first_score(S), SC::first_score(S + 1)>([&](auto rc) {
             constexpr int R = decltype(rc)::value;
             const int v = s_exp[R / 16][R % 16];
-            p[R] = fast_exp2(mask_exp && v == INT_MIN ? -INFINITY : fmaf((float)v, c_exp, bias));
+            p[R] = fast_exp2(fmaf(__int_as_float(v), c_exp, bexp));
             asm volatile("" : "+v"(p[R]));
         });
         if constexpr (S > 0)
@@ -594,8 +628,7 @@ __device__ __forceinline__ int s_step(SState<D> &st, const i32x4 (&qf)[D / 32], 
 }
 
 // TAIL: some key tile runs past N (N not a multiple of 64); without it and
-// without a causal mask no tile is masked, and the per-score mask tests of
-// the exponentials compile away.
+// without a causal mask no tile is masked and the mask pass compiles away.
 template <int D, bool CAUSAL, bool OUT_F32, bool TAIL>
 __device__ __forceinline__ void sage_qtile(const PrefillArgs &a, const SageWs &w,
                                            unsigned char *smem, int bh, int qt, int wave, int lane)
@@ -650,9 +683,11 @@ __device__ __forceinline__ void sage_qtile(const PrefillArgs &a, const SageWs &w
     // per-tile score scales c(t) = cq * dK(t) for tiles t+1 .. t+5 of an even
     // step t; those of tiles t+4, t+5 are loaded at step t and land by the
     // synchronisation before step t+2
+    // (kept >= the smallest normal float, so that a masked score's -inf times c stays -inf)
     auto kd = [&](int t) { return t < ntiles ? kdel[t] : 1.f; };
-    float c1 = cq * kd(1), c2 = cq * kd(2), c3 = cq * kd(3), kd4 = 1.f, kd5 = 1.f;
-    const float c0 = cq * kd(0);
+    auto tc = [&](float kdv) { return fmaxf(cq * kdv, __FLT_MIN__); };
+    float c1 = tc(kd(1)), c2 = tc(kd(2)), c3 = tc(kd(3)), kd4 = 1.f, kd5 = 1.f;
+    const float c0 = tc(kd(0));
 
     const SLanes<D> ln = s_lanes<D>(lane);
     SState<D> st;
@@ -664,26 +699,26 @@ __device__ __forceinline__ void sage_qtile(const PrefillArgs &a, const SageWs &w
     st.pending = false;
 
     i32x16 sA[2], sB[2];   // S(j): sA for even j, sB for odd j
+    const i32x16 sbias = sbias16();
     uint32_t pA[8], pB[8];  // P(j) likewise
 
     // pre-step: S(0), S(1); m from S(0) (exact), P(0); raise for S(1)
     vm_wait_n<0>();
     __syncthreads();
     if (0 < ntw) {
-        qk_tile_i8<D>(sA, qf, lds_addr(kst(0)), ln);
+        qk_tile_i8<D>(sA, qf, lds_addr(kst(0)), ln, sbias);
         if (ntw > 1)
-            qk_tile_i8<D>(sB, qf, lds_addr(kst(1)), ln);
-        const bool m0 = needs_mask(0);
-        if (m0)
+            qk_tile_i8<D>(sB, qf, lds_addr(kst(1)), ln, sbias);
+        if (needs_mask(0))
             mask_i8<CAUSAL>(sA, 0, N, g, my_q);
         const int i0 = imax_tile(sA);
-        st.m = max_xor32(i0 == INT_MIN ? -INFINITY : (float)i0 * c0);
-        st.l = s_exp_tile(sA, c0, kLog2_448 - st.m, m0, pA);
+        st.m = max_xor32(smax_log2(i0, c0));
+        st.l = s_exp_tile(sA, c0, kLog2_448 - st.m, pA);
         if (ntw > 1) {
             if (needs_mask(1))
                 mask_i8<CAUSAL>(sB, kBlk, N, g, my_q);
             const int i1 = imax_tile(sB);
-            s_raise<D>(st, i1 == INT_MIN ? -INFINITY : (float)i1 * c1);
+            s_raise<D>(st, smax_log2(i1, c1));
         }
     }
 
@@ -721,23 +756,23 @@ __device__ __forceinline__ void sage_qtile(const PrefillArgs &a, const SageWs &w
         uint32_t(&pn)[8] = E ? pA : pB;   // P(t+1)
         const float l_before = st.l;
         const int imx = s_step<D, CAUSAL>(st, qf, lds_addr(kst(t + 2)), lds_addr(vst(t)), ln,
-                                          s_exp, s_qk, pc, pn, c_exp, needs_mask(t + 1),
-                                          needs_mask(t + 2), (t + 2) * kBlk, N, g, my_q, dma);
+                                          s_exp, s_qk, pc, pn, c_exp, needs_mask(t + 2),
+                                          (t + 2) * kBlk, N, g, my_q, sbias, dma);
         if (t + 1 >= ntw)
             st.l = l_before;  // tile t+1 does not exist for this wave
         // PV(t) has been issued with P(t): O can take the factor of the raise
         // that P(t+1) was computed after
         s_apply_pending<D>(st);
         if (t + 2 < ntw)
-            s_raise<D>(st, imx == INT_MIN ? -INFINITY : (float)imx * c_qk);
+            s_raise<D>(st, smax_log2(imx, c_qk));
     };
     int t = 0;
     for (; t + 1 < ntw; t += 2) {
         step(t, std::integral_constant<int, 0>{}, c1, c2);
         step(t + 1, std::integral_constant<int, 1>{}, c2, c3);
         c1 = c3;
-        c2 = cq * kd4;
-        c3 = cq * kd5;
+        c2 = tc(kd4);
+        c3 = tc(kd5);
     }
     if (t < ntw) {
         step(t, std::integral_constant<int, 0>{}, c1, c2);
