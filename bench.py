@@ -146,8 +146,17 @@ def bench_bwd(args, stream):
         "kernels_ms": {k_: t for k_, (t, _) in per_kernel.items()},
         "roofline": {"bound": "mfma", "kernel": "bwd_delta + bwd_dq + bwd_dkv",
                      "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "kernel_ms": kms, "traffic": None},
+                     "frac": achieved / PEAK_BF16_TFLOPS, "kernel_ms": kms,
+                     "traffic": bwd_traffic()},
     }
+
+
+def bwd_traffic():
+    """HBM bytes of one backward call (its three kernels), or None when any
+    of them has no counter run for its current source."""
+    parts = [measured_traffic(k, ["bwd.hip", "cdna4.hpp"])
+             for k in ("bwd_delta", "bwd_dq", "bwd_dkv")]
+    return None if any(p is None for p in parts) else sum(parts)
 
 
 def bench_varlen(args, stream):
