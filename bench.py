@@ -37,6 +37,7 @@ PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_FP8_TFLOPS = 5033.2    # fp8 / int8 dense
 PEAK_HBM_GBS = 8000.0       # HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+UTIL_FILE = os.path.join(ROOT, "profiles", "mfma_util.json")
 CSRC = os.path.join(ROOT, "softmax_attention_attn_amd", "csrc")
 
 
@@ -63,6 +64,21 @@ def measured_traffic(kernel: str, files):
     if not ent or ent.get("source_hash") != kernel_source_hash(files):
         return None
     return ent.get("bytes_per_launch")
+
+
+def measured_util(kernel: str, files):
+    """Counter-derived busy fractions of a kernel (MFMA, VALU, LDS bank
+    conflicts; rocprofv3 --pmc, in the kernel's own clock cycles) and the
+    FLOPs its MFMAs executed, from the committed counter run, or None when
+    the kernel's sources changed since."""
+    try:
+        data = json.load(open(UTIL_FILE))
+    except (OSError, ValueError):
+        return None
+    ent = data.get(kernel)
+    if not ent or ent.get("source_hash") != kernel_source_hash(files):
+        return None
+    return {k: ent[k] for k in ("mfma_busy", "valu_busy", "lds_bank_conflict", "executed_flop")}
 
 
 def time_calls(fn, steps, warmup, stream):
@@ -108,7 +124,9 @@ def bench_prefill(args, stream):
                      "frac": achieved / PEAK_BF16_TFLOPS,
                      "kernel_ms": kms,
                      "traffic": measured_traffic("prefill_exact",
-                                                 ["prefill_exact.hip", "cdna4.hpp"])},
+                                                 ["prefill_exact.hip", "cdna4.hpp"]),
+                     "counters": measured_util("prefill_exact",
+                                               ["prefill_exact.hip", "cdna4.hpp"])},
         "inputs": (inp["q"], inp["k"], inp["v"]),
     }
     return res
@@ -147,7 +165,9 @@ def bench_bwd(args, stream):
         "roofline": {"bound": "mfma", "kernel": "bwd_delta + bwd_dq + bwd_dkv",
                      "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "kernel_ms": kms,
-                     "traffic": bwd_traffic()},
+                     "traffic": bwd_traffic(),
+                     "counters": {k: measured_util(k, ["bwd.hip", "cdna4.hpp"])
+                                  for k in ("bwd_dq", "bwd_dkv")}},
     }
 
 
@@ -218,7 +238,8 @@ def bench_decode(args, stream):
             "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved,
                          "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": achieved / PEAK_HBM_GBS, "kernel_ms": kms,
-                         "traffic": measured_traffic(kernel, ["decode.hip", "cdna4.hpp"])},
+                         "traffic": measured_traffic(kernel, ["decode.hip", "cdna4.hpp"]),
+                         "counters": measured_util(kernel, ["decode.hip", "cdna4.hpp"])},
         }
         r.update(extra)
         return r
@@ -270,7 +291,8 @@ def bench_sage(args, stream):
         "roofline": {"bound": "mfma", "kernel": "sage_attn", "achieved": achieved,
                      "peak": PEAK_FP8_TFLOPS, "unit": "TOP/s", "frac": achieved / PEAK_FP8_TFLOPS,
                      "kernel_ms": kms,
-                     "traffic": measured_traffic("sage_attn", ["sage.hip", "cdna4.hpp"])},
+                     "traffic": measured_traffic("sage_attn", ["sage.hip", "cdna4.hpp"]),
+                     "counters": measured_util("sage_attn", ["sage.hip", "cdna4.hpp"])},
     }
 
 
