@@ -35,51 +35,67 @@ constexpr int kBThreads = 64 * kBWaves;
 constexpr int kRows = 32 * kBWaves;  // queries (dq) or keys (dkv) per workgroup
 constexpr int kTile = 64;            // streamed rows per step
 
-// LDS tile of kTile rows of D bf16, rows padded by 16 bytes: a lane group
-// reading 16 bytes of 16 consecutive rows hits 16 distinct bank quads.
-template <int D>
+// LDS tile of kTile rows of D bf16 (16-byte chunks, 16 chunks = the 64 banks).
+//  * Padded (SWZ false): rows of 2D + 16 bytes.  A lane group reading 16 bytes
+//    of 16 consecutive rows hits 16 distinct bank quads; the transposing reads
+//    (4 rows x 64 bytes per 32 lanes) fall partly on the same banks.
+//  * Swizzled (SWZ true, D = 128): rows of 2D + 64 bytes, so consecutive rows
+//    start 4 bank quads apart, and the low two bits of a row's chunk index
+//    are XORed with bits 2-3 of the row (swz).  Both read patterns then touch
+//    each of the 64 banks once per phase: 16 rows of one chunk for a row read,
+//    and 4 rows x one 64-byte block for a transposing read.
+template <int D, bool SWZ = false>
 struct BCfg {
     static constexpr int kChunks = D / 8;             // 16-byte chunks per row
-    static constexpr int kPitch = D * 2 + 16;         // bytes per LDS row
-    static constexpr int kPieces = kTile * (kChunks + 1) / 64;  // 1 KB direct loads
+    static constexpr int kPad = SWZ ? 4 : 1;          // pad chunks per row
+    static constexpr int kPitch = D * 2 + 16 * kPad;  // bytes per LDS row
+    static constexpr int kPieces = kTile * (kChunks + kPad) / 64;  // 1 KB direct loads
     static constexpr int kBytes = kPieces * 1024;
     static constexpr int kPerWave = (kPieces + kBWaves - 1) / kBWaves;
-    static_assert(kPieces * 64 == kTile * (kChunks + 1), "tile split");
+    static_assert(kPieces * 64 == kTile * (kChunks + kPad), "tile split");
+    static_assert(!SWZ || D == 128, "swizzled layout is laid out for 16 chunks per row");
 };
+
+// chunk-index XOR of row `row` in the swizzled layout
+__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
 
 // Direct loads of one padded tile: piece p = wave + 4i of the tile's pieces,
 // lane l fills LDS slot 64p + l = row (64p+l)/(C+1), chunk (64p+l)%(C+1) (the
 // pad chunk re-reads chunk 0).  Rows at or past `rows` read as zero (the
 // buffer resource ends there).
-template <int D>
+template <int D, bool SWZ = false>
 struct TileLanes {
-    uint32_t off[BCfg<D>::kPerWave];  // source byte offset within the tile
+    uint32_t off[BCfg<D, SWZ>::kPerWave];  // source byte offset within the tile
 };
 
-template <int D>
-__device__ __forceinline__ TileLanes<D> tile_lanes(int wave, int lane)
+// slot 64p + l of the tile is row q / (C + pad), physical chunk q % (C + pad);
+// a pad chunk re-reads chunk 0, a swizzled row's physical chunk c holds
+// logical chunk c ^ swz(row)
+template <int D, bool SWZ = false>
+__device__ __forceinline__ TileLanes<D, SWZ> tile_lanes(int wave, int lane)
 {
-    constexpr int C = BCfg<D>::kChunks;
-    TileLanes<D> t;
+    constexpr int C = BCfg<D, SWZ>::kChunks, W = C + BCfg<D, SWZ>::kPad;
+    TileLanes<D, SWZ> t;
 #pragma unroll
-    for (int i = 0; i < BCfg<D>::kPerWave; ++i) {
+    for (int i = 0; i < BCfg<D, SWZ>::kPerWave; ++i) {
         const int q = (wave + kBWaves * i) * 64 + lane;
-        const int row = q / (C + 1), c = q % (C + 1);
-        t.off[i] = row * (D * 2) + (c == C ? 0 : c) * 16;
+        const int row = q / W, c = q % W;
+        const int logical = c >= C ? 0 : SWZ ? c ^ swz(row) : c;
+        t.off[i] = row * (D * 2) + logical * 16;
     }
     return t;
 }
 
-template <int D>
+template <int D, bool SWZ = false>
 __device__ __forceinline__ void load_tile(unsigned char *lds, const uint16_t *src, int r0, int N,
-                                          int wave, const TileLanes<D> &tl)
+                                          int wave, const TileLanes<D, SWZ> &tl)
 {
     const int rows = min(kTile, N - r0);
     const __amdgpu_buffer_rsrc_t r = raw_rsrc(src + (size_t)r0 * D, (uint32_t)rows * D * 2);
 #pragma unroll
-    for (int i = 0; i < BCfg<D>::kPerWave; ++i) {
+    for (int i = 0; i < BCfg<D, SWZ>::kPerWave; ++i) {
         const int piece = wave + kBWaves * i;
-        if (piece < BCfg<D>::kPieces)
+        if (piece < BCfg<D, SWZ>::kPieces)
             dma16_rsrc(r, tl.off[i], lds + piece * 1024);
     }
 }
@@ -105,6 +121,40 @@ __device__ __forceinline__ uint32_t trans_addr(uint32_t tile, int lane)
 {
     const int G = lane >> 4, L = lane & 15, j = L >> 2, q = L & 3, h = G >> 1;
     return tile + (4 * h + j) * BCfg<D>::kPitch + (16 * (G & 1) + 4 * q) * 2;
+}
+
+// Swizzled tiles (row0 and ROW0 multiples of 16, so swz depends on the lane
+// only).  Row read of k-step ks: lane (n, g) takes logical chunk 2ks + g of
+// row row0 + n, physical chunk 4(ks/2) + ((2(ks%2) + g) ^ swz(n)); the address
+// for each parity of ks is kept, and 64(ks/2) bytes go into the offset.
+template <int PAR>
+__device__ __forceinline__ uint32_t swz_row_addr(uint32_t tile, int lane)
+{
+    const int n = lane & 31, g = lane >> 5;
+    return tile + n * BCfg<128, true>::kPitch + (((2 * PAR + g) ^ swz(n)) << 4);
+}
+
+// Transposing read of rows ROW0 + SEC + 4h + j (SEC 0 or 8): lane 4j + q of
+// 16-lane group G takes bytes 32(G&1) + 8q of a 64-byte block, that is chunk
+// 2(G&1) + q/2 of the block, half q%2; swz of its row is (SEC/4 + h) % 4.
+template <int SEC>
+__device__ __forceinline__ uint32_t swz_trans_addr(uint32_t tile, int lane)
+{
+    const int G = lane >> 4, L = lane & 15, j = L >> 2, q = L & 3, h = G >> 1;
+    const int kk = (2 * (G & 1) + (q >> 1)) ^ ((SEC / 4 + h) & 3);
+    return tile + (SEC + 4 * h + j) * BCfg<128, true>::kPitch + (kk << 4) + (q & 1) * 8;
+}
+
+// the 16 contraction rows starting at ROW0 and the column block C of a
+// swizzled tile, from the two lane addresses of swz_trans_addr<0> and <8>
+template <int ROW0, int C>
+__device__ __forceinline__ u32x4 swz_trans_read(uint32_t a0, uint32_t a8)
+{
+    static_assert(ROW0 % 16 == 0, "row block");
+    constexpr int off = ROW0 * BCfg<128, true>::kPitch + C * 64;
+    const u32x2 a = lds_read_tr16_b64<off>(a0);
+    const u32x2 b = lds_read_tr16_b64<off>(a8);
+    return u32x4{a[0], a[1], b[0], b[1]};
 }
 
 // the 16 contraction rows starting at ROW0 and the column block C of the
@@ -227,7 +277,10 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a)
 template <int D, bool CAUSAL, bool OUT_F32>
 __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(BwdArgs a)
 {
-    constexpr int KB = BCfg<D>::kBytes, KS = D / 16, NC = D / 32;
+    // K is read both row-wise and transposed: the swizzled layout (d = 128)
+    constexpr bool SW = D == 128;
+    using Cf = BCfg<D, SW>;
+    constexpr int KB = Cf::kBytes, KS = D / 16, NC = D / 32;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * KB];
     const int lane = threadIdx.x & 63, g = lane >> 5, n = lane & 31;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -245,11 +298,16 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     const int ntiles = (kend + kTile - 1) / kTile;
     const int ntw = CAUSAL ? min(ntiles, (qw0 + 31) / kTile + 1) : ntiles;  // this wave's tiles
 
-    const TileLanes<D> tl = tile_lanes<D>(wave, lane);
+    const TileLanes<D, SW> tl = tile_lanes<D, SW>(wave, lane);
     auto kst = [&](int t) { return smem + (t & 1) * 2 * KB; };
     auto vst = [&](int t) { return smem + (t & 1) * 2 * KB + KB; };
-    load_tile<D>(kst(0), kb, 0, N, wave, tl);
-    load_tile<D>(vst(0), vb, 0, N, wave, tl);
+    load_tile<D, SW>(kst(0), kb, 0, N, wave, tl);
+    load_tile<D, SW>(vst(0), vb, 0, N, wave, tl);
+    // lane parts of the swizzled read addresses (tile-independent)
+    const uint32_t lrow0 = SW ? swz_row_addr<0>(0, lane) : 0;
+    const uint32_t lrow1 = SW ? swz_row_addr<1>(0, lane) : 0;
+    const uint32_t ltr0 = SW ? swz_trans_addr<0>(0, lane) : 0;
+    const uint32_t ltr8 = SW ? swz_trans_addr<8>(0, lane) : 0;
 
     // Q^T and dO^T fragments (B operands): lane holds row my_q, columns 16ks + 8g .. +7
     bf16x8 qf[KS], df[KS];
@@ -274,13 +332,14 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         vm_wait_n<0>();
         __syncthreads();  // tile t landed; stage (t+1)&1 no longer read
         if (t + 1 < ntiles) {
-            load_tile<D>(kst(t + 1), kb, (t + 1) * kTile, N, wave, tl);
-            load_tile<D>(vst(t + 1), vb, (t + 1) * kTile, N, wave, tl);
+            load_tile<D, SW>(kst(t + 1), kb, (t + 1) * kTile, N, wave, tl);
+            load_tile<D, SW>(vst(t + 1), vb, (t + 1) * kTile, N, wave, tl);
         }
         if (t >= ntw)
             continue;
         const uint32_t ka = lds_addr(kst(t)), va = lds_addr(vst(t));
-        const uint32_t kd = direct_addr<D>(ka, 0, lane), vd = direct_addr<D>(va, 0, lane);
+        const uint32_t kd = SW ? ka + lrow0 : direct_addr<D>(ka, 0, lane);
+        const uint32_t vd = SW ? ka + lrow1 : direct_addr<D>(va, 0, lane);
         // S^T = K Q^T and dP^T = V dO^T: rows = keys 32 blk + 8(r/4) + 4g + r%4
         f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
         // product i: block i % 2 (alternating accumulators), k-step i / 2;
@@ -288,9 +347,18 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         operand_stream<2 * KS, 2, 2>(
             [&](auto i, u32x4 &x, u32x4 &y) {
                 constexpr int I = decltype(i)::value;
-                constexpr int off = 32 * (I % 2) * BCfg<D>::kPitch + 32 * (I / 2);
-                x = lds_read_b128<off>(kd);
-                y = lds_read_b128<off>(vd);
+                if constexpr (SW) {
+                    // kd / vd: the addresses for even / odd k-steps; the V tile
+                    // is KB bytes after the K tile
+                    constexpr int ks = I / 2, off = 32 * (I % 2) * Cf::kPitch + 64 * (ks / 2);
+                    const uint32_t a = (ks & 1) ? vd : kd;
+                    x = lds_read_b128<off>(a);
+                    y = lds_read_b128<off + KB>(a);
+                } else {
+                    constexpr int off = 32 * (I % 2) * Cf::kPitch + 32 * (I / 2);
+                    x = lds_read_b128<off>(kd);
+                    y = lds_read_b128<off>(vd);
+                }
             },
             [&](auto i, const u32x4 &x, const u32x4 &y) {
                 constexpr int I = decltype(i)::value;
@@ -312,15 +380,21 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
             pack16(ds, dsw[blk]);
         }
         // dQ^T += K^T dS^T: contraction over the tile's keys, 16 per MFMA
-        const uint32_t kt = trans_addr<D>(ka, lane);
+        const uint32_t kt = SW ? ka + ltr0 : trans_addr<D>(ka, lane);
+        const uint32_t kt8 = SW ? ka + ltr8 : 0;
         // product pair i: keys 16u .. 16u+15 (u = i / (NC/2)) into the
         // feature blocks c0 = 2(i % (NC/2)) and c0 + 1, so that consecutive
         // MFMAs accumulate into different blocks
         operand_stream<2 * NC, 2, 4>(
             [&](auto i, u32x4 &x, u32x4 &y) {
                 constexpr int I = decltype(i)::value, u = I / (NC / 2), c0 = 2 * (I % (NC / 2));
-                x = trans_read<D, 16 * u, c0>(kt);
-                y = trans_read<D, 16 * u, c0 + 1>(kt);
+                if constexpr (SW) {
+                    x = swz_trans_read<16 * u, c0>(kt, kt8);
+                    y = swz_trans_read<16 * u, c0 + 1>(kt, kt8);
+                } else {
+                    x = trans_read<D, 16 * u, c0>(kt);
+                    y = trans_read<D, 16 * u, c0 + 1>(kt);
+                }
             },
             [&](auto i, const u32x4 &x, const u32x4 &y) {
                 constexpr int I = decltype(i)::value, u = I / (NC / 2), c0 = 2 * (I % (NC / 2));
