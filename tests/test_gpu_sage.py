@@ -117,7 +117,10 @@ def test_sage_prefill_workload_sampled(attn):
     o, lse = attn.fwd(q.cuda(), k.cuda(), v.cuda(), causal=w.causal, mode="sage",
                       out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
-    rows = workloads.sample_rows(w.B, w.H, w.N, n_random=256, whole_slices=())
+    # two whole (b, h) slices, the tile-edge and last rows of every slice and
+    # 4096 seeded random rows
+    rows = workloads.sample_rows(w.B, w.H, w.N, n_random=4096,
+                                 whole_slices=((0, 0), (w.B - 1, w.H - 1)))
     o = o.float().cpu().numpy().reshape(-1, w.d)[rows]
     lse = lse.cpu().numpy().reshape(-1)[rows]
     qb, kb, vb = _bits(q, k, v)
