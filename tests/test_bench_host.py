@@ -1,0 +1,62 @@
+"""Host logic of bench.py, on the CPU: the committed counter runs are reported
+only while the kernel source they were taken on is unchanged, the backward's
+traffic is the sum of its three kernels', and a request for more than one GPU
+is refused before anything touches a device."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture()
+def bench(monkeypatch, tmp_path):
+    import bench as B
+    files = ["bwd.hip", "cdna4.hpp"]
+    good = B.kernel_source_hash(files)
+    util = {"bwd_dq": {"source_hash": good, "mfma_busy": 0.4, "valu_busy": 0.3,
+                       "lds_bank_conflict": 0.0, "executed_flop": 1.0},
+            "bwd_dkv": {"source_hash": "0" * 16, "mfma_busy": 0.3, "valu_busy": 0.2,
+                        "lds_bank_conflict": 0.2, "executed_flop": 2.0}}
+    traffic = {k: {"source_hash": good, "bytes_per_launch": float(n)}
+               for k, n in (("bwd_delta", 1), ("bwd_dq", 10), ("bwd_dkv", 100))}
+    (tmp_path / "u.json").write_text(json.dumps(util))
+    (tmp_path / "t.json").write_text(json.dumps(traffic))
+    monkeypatch.setattr(B, "UTIL_FILE", str(tmp_path / "u.json"))
+    monkeypatch.setattr(B, "TRAFFIC_FILE", str(tmp_path / "t.json"))
+    return B, files, tmp_path
+
+
+def test_counters_follow_the_source_hash(bench):
+    B, files, _ = bench
+    assert B.measured_util("bwd_dq", files) == {"mfma_busy": 0.4, "valu_busy": 0.3,
+                                                "lds_bank_conflict": 0.0, "executed_flop": 1.0}
+    assert B.measured_util("bwd_dkv", files) is None      # taken on another source
+    assert B.measured_util("prefill_exact", files) is None  # never taken
+
+
+def test_backward_traffic_is_the_sum_of_its_kernels(bench):
+    B, files, tmp_path = bench
+    assert B.bwd_traffic() == 111.0
+    data = json.loads((tmp_path / "t.json").read_text())
+    data["bwd_dkv"]["source_hash"] = "f" * 16
+    (tmp_path / "t.json").write_text(json.dumps(data))
+    assert B.bwd_traffic() is None
+
+
+def test_committed_profiles_parse():
+    for name in ("hbm_traffic.json", "mfma_util.json"):
+        data = json.load(open(os.path.join(ROOT, "profiles", name)))
+        for key, ent in data.items():
+            if key.startswith("_"):
+                continue
+            assert len(ent["source_hash"]) == 16 and ent["sources"], (name, key)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2 and "one GPU" in r.stderr, (r.returncode, r.stderr[-500:])
