@@ -65,7 +65,9 @@ typedef enum {
      * kv head, in fp32); Q and K' quantised to symmetric INT8 per block of 64
      * consecutive tokens of one (batch, head) with scale max|x|/127; S from an
      * INT8 MFMA with exact int32 accumulation; P quantised to OCP E4M3 as
-     * E4M3(448 * exp(S - m_running)); V quantised to E4M3 per (batch, kv head,
+     * E4M3(448 * exp(S - m_running)), the exponent formed in fp32 to within
+     * half a unit of the integer score (times its scale) before the E4M3
+     * rounding; V quantised to E4M3 per (batch, kv head,
      * channel) with scale max|V|/448; PV by an FP8 MFMA with fp32
      * accumulation.  lse is the true LSE (the Smooth-K shift q_i . kmean is
      * added back).  Needs a workspace. */
