@@ -90,7 +90,7 @@ def _load():
         _u16p, _u16p, _u16p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_int, ctypes.c_int,
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
-        _i64p, ctypes.c_int64, _f64p, _f64p, ctypes.c_int]
+        ctypes.c_int, _i64p, ctypes.c_int64, _f64p, _f64p, ctypes.c_int]
     lib.oracle_sage_quantise.restype = ctypes.c_int
     lib.oracle_sage_quantise.argtypes = [
         _u16p, _u16p, _u16p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -239,12 +239,16 @@ def lse_merge(o_parts, lse_parts):
 def sage_rows(q, k, v, *, causal: bool, scale: float, rows=None, blk: int = 64,
               tile_n: int = 64, smooth_k: bool = True, quant_qk: bool = True,
               quant_p: bool = True, quant_v: bool = True, p_scale: float = 448.0,
-              threads: int | None = None):
+              l_from_quantised_p: bool = False, threads: int | None = None):
     """Quantised (SageAttention-style) attention emulated step by step in fp64.
 
     Same shapes and ``rows`` convention as :func:`attn_rows` (Nq == Nk == N).
     ``tile_n`` is the key-tile width of the online softmax, which decides the
-    running max that P is quantised against.  Returns (o, lse).
+    running max that P is quantised against.  ``smooth_k``, ``quant_qk``,
+    ``quant_p`` and ``quant_v`` switch single steps of the recipe off (for
+    attributing its error to its sources); ``l_from_quantised_p`` sums the
+    quantised P instead of the unrounded one into the row sum (an alternative
+    reading).  Returns (o, lse).
     """
     q, k, v = _u16(q), _u16(k), _u16(v)
     B, H, N, d = q.shape
@@ -263,7 +267,8 @@ def sage_rows(q, k, v, *, causal: bool, scale: float, rows=None, blk: int = 64,
     r = _load().oracle_sage_rows(_ptr(q, _u16p), _ptr(k, _u16p), _ptr(v, _u16p), B, H, Hkv, N,
                                  d, int(bool(causal)), float(scale), int(blk), int(tile_n),
                                  int(smooth_k), int(quant_qk), int(quant_p), int(quant_v),
-                                 float(p_scale), rows_p, nrows, _ptr(o, _f64p),
+                                 float(p_scale), int(bool(l_from_quantised_p)), rows_p,
+                                 nrows, _ptr(o, _f64p),
                                  _ptr(lse, _f64p), int(threads or default_threads()))
     if r < 0:
         raise ValueError("oracle_sage_rows rejected its arguments")

@@ -511,12 +511,14 @@ static void sage_free(sage_state *st)
  * because P is quantised against the running max.
  * p_scale: factor applied to p before the E4M3 cast (448 for the recipe);
  * quant_p = 0 skips P quantisation, quant_v = 0 skips V quantisation (used for
- * error attributions); quant_qk = 0 uses the unquantised (smoothed) Q and K.
+ * error attributions); quant_qk = 0 uses the unquantised (smoothed) Q and K;
+ * l_quant = 1 makes l the sum of the quantised P^_j / 448 instead of the
+ * unrounded p_j (an alternative reading, for the same attributions).
  */
 double oracle_sage_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                         int B, int H, int Hkv, int N, int d, int causal, double scale,
                         int blk, int tile_n, int smooth_k, int quant_qk, int quant_p,
-                        int quant_v, double p_scale,
+                        int quant_v, double p_scale, int l_quant,
                         const int64_t *rows, int64_t nrows, double *o, double *lse,
                         int nthreads)
 {
@@ -579,8 +581,11 @@ double oracle_sage_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                     acc[c] *= alpha;
                 for (int64_t j = j0; j < j1; ++j) {
                     double p = exp(S[j - j0] - mnew);
-                    l += p;
                     double ph = quant_p ? oracle_e4m3_round(p_scale * p) : p_scale * p;
+                    /* l sums the unrounded p (the recipe); l_quant instead sums
+                     * the quantised values ph / p_scale, an alternative reading
+                     * kept for comparison */
+                    l += l_quant ? ph / p_scale : p;
                     const double *vj = st.vq + (bg * N + j) * d;
                     const uint16_t *vr = v + (bg * N + j) * d;
                     for (int c = 0; c < d; ++c) {

@@ -239,3 +239,56 @@ def test_emulator_lse_is_true_lse(oracle_lib):
     _, lse_raw = oracle.sage_rows(qb, kb, vb, causal=True, scale=0.125, quant_qk=False,
                                   quant_p=False, quant_v=False)
     np.testing.assert_allclose(lse_raw, lsee, atol=1e-11)
+
+
+# ---------------------------------------------------- hand-computed running max
+
+def _two_key_case(order):
+    """q = (1, 0) for both query rows; K rows (-1/2, 0), (+1/2, 0) in the given
+    order (their mean is 0, so Smooth-K leaves them); V rows (1, 2), (-1/2, 1).
+    With scale 1 every quantity is exact in INT8 / E4M3: q^ = (127, 0) with
+    dQ = 1/127, k^ = (-+127, 0) with dK = (1/2)/127, so the scores are -+1/2;
+    V / dV = (448, 448), (-224, 224)."""
+    q = torch.tensor([[[[1.0, 0.0], [1.0, 0.0]]]], dtype=torch.bfloat16)
+    kr = [[-0.5, 0.0], [0.5, 0.0]]
+    k = torch.tensor([[kr if order == "rising" else kr[::-1]]], dtype=torch.bfloat16)
+    v = torch.tensor([[[[1.0, 2.0], [-0.5, 1.0]]]], dtype=torch.bfloat16)
+    return _bits(q, k, v)
+
+
+@pytest.mark.parametrize("case", ["rising_tile1", "falling_tile1", "rising_one_tile",
+                                  "falling_tile1_lquant"])
+def test_emulator_running_max_hand_computed(oracle_lib, case):
+    """P^ = E4M3(448 exp(S - m)) against the running max of each key tile,
+    fixed by hand on a two-key row (e = exp(-1), the score gap is 1):
+    * rising scores, one key per tile: each key is its tile's max when it is
+      quantised, so P^ = (448, 448) and, after the rescale by e, the weights
+      are (e, 1) -- the exact softmax;
+    * falling scores, one key per tile: the second key is quantised against
+      the first key's max, 448 e = 164.8 -> P^ = 160 (E4M3 steps by 16 on
+      [128, 256)), weights (1, 160/448);
+    * rising scores in one tile of two keys: both quantised against the tile
+      max, weights (160/448, 1);
+    * the row sum l is the unrounded 1 + e in all three, so the LSE is
+      1/2 + ln(1 + e); with the quantised-P row sum instead it is
+      1/2 + ln(1 + 160/448) and O is normalised by that.
+    A P quantised against the final row max, or a running max not rescaling
+    the accumulator, gives other weights in at least one case."""
+    order = "rising" if case.startswith("rising") else "falling"
+    tile_n = 2 if case == "rising_one_tile" else 1
+    lq = case.endswith("lquant")
+    qb, kb, vb = _two_key_case(order)
+    o, lse = oracle.sage_rows(qb, kb, vb, causal=False, scale=1.0, tile_n=tile_n, blk=64,
+                              l_from_quantised_p=lq)
+    e = math.exp(-1.0)
+    v0, v1 = np.array([1.0, 2.0]), np.array([-0.5, 1.0])
+    if order == "rising":  # key 0 scores -1/2, key 1 scores +1/2
+        w0, w1 = (e, 1.0) if tile_n == 1 else (160 / 448, 1.0)
+    else:                  # key 0 scores +1/2, key 1 scores -1/2
+        w0, w1 = 1.0, 160 / 448
+    l = (w0 + w1) if lq else (1.0 + e)
+    o_hand = (w0 * v0 + w1 * v1) / l
+    lse_hand = 0.5 + math.log(l)
+    for row in range(2):
+        np.testing.assert_allclose(o[0, 0, row], o_hand, rtol=1e-6, atol=1e-7)
+        assert abs(lse[0, 0, row] - lse_hand) < 1e-6, (lse[0, 0, row], lse_hand)
