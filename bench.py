@@ -3,18 +3,27 @@
 One step is one call of the library on the headline workload (exact bf16
 causal prefill, B=4 H=32 N=4096 d=128), with inputs resident in HBM.  W
 untimed warm-up steps, then K timed steps between two events on the launch
-stream (torch's current stream), synchronised on both sides.  The library's
-own per-kernel HIP events (attn_profiler_*) time the dominant kernel inside
-the same timed region for the roofline figure.
+stream (torch's current stream), synchronised on both sides; an event between
+consecutive steps gives the per-step times, reported as mean, median, p10 and
+p90.  The library's own per-launch HIP events (attn_profiler_*, recorded on
+the launch stream from a pool created before the timed region) time every
+kernel inside the same region for the roofline figures.
 
-The same JSON line also carries the split-KV decode workload (HBM bound,
-GB/s; contiguous caches, and the same caches spread over a pool of 16-row
-pages), the backward of the headline workload, a packed batch of
-variable-length sequences, and the quantised prefill workload, each with its own roofline object,
+The same JSON line also carries, each with its own roofline object where the
+workload has a bound worth stating:
+  noncausal  the headline shape without the mask;
+  tiny       B1 H2 N256 d64 fp32 O (a latency figure: two workgroups);
+  long       B1 H16 N65536 d128 causal with outlier keys;
+  bwd        the backward of the headline workload;
+  varlen     a packed batch of variable-length sequences;
+  sage       the quantised prefill B2 H24 N16384 d128, with its quantisation
+             statistics read back from the workspace;
+  decode     GQA split-KV decode, contiguous caches and 16-row pages;
 and the fp64 CPU oracle timed on a bounded sample of the headline workload.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                  [--only prefill|bwd|varlen|decode|sage] [--calibrate-copy]
+                  [--only prefill|noncausal|tiny|long|bwd|varlen|sage|decode]
+                  [--calibrate-copy]
 """
 from __future__ import annotations
 
@@ -39,6 +48,7 @@ PEAK_HBM_GBS = 8000.0       # HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 UTIL_FILE = os.path.join(ROOT, "profiles", "mfma_util.json")
 CSRC = os.path.join(ROOT, "softmax_attention_attn_amd", "csrc")
+LEGS = ("prefill", "noncausal", "tiny", "long", "bwd", "varlen", "sage", "decode")
 
 
 def log(*a):
@@ -53,83 +63,155 @@ def kernel_source_hash(files) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, files):
-    """HBM bytes per launch from the committed counter runs, or None when the
-    kernel sources changed since the counters were taken."""
+def _profile_entry(path, key, files):
     try:
-        data = json.load(open(TRAFFIC_FILE))
+        data = json.load(open(path))
     except (OSError, ValueError):
         return None
-    ent = data.get(kernel)
+    ent = data.get(key)
     if not ent or ent.get("source_hash") != kernel_source_hash(files):
         return None
-    return ent.get("bytes_per_launch")
+    return ent
 
 
-def measured_util(kernel: str, files):
+def measured_traffic(key: str, files):
+    """HBM bytes per launch from the committed counter runs (``key`` names the
+    kernel and workload), or None when the kernel sources changed since the
+    counters were taken."""
+    ent = _profile_entry(TRAFFIC_FILE, key, files)
+    return None if ent is None else ent.get("bytes_per_launch")
+
+
+def measured_util(key: str, files):
     """Counter-derived busy fractions of a kernel (MFMA, VALU, LDS bank
-    conflicts; rocprofv3 --pmc, in the kernel's own clock cycles) and the
-    FLOPs its MFMAs executed, from the committed counter run, or None when
-    the kernel's sources changed since."""
-    try:
-        data = json.load(open(UTIL_FILE))
-    except (OSError, ValueError):
+    conflicts; rocprofv3 --pmc, in the kernel's own clock cycles), the FLOPs
+    its MFMAs executed and its L2 hit rate, from the committed counter runs,
+    or None when the kernel's sources changed since."""
+    ent = _profile_entry(UTIL_FILE, key, files)
+    if ent is None:
         return None
-    ent = data.get(kernel)
-    if not ent or ent.get("source_hash") != kernel_source_hash(files):
-        return None
-    return {k: ent[k] for k in ("mfma_busy", "valu_busy", "lds_bank_conflict", "executed_flop")}
+    return {k: ent[k] for k in ("mfma_busy", "valu_busy", "lds_bank_conflict", "executed_flop",
+                                "l2_hit") if k in ent}
+
+
+def summed_traffic(keys, files):
+    """HBM bytes of one call made of several kernels (the sum of their
+    per-launch traffic), or None when any of them has no counter run for its
+    current source."""
+    parts = [measured_traffic(k, files) for k in keys]
+    return None if any(p is None for p in parts) else sum(parts)
+
+
+def bwd_traffic():
+    return summed_traffic(("bwd_delta", "bwd_dq", "bwd_dkv"), ["bwd.hip", "cdna4.hpp"])
+
+
+def stats(xs):
+    a = np.asarray(xs, dtype=np.float64)
+    return {"mean": float(a.mean()), "median": float(np.median(a)),
+            "p10": float(np.percentile(a, 10)), "p90": float(np.percentile(a, 90)),
+            "n": int(a.size)}
 
 
 def time_calls(fn, steps, warmup, stream):
+    """Run ``fn`` warmup times, then time ``steps`` calls back to back.
+
+    Returns (per-step stats in ms, {kernel: per-launch stats in ms}).  The
+    per-step times come from events recorded between consecutive calls on the
+    launch stream; the kernel times from the library's per-launch events."""
     import softmax_attention_attn_amd as A
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     A.attn_profiler_enable(True)
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(steps):
+    evs[0].record(stream)
+    for i in range(steps):
         fn()
-    end.record(stream)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    kern = A.attn_profiler_read()
+    total_ms = evs[0].elapsed_time(evs[-1])
+    per_step = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    launches = A.attn_profiler_launches()
     A.attn_profiler_enable(False)
-    per_kernel = {k: (t / n if n else 0.0, n) for k, (t, n) in kern.items()}
-    return total_ms / steps, per_kernel
+    per_kernel = {}
+    for name, ms in launches:
+        per_kernel.setdefault(name, []).append(ms)
+    st = stats(per_step)
+    st["mean"] = total_ms / steps  # the whole timed region, K steps
+    return st, {k: stats(v) for k, v in per_kernel.items()}
 
 
-def bench_prefill(args, stream):
-    import softmax_attention_attn_amd as A
-    w = workloads.WORKLOADS["llm_prefill"]
+def roofline(bound, kernel, work, kstats, peak, unit, traffic=None, counters=None, **extra):
+    """Roofline object of one kernel: algorithmic work per launch over the
+    kernel's mean launch time (the median-based figure alongside)."""
+    scale = 1e12 if unit in ("TFLOP/s", "TOP/s") else 1e9
+    ach = work / (kstats["mean"] * 1e-3) / scale
+    r = {"bound": bound, "kernel": kernel, "achieved": ach, "peak": peak, "unit": unit,
+         "frac": ach / peak, "traffic": traffic, "kernel_ms": kstats,
+         "achieved_median": work / (kstats["median"] * 1e-3) / scale, "work": work}
+    if counters is not None:
+        r["counters"] = counters
+    r.update(extra)
+    return r
+
+
+def _prefill_inputs(w):
     inp = workloads.make(w)
-    q, k, v = inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda()
-    o = torch.empty_like(q)
+    return inp, inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda()
+
+
+def bench_exact(args, stream, wname, key, causal=None, out_dtype=torch.bfloat16):
+    """Exact prefill on a named workload (causal as the workload says unless
+    given); roofline for prefill_exact."""
+    import softmax_attention_attn_amd as A
+    w = workloads.WORKLOADS[wname]
+    causal = w.causal if causal is None else causal
+    inp, q, k, v = _prefill_inputs(w)
+    o = torch.empty(q.shape, dtype=out_dtype, device="cuda")
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
 
     def step():
-        A.fwd(q, k, v, causal=w.causal, o=o, lse=lse, stream=stream)
+        A.fwd(q, k, v, causal=causal, o=o, lse=lse, out_dtype=out_dtype, stream=stream)
 
-    ms, per_kernel = time_calls(step, args.steps, args.warmup, stream)
-    flops = w.flops()
-    kms = per_kernel["prefill_exact"][0]
-    achieved = flops / (kms * 1e-3) / 1e12
+    st, per_kernel = time_calls(step, args.steps, args.warmup, stream)
+    flops = 4.0 * w.B * w.H * w.N * w.N * w.d / (2 if causal else 1)
+    files = ["prefill_exact.hip", "cdna4.hpp"]
     res = {
-        "workload": w, "ms_per_step": ms, "value": flops / (ms * 1e-3) / 1e12,
-        "roofline": {"bound": "mfma", "kernel": "prefill_exact", "achieved": achieved,
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS,
-                     "kernel_ms": kms,
-                     "traffic": measured_traffic("prefill_exact",
-                                                 ["prefill_exact.hip", "cdna4.hpp"]),
-                     "counters": measured_util("prefill_exact",
-                                               ["prefill_exact.hip", "cdna4.hpp"])},
-        "inputs": (inp["q"], inp["k"], inp["v"]),
+        "workload": w.name, "causal": causal, "B": w.B, "H": w.H, "Hkv": w.Hkv, "N": w.N,
+        "d": w.d, "out": "%s O + fp32 LSE" % ("bf16" if out_dtype == torch.bfloat16 else "fp32"),
+        "ms_per_step": st["mean"], "step_ms": st, "flops": flops,
+        "value": flops / (st["mean"] * 1e-3) / 1e12, "unit": "TFLOP/s",
+        "roofline": roofline("mfma", "prefill_exact", flops, per_kernel["prefill_exact"],
+                             PEAK_BF16_TFLOPS, "TFLOP/s",
+                             traffic=measured_traffic(key, files),
+                             counters=measured_util(key, files)),
     }
-    return res
+    return res, inp
+
+
+def bench_tiny(args, stream):
+    """B1 H2 N256 d64 non-causal, fp32 O: two workgroups on a 256-CU chip, so
+    a latency figure (launch to completion), not a roofline claim."""
+    import softmax_attention_attn_amd as A
+    w = workloads.WORKLOADS["tiny_exact"]
+    _, q, k, v = _prefill_inputs(w)
+    o = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+
+    def step():
+        A.fwd(q, k, v, causal=w.causal, o=o, lse=lse, out_dtype=torch.float32, stream=stream)
+
+    st, per_kernel = time_calls(step, max(args.steps, 100), args.warmup, stream)
+    flops = w.flops()
+    ks = per_kernel["prefill_exact"]
+    return {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+            "out": "fp32 O + fp32 LSE", "step_ms": st, "kernel_ms": ks,
+            "latency_us_median": st["median"] * 1e3, "kernel_us_median": ks["median"] * 1e3,
+            "value": flops / (st["median"] * 1e-3) / 1e12, "unit": "TFLOP/s",
+            "note": "latency bound: 2 workgroups (one 256-query tile per head) on 256 CUs; "
+                    "value is FLOPs over the median step time"}
 
 
 def bench_bwd(args, stream):
@@ -137,8 +219,7 @@ def bench_bwd(args, stream):
     and LSE from the forward (outside the timed region)."""
     import softmax_attention_attn_amd as A
     w = workloads.WORKLOADS["llm_prefill"]
-    inp = workloads.make(w)
-    q, k, v = inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda()
+    _, q, k, v = _prefill_inputs(w)
     do = workloads.make_prefill(w.B, w.H, w.Hkv, w.N, w.d, seed=1)[0].cuda()
     o, lse = A.fwd(q, k, v, causal=w.causal)
     dq = torch.empty_like(q)
@@ -151,32 +232,24 @@ def bench_bwd(args, stream):
         A.bwd(q, k, v, o, lse, do, causal=w.causal, dq=dq, dk=dk, dv=dv, workspace=ws,
               stream=stream)
 
-    ms, per_kernel = time_calls(step, args.steps, args.warmup, stream)
+    st, per_kernel = time_calls(step, args.steps, args.warmup, stream)
     # five products of the forward's size (S, dP, dV, dK, dQ): 2.5x the
     # forward's FLOPs; the recomputation of S and dP in the dQ kernel is not
     # counted
     flops = 2.5 * w.flops()
-    kms = sum(t for t, _ in per_kernel.values())
-    achieved = flops / (kms * 1e-3) / 1e12
+    names = ("bwd_delta", "bwd_dq", "bwd_dkv")
+    ksum = {"mean": sum(per_kernel[n]["mean"] for n in names),
+            "median": sum(per_kernel[n]["median"] for n in names)}
+    files = ["bwd.hip", "cdna4.hpp"]
     return {
-        "workload": w.name + "_bwd", "value": flops / (ms * 1e-3) / 1e12, "unit": "TFLOP/s",
-        "ms_per_step": ms, "flops": flops,
-        "kernels_ms": {k_: t for k_, (t, _) in per_kernel.items()},
-        "roofline": {"bound": "mfma", "kernel": "bwd_delta + bwd_dq + bwd_dkv",
-                     "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "kernel_ms": kms,
-                     "traffic": bwd_traffic(),
-                     "counters": {k: measured_util(k, ["bwd.hip", "cdna4.hpp"])
-                                  for k in ("bwd_dq", "bwd_dkv")}},
+        "workload": w.name + "_bwd", "value": flops / (st["mean"] * 1e-3) / 1e12,
+        "unit": "TFLOP/s", "ms_per_step": st["mean"], "step_ms": st, "flops": flops,
+        "kernels_ms": per_kernel,
+        "roofline": roofline("mfma", "bwd_delta + bwd_dq + bwd_dkv", flops, ksum,
+                             PEAK_BF16_TFLOPS, "TFLOP/s",
+                             traffic=summed_traffic(names, files),
+                             counters={n: measured_util(n, files) for n in ("bwd_dq", "bwd_dkv")}),
     }
-
-
-def bwd_traffic():
-    """HBM bytes of one backward call (its three kernels), or None when any
-    of them has no counter run for its current source."""
-    parts = [measured_traffic(k, ["bwd.hip", "cdna4.hpp"])
-             for k in ("bwd_delta", "bwd_dq", "bwd_dkv")]
-    return None if any(p is None for p in parts) else sum(parts)
 
 
 def bench_varlen(args, stream):
@@ -191,20 +264,99 @@ def bench_varlen(args, stream):
     def step():
         A.fwd_varlen(q, k, v, cu, w.N, causal=w.causal, o=o, lse=lse, stream=stream)
 
-    ms, per_kernel = time_calls(step, args.steps, args.warmup, stream)
+    st, per_kernel = time_calls(step, args.steps, args.warmup, stream)
     flops = w.flops(inp["seqlens"].numpy())
-    kms = per_kernel["prefill_exact_varlen"][0]
-    achieved = flops / (kms * 1e-3) / 1e12
+    files = ["prefill_exact.hip", "cdna4.hpp"]
     return {
-        "workload": w.name, "value": flops / (ms * 1e-3) / 1e12, "unit": "TFLOP/s",
-        "ms_per_step": ms, "seqlens": inp["seqlens"].tolist(), "H": w.H, "Hkv": w.Hkv,
-        "d": w.d, "causal": w.causal,
-        "roofline": {"bound": "mfma", "kernel": "prefill_exact_varlen", "achieved": achieved,
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "kernel_ms": kms,
-                     "traffic": measured_traffic("prefill_exact_varlen",
-                                                 ["prefill_exact.hip", "cdna4.hpp"])},
+        "workload": w.name, "value": flops / (st["mean"] * 1e-3) / 1e12, "unit": "TFLOP/s",
+        "ms_per_step": st["mean"], "step_ms": st, "seqlens": inp["seqlens"].tolist(),
+        "H": w.H, "Hkv": w.Hkv, "d": w.d, "causal": w.causal,
+        "roofline": roofline("mfma", "prefill_exact_varlen", flops,
+                             per_kernel["prefill_exact_varlen"], PEAK_BF16_TFLOPS, "TFLOP/s",
+                             traffic=measured_traffic("prefill_exact_varlen", files)),
     }
+
+
+def sage_quant_stats(A, ws, w):
+    """Scale ranges and code counts of the quantisation state one quantised
+    call left in its workspace (read back after the timed region)."""
+    lay = A.attn_sage_workspace_layout(w.B, w.H, w.Hkv, w.N, w.d)
+    nblk = (w.N + 63) // 64
+    npad = nblk * 64
+    BH, BG = w.B * w.H, w.B * w.Hkv
+
+    def f32(name, n):
+        off = lay[name]
+        return ws[off:off + 4 * n].view(torch.float32)
+
+    def u8(name, n):
+        off = lay[name]
+        return ws[off:off + n]
+
+    def rng(t):
+        return {"min": float(t.min()), "max": float(t.max()), "median": float(t.median())}
+
+    qd, kd = f32("qdelta", BH * nblk), f32("kdelta", BG * nblk)
+    vs, km = f32("vscale", BG * w.d), f32("kmean", BG * w.d)
+    qh = u8("qhat", BH * npad * w.d).view(torch.int8).view(BH, npad, w.d)[:, :w.N]
+    kh = u8("khat", BG * npad * w.d).view(torch.int8).view(BG, npad, w.d)[:, :w.N]
+    vh = u8("vhatT", BG * w.d * npad).view(BG, w.d, npad)[:, :, :w.N]
+    mag = vh & 0x7F  # E4M3 magnitude code: 0x7E is 448, codes below 8 subnormal
+    nv = vh.numel()
+    return {
+        "q_scale": rng(qd), "k_scale": rng(kd), "v_scale": rng(vs), "k_mean": rng(km),
+        "int8_q_at_127": int((qh.abs() == 127).sum()), "int8_q_codes": qh.numel(),
+        "int8_k_at_127": int((kh.abs() == 127).sum()), "int8_k_codes": kh.numel(),
+        "fp8_v_at_448": int((mag == 0x7E).sum()), "fp8_v_nan_codes": int((mag == 0x7F).sum()),
+        "fp8_v_subnormal": int(((mag > 0) & (mag < 8)).sum()),
+        "fp8_v_zero": int((mag == 0).sum()), "fp8_v_codes": nv,
+        "note": "a code at +-127 / +-448 is a value at its block's or channel's max|x| (the "
+                "scale maps it there): none beyond the range by construction; P codes are "
+                "E4M3(448 p) with p <= 1 against the exact running max, so P never saturates",
+    }
+
+
+def bench_sage(args, stream):
+    import softmax_attention_attn_amd as A
+    w = workloads.WORKLOADS["sage_prefill"]
+    inp = workloads.make(w)
+    q, k, v = inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda()
+    del inp
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    ws = torch.empty((A.attn_fwd_workspace_size(w.B, w.H, w.Hkv, w.N, w.d, A.MODES["sage"]),),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        A.fwd(q, k, v, causal=w.causal, mode="sage", o=o, lse=lse, workspace=ws, stream=stream)
+
+    st, per_kernel = time_calls(step, args.steps, args.warmup, stream)
+    ops = w.flops()
+    files = ["sage.hip", "cdna4.hpp"]
+    return {
+        "workload": w.name, "value": ops / (st["mean"] * 1e-3) / 1e12, "unit": "TOP/s",
+        "ms_per_step": st["mean"], "step_ms": st,
+        "note": "INT8 QK^T + FP8 PV MFMA; value includes the quantisation prologue kernels, "
+                "the roofline the fused attention kernel",
+        "kernels_ms": per_kernel,
+        "quant_stats": sage_quant_stats(A, ws, w),
+        "error_budget": sage_error_budget(),
+        "roofline": roofline("mfma", "sage_attn", ops, per_kernel["sage_attn"],
+                             PEAK_FP8_TFLOPS, "TOP/s",
+                             traffic=measured_traffic("sage_attn", files),
+                             counters=measured_util("sage_attn", files)),
+    }
+
+
+def sage_error_budget():
+    """The quantised recipe's error against exact attention split by source,
+    as stored by tests/golden/make_sage_error_budget.py (oracle runs on the
+    CPU; no value here comes from the GPU)."""
+    path = os.path.join(ROOT, "tests", "golden", "sage_error_budget.json")
+    try:
+        return json.load(open(path))
+    except (OSError, ValueError):
+        return None
 
 
 def bench_decode(args, stream):
@@ -224,27 +376,30 @@ def bench_decode(args, stream):
         A.decode(q, k, v, seqlens, split_tokens=w.split_tokens, o=o, lse=lse, workspace=ws,
                  stream=stream)
 
-    ms, per_kernel = time_calls(step, max(args.steps, 20), args.warmup, stream)
+    st, per_kernel = time_calls(step, args.steps, args.warmup, stream)
     # algorithmic bytes: every valid K and V row once, q, o (bf16) and lse (fp32)
     alg_bytes = sum_len * w.Hkv * w.d * 2 * 2 + w.B * w.H * w.d * 2 * 2 + w.B * w.H * 4
+    files = ["decode.hip", "cdna4.hpp"]
 
-    def result(ms, per_kernel, kernel, name, extra):
-        kms = per_kernel[kernel][0]
-        achieved = alg_bytes / (kms * 1e-3) / 1e9
+    def result(st, per_kernel, split, name, extra):
+        merge = "decode_merge"
+        call = {"mean": per_kernel[split]["mean"] + per_kernel[merge]["mean"],
+                "median": per_kernel[split]["median"] + per_kernel[merge]["median"]}
+        split_only = alg_bytes / (per_kernel[split]["mean"] * 1e-3) / 1e9
         r = {
-            "workload": name, "value": alg_bytes / (ms * 1e-3) / 1e9, "unit": "GB/s",
-            "ms_per_step": ms, "sum_seqlen": sum_len, "algorithmic_bytes": alg_bytes,
-            "kernels_ms": {k_: t for k_, (t, _) in per_kernel.items()},
-            "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved,
-                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": achieved / PEAK_HBM_GBS, "kernel_ms": kms,
-                         "traffic": measured_traffic(kernel, ["decode.hip", "cdna4.hpp"]),
-                         "counters": measured_util(kernel, ["decode.hip", "cdna4.hpp"])},
+            "workload": name, "value": alg_bytes / (st["mean"] * 1e-3) / 1e9, "unit": "GB/s",
+            "ms_per_step": st["mean"], "step_ms": st, "sum_seqlen": sum_len,
+            "algorithmic_bytes": alg_bytes, "kernels_ms": per_kernel,
+            "roofline": roofline(
+                "hbm", "%s + %s" % (split, merge), alg_bytes, call, PEAK_HBM_GBS, "GB/s",
+                traffic=summed_traffic((split, merge), files),
+                counters=measured_util(split, files),
+                split_kernel_only={"achieved": split_only, "frac": split_only / PEAK_HBM_GBS}),
         }
         r.update(extra)
         return r
 
-    res = result(ms, per_kernel, "decode_split", w.name, {})
+    res = result(st, per_kernel, "decode_split", w.name, {})
     # the same caches spread over a pool of 16-row pages in a random order
     ps = 16
     table, num_pages = workloads.make_page_table(seqlens.cpu(), ps, seed=77, spare_pages=0,
@@ -259,41 +414,15 @@ def bench_decode(args, stream):
         A.decode_paged(q, kp, vp, table, seqlens, split_tokens=w.split_tokens, o=o, lse=lse,
                        workspace=ws, stream=stream)
 
-    ms_p, per_kernel_p = time_calls(step_paged, max(args.steps, 20), args.warmup, stream)
-    res["paged"] = result(ms_p, per_kernel_p, "decode_split_paged", w.name + "_paged16",
+    st_p, per_kernel_p = time_calls(step_paged, args.steps, args.warmup, stream)
+    res["paged"] = result(st_p, per_kernel_p, "decode_split_paged", w.name + "_paged16",
                           {"page_size": ps, "num_pages": num_pages})
     return res
 
 
-def bench_sage(args, stream):
-    import softmax_attention_attn_amd as A
-    w = workloads.WORKLOADS["sage_prefill"]
-    inp = workloads.make(w)
-    q, k, v = inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda()
-    del inp
-    o = torch.empty_like(q)
-    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
-    ws = torch.empty((A.attn_fwd_workspace_size(w.B, w.H, w.Hkv, w.N, w.d, A.MODES["sage"]),),
-                     dtype=torch.uint8, device="cuda")
-
-    def step():
-        A.fwd(q, k, v, causal=w.causal, mode="sage", o=o, lse=lse, workspace=ws, stream=stream)
-
-    ms, per_kernel = time_calls(step, max(5, args.steps // 2), args.warmup, stream)
-    ops = w.flops()
-    kms = per_kernel["sage_attn"][0]
-    achieved = ops / (kms * 1e-3) / 1e12
-    return {
-        "workload": w.name, "value": ops / (ms * 1e-3) / 1e12, "unit": "TOP/s",
-        "ms_per_step": ms, "note": "INT8 QK^T + FP8 PV MFMA; value includes the quantisation "
-                                   "prologue kernels, the roofline the fused attention kernel",
-        "kernels_ms": {k_: t for k_, (t, _) in per_kernel.items()},
-        "roofline": {"bound": "mfma", "kernel": "sage_attn", "achieved": achieved,
-                     "peak": PEAK_FP8_TFLOPS, "unit": "TOP/s", "frac": achieved / PEAK_FP8_TFLOPS,
-                     "kernel_ms": kms,
-                     "traffic": measured_traffic("sage_attn", ["sage.hip", "cdna4.hpp"]),
-                     "counters": measured_util("sage_attn", ["sage.hip", "cdna4.hpp"])},
-    }
+def host_cores():
+    return {"affinity": len(os.sched_getaffinity(0)), "os_cpu_count": os.cpu_count(),
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
 
 
 def cpu_baseline(w, q, k, v):
@@ -310,10 +439,15 @@ def cpu_baseline(w, q, k, v):
     t0 = time.perf_counter()
     oracle.attn_rows(qb, kb, vb, causal=w.causal, scale=w.scale, rows=rows, threads=threads)
     dt = time.perf_counter() - t0
+    hc = host_cores()
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "host_cores": hc,
             "sample": "fp64 C oracle, every query row of %d of the %d (b,h) slices of %s "
-                      "(%d rows, %.3g FLOP) in %.1f s" % (len(slices), w.B * w.H, w.name,
-                                                         len(rows), flops, dt)}
+                      "(%d rows, %.3g FLOP) in %.1f s on %d threads (OpenMP over rows; the host "
+                      "has %s logical CPUs, %d in this process's affinity mask, and the thread "
+                      "count is capped by OMP_NUM_THREADS=%s)" % (
+                          len(slices), w.B * w.H, w.name, len(rows), flops, dt, threads,
+                          hc["os_cpu_count"], hc["affinity"], hc["omp_num_threads"])}
 
 
 def calibrate_copy():
@@ -332,16 +466,18 @@ def calibrate_copy():
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "bwd", "varlen", "decode", "sage"],
-                    default=None)
+    ap.add_argument("--only", choices=LEGS, default=None)
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(requested --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs an MI355X GPU", file=sys.stderr)
@@ -351,30 +487,55 @@ def main():
         return
     stream = torch.cuda.current_stream()
     out = {}
-    pre = None
-    if args.only in (None, "prefill"):
-        log("prefill: llm_prefill")
-        pre = bench_prefill(args, stream)
-        log("prefill %.3f ms/step, %.1f TFLOP/s" % (pre["ms_per_step"], pre["value"]))
-    if args.only in (None, "bwd"):
+    pre = pre_inp = None
+
+    def want(leg):
+        return args.only in (None, leg)
+
+    if want("prefill"):
+        log("prefill: llm_prefill causal")
+        pre, pre_inp = bench_exact(args, stream, "llm_prefill", "prefill_exact")
+        log("prefill %.4f ms/step (median %.4f), %.1f TFLOP/s, kernel frac %.3f" % (
+            pre["ms_per_step"], pre["step_ms"]["median"], pre["value"],
+            pre["roofline"]["frac"]))
+    if want("noncausal"):
+        log("noncausal: llm_prefill without the mask")
+        nc, _ = bench_exact(args, stream, "llm_prefill", "prefill_exact_noncausal", causal=False)
+        log("noncausal %.4f ms/step, %.1f TFLOP/s" % (nc["ms_per_step"], nc["value"]))
+        out["noncausal"] = nc
+    if want("tiny"):
+        log("tiny: tiny_exact")
+        tn = bench_tiny(args, stream)
+        log("tiny median %.1f us per call (kernel %.1f us)" % (tn["latency_us_median"],
+                                                               tn["kernel_us_median"]))
+        out["tiny"] = tn
+    if want("long"):
+        log("long: long_prefill causal with outliers")
+        lg, _ = bench_exact(args, stream, "long_prefill", "prefill_exact_long")
+        lg["target_ms"] = 1.76e13 / (0.6 * PEAK_BF16_TFLOPS * 1e12) * 1e3
+        log("long %.3f ms/step, %.1f TFLOP/s (frac %.3f)" % (lg["ms_per_step"], lg["value"],
+                                                              lg["roofline"]["frac"]))
+        out["long"] = lg
+        torch.cuda.empty_cache()
+    if want("bwd"):
         log("bwd: llm_prefill backward")
         bw = bench_bwd(args, stream)
         log("bwd %.3f ms/step, %.1f TFLOP/s" % (bw["ms_per_step"], bw["value"]))
         out["bwd"] = bw
         torch.cuda.empty_cache()
-    if args.only in (None, "varlen"):
+    if want("varlen"):
         log("varlen: varlen_prefill")
         vl = bench_varlen(args, stream)
         log("varlen %.3f ms/step, %.1f TFLOP/s" % (vl["ms_per_step"], vl["value"]))
         out["varlen"] = vl
-    if args.only in (None, "sage"):
+    if want("sage"):
         log("sage: sage_prefill")
         sg = bench_sage(args, stream)
         log("sage %.3f ms/step, %.1f TOP/s (attention kernel %.1f TOP/s)" % (
             sg["ms_per_step"], sg["value"], sg["roofline"]["achieved"]))
         out["sage"] = sg
         torch.cuda.empty_cache()
-    if args.only in (None, "decode"):
+    if want("decode"):
         log("decode: gqa_decode")
         dec = bench_decode(args, stream)
         log("decode %.3f ms/step, %.1f GB/s; paged (16-row pages) %.3f ms/step, %.1f GB/s" % (
@@ -385,21 +546,22 @@ def main():
     if pre is None:
         print(json.dumps(out))
         return
-    w = pre["workload"]
     line = {
         "metric": "attn fwd TFLOPS & % MFMA peak (prefill); decode HBM GB/s & % peak",
         "value": round(pre["value"], 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(pre["ms_per_step"], 4),
+        "step_ms": pre["step_ms"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.Hkv, "N": w.N, "d": w.d,
-                   "causal": w.causal, "out": "bf16 O + fp32 LSE"},
+        "config": {"workload": pre["workload"], "B": pre["B"], "H": pre["H"], "Hkv": pre["Hkv"],
+                   "N": pre["N"], "d": pre["d"], "causal": pre["causal"], "out": pre["out"]},
         "roofline": pre["roofline"],
     }
     line.update(out)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        line["cpu_baseline"] = cpu_baseline(w, *pre["inputs"])
+        w = workloads.WORKLOADS["llm_prefill"]
+        line["cpu_baseline"] = cpu_baseline(w, pre_inp["q"], pre_inp["k"], pre_inp["v"])
     print(json.dumps(line))
 
 

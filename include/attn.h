@@ -100,6 +100,43 @@ attn_status attn_fwd(const void *q, const void *k, const void *v, void *o, float
 size_t attn_fwd_workspace_size(int B, int H, int Hkv, int N, int d, int mode);
 
 /*
+ * The quantisation state a quantised-mode attn_fwd call leaves in its
+ * workspace, for inspecting the recipe's numeric path (scale ranges, codes at
+ * the ends of their ranges): the "cuda-kernel-pretrain" page's practice list
+ * asks that a low-precision path expose numeric counters such as scale
+ * distributions and overflow rates.  With nblk = ceil(N / 64) and
+ * Npad = 64 * nblk, the pieces are (row-major):
+ *   ATTN_SAGE_WS_KMEAN   fp32 [B*Hkv][d]        per-channel mean of K (Smooth-K)
+ *   ATTN_SAGE_WS_VSCALE  fp32 [B*Hkv][d]        V scale max|V| / 448 per channel
+ *   ATTN_SAGE_WS_QDELTA  fp32 [B*H][nblk]       Q scale max|Q| / 127 per 64-token block
+ *   ATTN_SAGE_WS_KDELTA  fp32 [B*Hkv][nblk]     the same for K - kmean
+ *   ATTN_SAGE_WS_QHAT    int8 [B*H][Npad][d]    quantised Q (rows >= N are 0)
+ *   ATTN_SAGE_WS_KHAT    int8 [B*Hkv][Npad][d]  quantised K - kmean
+ *   ATTN_SAGE_WS_VHATT   E4M3 [B*Hkv][d][Npad]  quantised V, feature-major
+ * and scratch of the kernels (the other enumerators).  Offsets are in bytes
+ * from the start of the workspace.
+ */
+typedef enum {
+    ATTN_SAGE_WS_KSUM_PART = 0,
+    ATTN_SAGE_WS_VMAX_PART,
+    ATTN_SAGE_WS_KMEAN,
+    ATTN_SAGE_WS_VSCALE,
+    ATTN_SAGE_WS_VINV,
+    ATTN_SAGE_WS_QDELTA,
+    ATTN_SAGE_WS_KDELTA,
+    ATTN_SAGE_WS_QKDOT,
+    ATTN_SAGE_WS_QHAT,
+    ATTN_SAGE_WS_KHAT,
+    ATTN_SAGE_WS_VHATT,
+    ATTN_SAGE_WS_COUNT
+} attn_sage_ws_piece;
+
+/* Fills offsets[0 .. ATTN_SAGE_WS_COUNT-1] with the byte offset of each piece
+ * for these sizes.  ATTN_ERR_INVALID_ARG for a null offsets or invalid sizes
+ * (as attn_fwd_workspace_size). */
+attn_status attn_sage_workspace_layout(int B, int H, int Hkv, int N, int d, size_t *offsets);
+
+/*
  * Attention forward over a packed batch of variable-length sequences (the
  * exact mode only): each sequence attends to its own tokens, with the same
  * computation as attn_fwd applied sequence by sequence.  Packing without
@@ -179,8 +216,9 @@ size_t attn_decode_workspace_size(int B, int H, int N_max, int d, int split_toke
  *              [0, num_pages); the kernels clamp others into that range
  *              (the result is then unspecified, but no access leaves the pool).
  *   seqlens    device int32 [B]; values are clamped to [1, max_pages * page_size].
- *   page_size  a power of two, >= 16 and >= split_tokens / 64 (a chunk spans
- *              at most 64 pages).
+ *   page_size  a power of two, >= 16, such that a chunk touches at most 64
+ *              pages: ceil((split_tokens + page_size - g) / page_size) <= 64
+ *              with g = gcd(split_tokens, page_size).
  *   other arguments as for attn_decode (N_max = max_pages * page_size).
  *   workspace  at least attn_decode_workspace_size(B, H, max_pages * page_size,
  *              d, split_tokens) bytes.
@@ -241,6 +279,13 @@ const char *attn_last_error(void);
  */
 attn_status attn_profiler_enable(int enable);
 int attn_profiler_read(char *names, int name_stride, double *total_ms, int *launches, int cap);
+
+/* The recorded launches one by one, in launch order: for i < returned count,
+ * names + i*name_stride holds the kernel name and ms[i] its elapsed time.
+ * Waits for the events like attn_profiler_read and clears the record (launches
+ * beyond cap are dropped).  The events come from a pool created by
+ * attn_profiler_enable, so recording creates none while the pool lasts. */
+int attn_profiler_launches(char *names, int name_stride, float *ms, int cap);
 
 #ifdef __cplusplus
 }

@@ -38,7 +38,8 @@ MODES = {"exact": ATTN_MODE_EXACT_BF16, "sage": ATTN_MODE_SAGE_QK_I8_BLK64_PV_FP
 EXPORTS = ("attn_fwd", "attn_fwd_workspace_size", "attn_fwd_varlen", "attn_bwd",
            "attn_bwd_workspace_size", "attn_decode", "attn_decode_workspace_size",
            "attn_decode_paged", "attn_status_string", "attn_last_error",
-           "attn_profiler_enable", "attn_profiler_read")
+           "attn_profiler_enable", "attn_profiler_read", "attn_profiler_launches",
+           "attn_sage_workspace_layout")
 
 
 class AttnError(RuntimeError):
@@ -79,6 +80,10 @@ def _load():
     lib.attn_profiler_read.restype = i
     lib.attn_profiler_read.argtypes = [ctypes.c_char_p, i, ctypes.POINTER(ctypes.c_double),
                                        ctypes.POINTER(ctypes.c_int), i]
+    lib.attn_profiler_launches.restype = i
+    lib.attn_profiler_launches.argtypes = [ctypes.c_char_p, i, ctypes.POINTER(ctypes.c_float), i]
+    lib.attn_sage_workspace_layout.restype = i
+    lib.attn_sage_workspace_layout.argtypes = [i, i, i, i, i, ctypes.POINTER(sz)]
     return lib
 
 
@@ -179,6 +184,29 @@ def attn_profiler_read(cap: int = 16, name_len: int = 64) -> dict:
     return out
 
 
+def attn_profiler_launches(cap: int = 4096, name_len: int = 64) -> list:
+    """[(kernel name, ms)] of the launches recorded since the profiler was
+    enabled or last read, in launch order."""
+    names = ctypes.create_string_buffer(cap * name_len)
+    ms = (ctypes.c_float * cap)()
+    n = _lib.attn_profiler_launches(names, name_len, ms, cap)
+    if n < 0:
+        _check(n)
+    return [(names.raw[j * name_len:(j + 1) * name_len].split(b"\0", 1)[0].decode(), ms[j])
+            for j in range(n)]
+
+
+SAGE_WS_PIECES = ("ksum_part", "vmax_part", "kmean", "vscale", "vinv", "qdelta", "kdelta",
+                  "qkdot", "qhat", "khat", "vhatT")
+
+
+def attn_sage_workspace_layout(B, H, Hkv, N, d) -> dict:
+    """{piece name: byte offset} of the quantised mode's workspace."""
+    off = (ctypes.c_size_t * len(SAGE_WS_PIECES))()
+    _check(_lib.attn_sage_workspace_layout(B, H, Hkv, N, d, off))
+    return dict(zip(SAGE_WS_PIECES, off))
+
+
 # ----------------------------------------------------------------- tensor API
 
 def _need(t, name, dtype, ndim):
@@ -192,6 +220,42 @@ def _need(t, name, dtype, ndim):
         raise ValueError("%s must have %d dims, got %s" % (name, ndim, tuple(t.shape)))
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
+
+
+def _need_out(t, name, dtype, shape, device):
+    """A caller-supplied output: a contiguous tensor of exactly this dtype and
+    shape on the inputs' GPU (the kernels write it in full)."""
+    _need(t, name, dtype, len(shape))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if t.device != device:
+        raise ValueError("%s is on %s, the inputs on %s" % (name, t.device, device))
+
+
+def _workspace(ws, need, device):
+    """(pointer, size in bytes) of a workspace: the caller's tensor, checked to
+    be a contiguous tensor on the inputs' GPU of at least ``need`` bytes, or a
+    new uint8 tensor of that size."""
+    if ws is None:
+        ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=device)
+    else:
+        if not isinstance(ws, torch.Tensor):
+            raise TypeError("workspace must be a torch tensor")
+        if ws.device != device:
+            raise ValueError("workspace is on %s, the inputs on %s" % (ws.device, device))
+        if not ws.is_contiguous():
+            raise ValueError("workspace must be contiguous")
+    nbytes = ws.numel() * ws.element_size()
+    if nbytes < need:
+        raise ValueError("workspace of %d bytes needed, %d given" % (need, nbytes))
+    return ws, nbytes
+
+
+def _out_code(dtype, what="out_dtype"):
+    try:
+        return {torch.bfloat16: ATTN_OUT_BF16, torch.float32: ATTN_OUT_FP32}[dtype]
+    except KeyError:
+        raise TypeError("%s must be torch.bfloat16 or torch.float32, got %s" % (what, dtype))
 
 
 def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, mode: str = "exact",
@@ -211,18 +275,29 @@ def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, mode: str 
         raise ValueError("k/v shape %s does not match q %s" % (tuple(k.shape), tuple(q.shape)))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    if mode not in MODES:
+        raise ValueError("mode must be one of %s" % sorted(MODES))
     m = MODES[mode]
-    o_code = {torch.bfloat16: ATTN_OUT_BF16, torch.float32: ATTN_OUT_FP32}[out_dtype]
+    o_code = _out_code(out_dtype)
+    dev = q.device
+    if k.device != dev or v.device != dev:
+        raise ValueError("q, k and v must be on one GPU")
     if o is None:
-        o = torch.empty((B, H, N, d), dtype=out_dtype, device=q.device)
+        o = torch.empty((B, H, N, d), dtype=out_dtype, device=dev)
+    else:
+        _need_out(o, "o", out_dtype, (B, H, N, d), dev)
     if lse is None and with_lse:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    elif lse is not None:
+        _need_out(lse, "lse", torch.float32, (B, H, N), dev)
     ws_bytes = attn_fwd_workspace_size(B, H, Hkv, N, d, m)
-    if ws_bytes and workspace is None:
-        workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=q.device)
+    ws_ptr, ws_len = None, 0
+    if ws_bytes or workspace is not None:
+        workspace, ws_len = _workspace(workspace, ws_bytes, dev)
+        ws_ptr = _ptr(workspace)
     st = _lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, N, d,
-                       int(bool(causal)), float(scale), m, o_code, _ptr(workspace),
-                       workspace.numel() if workspace is not None else 0, _stream(stream))
+                       int(bool(causal)), float(scale), m, o_code, ws_ptr, ws_len,
+                       _stream(stream))
     _check(st)
     return o, lse
 
@@ -244,19 +319,27 @@ def bwd(q, k, v, o, lse, dout, *, causal: bool = False, scale: float | None = No
         raise ValueError("shapes do not agree")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    g_code = {torch.bfloat16: ATTN_OUT_BF16, torch.float32: ATTN_OUT_FP32}[grad_dtype]
+    g_code = _out_code(grad_dtype, "grad_dtype")
+    dev = q.device
+    for t, name in ((k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (lse, "lse")):
+        if t.device != dev:
+            raise ValueError("%s is on %s, q on %s" % (name, t.device, dev))
     if dq is None:
-        dq = torch.empty((B, H, N, d), dtype=grad_dtype, device=q.device)
+        dq = torch.empty((B, H, N, d), dtype=grad_dtype, device=dev)
+    else:
+        _need_out(dq, "dq", grad_dtype, (B, H, N, d), dev)
     if dk is None:
-        dk = torch.empty((B, Hkv, N, d), dtype=grad_dtype, device=q.device)
+        dk = torch.empty((B, Hkv, N, d), dtype=grad_dtype, device=dev)
+    else:
+        _need_out(dk, "dk", grad_dtype, (B, Hkv, N, d), dev)
     if dv is None:
-        dv = torch.empty((B, Hkv, N, d), dtype=grad_dtype, device=q.device)
-    ws_bytes = attn_bwd_workspace_size(B, H, N)
-    if workspace is None:
-        workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=q.device)
+        dv = torch.empty((B, Hkv, N, d), dtype=grad_dtype, device=dev)
+    else:
+        _need_out(dv, "dv", grad_dtype, (B, Hkv, N, d), dev)
+    workspace, ws_len = _workspace(workspace, attn_bwd_workspace_size(B, H, N), dev)
     st = _lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
                        _ptr(dk), _ptr(dv), B, H, Hkv, N, d, int(bool(causal)), float(scale),
-                       g_code, _ptr(workspace), workspace.numel(), _stream(stream))
+                       g_code, _ptr(workspace), ws_len, _stream(stream))
     _check(st)
     return dq, dk, dv
 
@@ -281,15 +364,35 @@ def fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, *, causal: bool = False,
     B = cu_seqlens.shape[0] - 1
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    o_code = {torch.bfloat16: ATTN_OUT_BF16, torch.float32: ATTN_OUT_FP32}[out_dtype]
+    o_code = _out_code(out_dtype)
+    dev = q.device
+    for t, name in ((k, "k"), (v, "v"), (cu_seqlens, "cu_seqlens")):
+        if t.device != dev:
+            raise ValueError("%s is on %s, q on %s" % (name, t.device, dev))
     if o is None:
-        o = torch.empty((total, H, d), dtype=out_dtype, device=q.device)
+        o = torch.empty((total, H, d), dtype=out_dtype, device=dev)
+    else:
+        _need_out(o, "o", out_dtype, (total, H, d), dev)
     if lse is None and with_lse:
-        lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
+        lse = torch.empty((H, total), dtype=torch.float32, device=dev)
+    elif lse is not None:
+        _need_out(lse, "lse", torch.float32, (H, total), dev)
     st = _lib.attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens),
                               B, H, Hkv, total, int(max_seqlen), d, int(bool(causal)),
                               float(scale), ATTN_MODE_EXACT_BF16, o_code, _stream(stream))
     _check(st)
+    return o, lse
+
+
+def _decode_outputs(o, lse, with_lse, out_dtype, B, H, d, dev):
+    if o is None:
+        o = torch.empty((B, H, d), dtype=out_dtype, device=dev)
+    else:
+        _need_out(o, "o", out_dtype, (B, H, d), dev)
+    if lse is None and with_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    elif lse is not None:
+        _need_out(lse, "lse", torch.float32, (B, H), dev)
     return o, lse
 
 
@@ -309,17 +412,17 @@ def decode(q, k_cache, v_cache, seqlens, *, scale: float | None = None,
         raise ValueError("seqlens must have B entries")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    o_code = {torch.bfloat16: ATTN_OUT_BF16, torch.float32: ATTN_OUT_FP32}[out_dtype]
-    if o is None:
-        o = torch.empty((B, H, d), dtype=out_dtype, device=q.device)
-    if lse is None and with_lse:
-        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
-    ws_bytes = attn_decode_workspace_size(B, H, N_max, d, split_tokens)
-    if workspace is None:
-        workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=q.device)
+    o_code = _out_code(out_dtype)
+    dev = q.device
+    for t, name in ((k_cache, "k_cache"), (v_cache, "v_cache"), (seqlens, "seqlens")):
+        if t.device != dev:
+            raise ValueError("%s is on %s, q on %s" % (name, t.device, dev))
+    o, lse = _decode_outputs(o, lse, with_lse, out_dtype, B, H, d, dev)
+    workspace, ws_len = _workspace(
+        workspace, attn_decode_workspace_size(B, H, N_max, d, split_tokens), dev)
     st = _lib.attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(o),
                           _ptr(lse), B, H, Hkv, N_max, d, float(scale), ATTN_MODE_EXACT_BF16,
-                          o_code, int(split_tokens), _ptr(workspace), workspace.numel(),
+                          o_code, int(split_tokens), _ptr(workspace), ws_len,
                           _stream(stream))
     _check(st)
     return o, lse
@@ -346,18 +449,19 @@ def decode_paged(q, k_pages, v_pages, block_table, seqlens, *, scale: float | No
     max_pages = block_table.shape[1]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    o_code = {torch.bfloat16: ATTN_OUT_BF16, torch.float32: ATTN_OUT_FP32}[out_dtype]
-    if o is None:
-        o = torch.empty((B, H, d), dtype=out_dtype, device=q.device)
-    if lse is None and with_lse:
-        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
-    ws_bytes = attn_decode_workspace_size(B, H, max_pages * page_size, d, split_tokens)
-    if workspace is None:
-        workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=q.device)
+    o_code = _out_code(out_dtype)
+    dev = q.device
+    for t, name in ((k_pages, "k_pages"), (v_pages, "v_pages"), (block_table, "block_table"),
+                    (seqlens, "seqlens")):
+        if t.device != dev:
+            raise ValueError("%s is on %s, q on %s" % (name, t.device, dev))
+    o, lse = _decode_outputs(o, lse, with_lse, out_dtype, B, H, d, dev)
+    workspace, ws_len = _workspace(
+        workspace, attn_decode_workspace_size(B, H, max_pages * page_size, d, split_tokens), dev)
     st = _lib.attn_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
                                 _ptr(seqlens), _ptr(o), _ptr(lse), B, H, Hkv, num_pages,
                                 page_size, max_pages, d, float(scale), ATTN_MODE_EXACT_BF16,
-                                o_code, int(split_tokens), _ptr(workspace), workspace.numel(),
+                                o_code, int(split_tokens), _ptr(workspace), ws_len,
                                 _stream(stream))
     _check(st)
     return o, lse

@@ -47,12 +47,42 @@ bool valid_scale(float s) { return std::isfinite(s) && s > 0.f; }
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // ---------------------------------------------------------------- profiler
+// Events come from a pool created when the profiler is enabled, so that the
+// timed region itself creates no events; the pool grows only if a run
+// records more launches than it holds.
 struct ProfEvent {
-    std::string name;
+    const char *name;  // a string literal of the launcher
     hipEvent_t begin, end;
 };
+constexpr size_t kProfReserve = 1024;  // launches recorded without growing the pool
 thread_local bool g_prof_on = false;
-thread_local std::vector<ProfEvent> g_prof;
+thread_local std::vector<ProfEvent> g_prof;  // pool; the first g_prof_used are recorded
+thread_local size_t g_prof_used = 0;
+
+bool prof_grow(size_t n)
+{
+    while (g_prof.size() < n) {
+        ProfEvent ev{nullptr, nullptr, nullptr};
+        if (hipEventCreate(&ev.begin) != hipSuccess)
+            return false;
+        if (hipEventCreate(&ev.end) != hipSuccess) {
+            hipEventDestroy(ev.begin);
+            return false;
+        }
+        g_prof.push_back(ev);
+    }
+    return true;
+}
+
+void prof_release()
+{
+    for (auto &ev : g_prof) {
+        hipEventDestroy(ev.begin);
+        hipEventDestroy(ev.end);
+    }
+    g_prof.clear();
+    g_prof_used = 0;
+}
 
 }  // namespace
 
@@ -62,18 +92,18 @@ void prof_begin(const char *name, hipStream_t s)
 {
     if (!g_prof_on)
         return;
-    ProfEvent ev{name, nullptr, nullptr};
-    if (hipEventCreate(&ev.begin) != hipSuccess || hipEventCreate(&ev.end) != hipSuccess)
+    if (g_prof_used == g_prof.size() && !prof_grow(g_prof.size() + kProfReserve))
         return;
+    ProfEvent &ev = g_prof[g_prof_used++];
+    ev.name = name;
     hipEventRecord(ev.begin, s);
-    g_prof.push_back(ev);
 }
 
 void prof_end(hipStream_t s)
 {
-    if (!g_prof_on || g_prof.empty())
+    if (!g_prof_on || g_prof_used == 0)
         return;
-    hipEventRecord(g_prof.back().end, s);
+    hipEventRecord(g_prof[g_prof_used - 1].end, s);
 }
 
 }  // namespace attn
@@ -168,6 +198,17 @@ size_t attn_fwd_workspace_size(int B, int H, int Hkv, int N, int d, int mode)
     if (mode == ATTN_MODE_SAGE_QK_I8_BLK64_PV_FP8_E4M3)
         return attn::sage_workspace_bytes(B, H, Hkv, N, d);
     return 0;
+}
+
+attn_status attn_sage_workspace_layout(int B, int H, int Hkv, int N, int d, size_t *offsets)
+{
+    if (!offsets)
+        return fail(ATTN_ERR_INVALID_ARG, "offsets must be non-null");
+    if (B <= 0 || H <= 0 || Hkv <= 0 || N <= 0 || d <= 0 || H % Hkv != 0)
+        return fail(ATTN_ERR_INVALID_ARG, "invalid sizes (B=%d H=%d Hkv=%d N=%d d=%d)", B, H, Hkv,
+                    N, d);
+    attn::sage_workspace_layout(B, H, Hkv, N, d, offsets);
+    return ok();
 }
 
 attn_status attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B,
@@ -341,10 +382,24 @@ attn_status attn_decode_paged(const void *q, const void *k_pages, const void *v_
                     num_pages, max_pages);
     if (page_size <= 0 || (page_size & (page_size - 1)) != 0)
         return fail(ATTN_ERR_INVALID_ARG, "page_size=%d is not a power of two", page_size);
-    if (page_size < 16 || (split_tokens > 0 && (long long)page_size * 64 < split_tokens))
-        return fail(ATTN_ERR_UNSUPPORTED,
-                    "page_size=%d (supported: >= 16 and >= split_tokens/64 = %d)", page_size,
-                    split_tokens / 64);
+    if (page_size < 16)
+        return fail(ATTN_ERR_UNSUPPORTED, "page_size=%d (supported: >= 16)", page_size);
+    if (split_tokens > 0) {
+        // pages touched by a chunk [c*S, c*S + S) in the worst case over c:
+        // ceil((S + P - gcd(S, P)) / P); a chunk's page numbers are held one
+        // per lane, so at most 64
+        long long g = split_tokens, r = page_size;
+        while (r) {
+            const long long t = g % r;
+            g = r;
+            r = t;
+        }
+        const long long span = (split_tokens + page_size - g + page_size - 1) / page_size;
+        if (span > 64)
+            return fail(ATTN_ERR_UNSUPPORTED,
+                        "page_size=%d with split_tokens=%d: a chunk can touch %lld pages "
+                        "(supported: 64)", page_size, split_tokens, span);
+    }
     const long long n_max = (long long)max_pages * page_size;
     if (n_max > 0x7fffffffLL)
         return fail(ATTN_ERR_UNSUPPORTED, "max_pages * page_size = %lld exceeds 2^31 - 1", n_max);
@@ -363,12 +418,15 @@ attn_status attn_decode_paged(const void *q, const void *k_pages, const void *v_
 
 attn_status attn_profiler_enable(int enable)
 {
-    for (auto &ev : g_prof) {
-        hipEventDestroy(ev.begin);
-        hipEventDestroy(ev.end);
+    prof_release();
+    g_prof_on = false;
+    if (enable) {
+        if (!prof_grow(kProfReserve)) {
+            prof_release();
+            return fail(ATTN_ERR_HIP, "profiler: hipEventCreate failed");
+        }
+        g_prof_on = true;
     }
-    g_prof.clear();
-    g_prof_on = enable != 0;
     return ok();
 }
 
@@ -380,7 +438,8 @@ int attn_profiler_read(char *names, int name_stride, double *total_ms, int *laun
     std::vector<double> tot;
     std::vector<int> cnt;
     attn_status st = ATTN_OK;
-    for (auto &ev : g_prof) {
+    for (size_t j = 0; j < g_prof_used; ++j) {
+        const ProfEvent &ev = g_prof[j];
         float ms = 0.f;
         hipError_t e = hipEventSynchronize(ev.end);
         if (e == hipSuccess)
@@ -400,11 +459,7 @@ int attn_profiler_read(char *names, int name_stride, double *total_ms, int *laun
         tot[i] += ms;
         cnt[i] += 1;
     }
-    for (auto &ev : g_prof) {
-        hipEventDestroy(ev.begin);
-        hipEventDestroy(ev.end);
-    }
-    g_prof.clear();
+    g_prof_used = 0;  // the pool is kept for the next run
     if (st != ATTN_OK)
         return st;
     int n = (int)seen.size() < cap ? (int)seen.size() : cap;
@@ -413,6 +468,30 @@ int attn_profiler_read(char *names, int name_stride, double *total_ms, int *laun
         total_ms[i] = tot[i];
         launches[i] = cnt[i];
     }
+    ok();
+    return n;
+}
+
+int attn_profiler_launches(char *names, int name_stride, float *ms, int cap)
+{
+    if (!names || !ms || name_stride <= 1 || cap <= 0)
+        return fail(ATTN_ERR_INVALID_ARG, "profiler_launches: bad output buffers");
+    const int n = (int)g_prof_used < cap ? (int)g_prof_used : cap;
+    attn_status st = ATTN_OK;
+    for (int j = 0; j < n; ++j) {
+        const ProfEvent &ev = g_prof[j];
+        hipError_t e = hipEventSynchronize(ev.end);
+        if (e == hipSuccess)
+            e = hipEventElapsedTime(&ms[j], ev.begin, ev.end);
+        if (e != hipSuccess) {
+            st = fail(ATTN_ERR_HIP, "profiler_launches: %s", hipGetErrorString(e));
+            break;
+        }
+        std::snprintf(names + (size_t)j * name_stride, name_stride, "%s", ev.name);
+    }
+    g_prof_used = 0;
+    if (st != ATTN_OK)
+        return st;
     ok();
     return n;
 }

@@ -68,6 +68,10 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);  // contiguous or 
 hipError_t launch_sage(const SageArgs &a, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t s);
 size_t sage_workspace_bytes(int B, int H, int Hkv, int N, int d);
+// byte offset of each piece of the quantised mode's workspace (attn.h's
+// attn_sage_ws_piece order, kSageWsPieces entries)
+constexpr int kSageWsPieces = 11;
+void sage_workspace_layout(int B, int H, int Hkv, int N, int d, size_t *offsets);
 
 // Benchmark timing hooks (api.cpp): bracket one kernel launch with events when
 // the profiler is enabled on this thread.

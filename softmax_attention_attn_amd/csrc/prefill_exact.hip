@@ -4,7 +4,7 @@
 // page, §2): one workgroup owns a tile of kBM = 256 queries of one
 // (batch, head); each of its 8 waves keeps the Q fragments of its 32 queries
 // in registers for the whole pass; K and V tiles of kBN = 64 keys stream
-// through a double-buffered LDS stage; an online softmax (running row max m
+// through 4-stage LDS rings; an online softmax (running row max m
 // and row sum l) accumulates O in registers without ever writing scores to
 // memory; causal tiles entirely above the diagonal are never loaded.
 //

@@ -32,6 +32,7 @@
 // operand, and its A operand is the matching 32 bytes of two feature rows of
 // the transposed V tile.  Key tiles equal the 64-token quantisation blocks,
 // so dK is one scalar per tile and dQ one scalar per wave.
+#include "../../include/attn.h"
 #include "attn_internal.hpp"
 #include "cdna4.hpp"
 
@@ -94,28 +95,52 @@ struct SageWs {
     uint8_t *vhatT;    // [BG][D][Npad]  E4M3 codes, feature-major
 };
 
-SageWs carve(void *base, int B, int H, int Hkv, int N, int d)
+// Byte offsets of the workspace pieces, in SageWsPiece order; the last entry
+// is the total size.
+static_assert(ATTN_SAGE_WS_COUNT == kSageWsPieces, "workspace pieces");
+
+void layout(int B, int H, int Hkv, int N, int d, size_t (&off)[kSageWsPieces + 1])
 {
     const size_t BH = (size_t)B * H, BG = (size_t)B * Hkv;
     const size_t nblk = (N + kBlk - 1) / kBlk, Npad = nblk * kBlk;
+    const size_t bytes[kSageWsPieces] = {
+        sizeof(double) * BG * kNCh * d,  // ATTN_SAGE_WS_KSUM_PART
+        sizeof(float) * BG * kNCh * d,   // ATTN_SAGE_WS_VMAX_PART
+        sizeof(float) * BG * d,          // ATTN_SAGE_WS_KMEAN
+        sizeof(float) * BG * d,          // ATTN_SAGE_WS_VSCALE
+        sizeof(float) * BG * d,          // ATTN_SAGE_WS_VINV
+        sizeof(float) * BH * nblk,       // ATTN_SAGE_WS_QDELTA
+        sizeof(float) * BG * nblk,       // ATTN_SAGE_WS_KDELTA
+        sizeof(float) * BH * N,          // ATTN_SAGE_WS_QKDOT
+        BH * Npad * d,                   // ATTN_SAGE_WS_QHAT
+        BG * Npad * d,                   // ATTN_SAGE_WS_KHAT
+        BG * d * Npad,                   // ATTN_SAGE_WS_VHATT
+    };
+    size_t p = 0;
+    for (int i = 0; i < kSageWsPieces; ++i) {
+        off[i] = p;
+        p += align256(bytes[i]);
+    }
+    off[kSageWsPieces] = p;
+}
+
+SageWs carve(void *base, int B, int H, int Hkv, int N, int d)
+{
+    size_t off[kSageWsPieces + 1];
+    layout(B, H, Hkv, N, d, off);
     char *p = (char *)base;
     SageWs w;
-    auto take = [&](size_t bytes) {
-        char *r = p;
-        p += align256(bytes);
-        return r;
-    };
-    w.ksum_part = (double *)take(sizeof(double) * BG * kNCh * d);
-    w.vmax_part = (float *)take(sizeof(float) * BG * kNCh * d);
-    w.kmean = (float *)take(sizeof(float) * BG * d);
-    w.vscale = (float *)take(sizeof(float) * BG * d);
-    w.vinv = (float *)take(sizeof(float) * BG * d);
-    w.qdelta = (float *)take(sizeof(float) * BH * nblk);
-    w.kdelta = (float *)take(sizeof(float) * BG * nblk);
-    w.qkdot = (float *)take(sizeof(float) * BH * N);
-    w.qhat = (int8_t *)take(BH * Npad * d);
-    w.khat = (int8_t *)take(BG * Npad * d);
-    w.vhatT = (uint8_t *)take(BG * d * Npad);
+    w.ksum_part = (double *)(p + off[ATTN_SAGE_WS_KSUM_PART]);
+    w.vmax_part = (float *)(p + off[ATTN_SAGE_WS_VMAX_PART]);
+    w.kmean = (float *)(p + off[ATTN_SAGE_WS_KMEAN]);
+    w.vscale = (float *)(p + off[ATTN_SAGE_WS_VSCALE]);
+    w.vinv = (float *)(p + off[ATTN_SAGE_WS_VINV]);
+    w.qdelta = (float *)(p + off[ATTN_SAGE_WS_QDELTA]);
+    w.kdelta = (float *)(p + off[ATTN_SAGE_WS_KDELTA]);
+    w.qkdot = (float *)(p + off[ATTN_SAGE_WS_QKDOT]);
+    w.qhat = (int8_t *)(p + off[ATTN_SAGE_WS_QHAT]);
+    w.khat = (int8_t *)(p + off[ATTN_SAGE_WS_KHAT]);
+    w.vhatT = (uint8_t *)(p + off[ATTN_SAGE_WS_VHATT]);
     return w;
 }
 
@@ -912,13 +937,17 @@ hipError_t launch_d(const SageArgs &sa, hipStream_t s)
 
 size_t sage_workspace_bytes(int B, int H, int Hkv, int N, int d)
 {
-    const size_t BH = (size_t)B * H, BG = (size_t)B * Hkv;
-    const size_t nblk = (N + kBlk - 1) / kBlk, Npad = nblk * kBlk;
-    return align256(sizeof(double) * BG * kNCh * d) + align256(sizeof(float) * BG * kNCh * d) +
-           align256(sizeof(float) * BG * d) * 3 +
-           align256(sizeof(float) * BH * nblk) + align256(sizeof(float) * BG * nblk) +
-           align256(sizeof(float) * BH * N) + align256(BH * Npad * d) + align256(BG * Npad * d) +
-           align256(BG * d * Npad);
+    size_t off[kSageWsPieces + 1];
+    layout(B, H, Hkv, N, d, off);
+    return off[kSageWsPieces];
+}
+
+void sage_workspace_layout(int B, int H, int Hkv, int N, int d, size_t *offsets)
+{
+    size_t off[kSageWsPieces + 1];
+    layout(B, H, Hkv, N, d, off);
+    for (int i = 0; i < kSageWsPieces; ++i)
+        offsets[i] = off[i];
 }
 
 hipError_t launch_sage(const SageArgs &sa, hipStream_t s)

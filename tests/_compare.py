@@ -3,11 +3,17 @@ from __future__ import annotations
 
 import numpy as np
 
-# Exact mode: max |dO| <= 1e-2 and relative LSE error <= 1e-3, the LSE error
-# taken as |dlse| / max(|lse_ref|, 1).  A bf16 output additionally gets half a
-# bf16 ulp of the reference value, the rounding any bf16 store must make.
+# Exact mode: max |dO| <= 1e-2 and relative LSE error <= 1e-3.
+#  * literal=True (the five stated workloads, where the gate is stated): every
+#    element within 1e-2, and |dlse| / |lse_ref| <= 1e-3; rows whose reference
+#    LSE is within 1e-2 of zero, where a relative error means nothing, get
+#    |dlse| <= 1e-5 instead (the fp32 LSE's own rounding is ~1e-6 there).
+#  * literal=False (small shapes and stress cases): a bf16 output additionally
+#    gets half a bf16 ulp of the reference value, the rounding any bf16 store
+#    must make, and the LSE error is |dlse| / max(|lse_ref|, 1).
 O_ABS_TOL = 1e-2
 LSE_REL_TOL = 1e-3
+LSE_NEAR_ZERO, LSE_ABS_TOL_NEAR_ZERO = 1e-2, 1e-5
 
 
 def bf16_half_ulp(x: np.ndarray) -> np.ndarray:
@@ -17,14 +23,14 @@ def bf16_half_ulp(x: np.ndarray) -> np.ndarray:
 
 
 def check_exact(o_gpu: np.ndarray, o_ref: np.ndarray, lse_gpu, lse_ref, *, bf16_out: bool,
-                what: str = ""):
+                what: str = "", literal: bool = False):
     """Assert the exact-mode tolerances; returns a dict of the measured errors."""
     o_gpu = np.asarray(o_gpu, dtype=np.float64)
     o_ref = np.asarray(o_ref, dtype=np.float64)
     assert o_gpu.shape == o_ref.shape, (o_gpu.shape, o_ref.shape)
     assert np.isfinite(o_gpu).all(), "%s: non-finite output" % what
     err = np.abs(o_gpu - o_ref)
-    bound = O_ABS_TOL + (bf16_half_ulp(o_ref) if bf16_out else 0.0)
+    bound = O_ABS_TOL + (bf16_half_ulp(o_ref) if bf16_out and not literal else 0.0)
     bad = err > bound
     res = {"max_abs_dO": float(err.max()), "n_over_1e-2": int((err > O_ABS_TOL).sum()),
            "n_over_bound": int(bad.sum())}
@@ -34,9 +40,21 @@ def check_exact(o_gpu: np.ndarray, o_ref: np.ndarray, lse_gpu, lse_ref, *, bf16_
         lse_gpu = np.asarray(lse_gpu, dtype=np.float64)
         lse_ref = np.asarray(lse_ref, dtype=np.float64)
         assert np.isfinite(lse_gpu).all(), "%s: non-finite lse" % what
-        rel = np.abs(lse_gpu - lse_ref) / np.maximum(np.abs(lse_ref), 1.0)
-        res["max_rel_dlse"] = float(rel.max())
-        assert rel.max() <= LSE_REL_TOL, "%s: lse rel err %.3g" % (what, rel.max())
+        dl = np.abs(lse_gpu - lse_ref)
+        if literal:
+            near0 = np.abs(lse_ref) < LSE_NEAR_ZERO
+            rel = dl[~near0] / np.abs(lse_ref[~near0])
+            res["max_rel_dlse"] = float(rel.max()) if rel.size else 0.0
+            res["n_lse_near_zero"] = int(near0.sum())
+            if near0.any():
+                res["max_abs_dlse_near_zero"] = float(dl[near0].max())
+                assert dl[near0].max() <= LSE_ABS_TOL_NEAR_ZERO, (
+                    "%s: |dlse| %.3g where |lse| < %g" % (what, dl[near0].max(), LSE_NEAR_ZERO))
+        else:
+            rel = dl / np.maximum(np.abs(lse_ref), 1.0)
+            res["max_rel_dlse"] = float(rel.max())
+        assert res["max_rel_dlse"] <= LSE_REL_TOL, "%s: lse rel err %.3g" % (
+            what, res["max_rel_dlse"])
     return res
 
 

@@ -139,6 +139,9 @@ def _decp(A, **kw):
     (dict(page_size=0), -1), (dict(page_size=24), -1), (dict(page_size=-16), -1),
     (dict(page_size=8), -2),                                   # below 16
     (dict(page_size=16, split_tokens=2048), -2),               # a chunk would span 128 pages
+    # 256-row pages do not divide 16320-key chunks: chunk 1 starts 192 rows into
+    # a page and touches 65 pages
+    (dict(page_size=256, split_tokens=16320), -2),
     (dict(page_size=1 << 20, max_pages=4096), -2),             # 2^32 positions
     (dict(H=7), -1), (dict(split_tokens=100), -1), (dict(mode=1), -2), (dict(d=80), -2),
     (dict(workspace=None), -3), (dict(workspace_bytes=1000), -3),

@@ -60,3 +60,18 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 2 and "one GPU" in r.stderr, (r.returncode, r.stderr[-500:])
+
+
+def test_stats_and_roofline(bench):
+    B, _, _ = bench
+    st = B.stats([1.0, 2.0, 3.0, 4.0, 100.0])
+    assert st["median"] == 3.0 and st["n"] == 5 and st["mean"] == 22.0
+    assert st["p10"] < 2.0 < st["p90"]
+    r = B.roofline("hbm", "k", 8e9, {"mean": 2.0, "median": 1.0}, 8000.0, "GB/s")
+    assert r["achieved"] == 4000.0 and r["frac"] == 0.5 and r["achieved_median"] == 8000.0
+
+
+def test_summed_traffic_needs_every_kernel(bench):
+    B, files, _ = bench
+    assert B.summed_traffic(("bwd_dq", "bwd_dkv"), files) == 110.0
+    assert B.summed_traffic(("bwd_dq", "decode_merge"), files) is None

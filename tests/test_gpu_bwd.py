@@ -105,16 +105,58 @@ def test_bwd_bf16_grads_and_scale(attn):
 
 
 def test_bwd_llm_prefill_slices(attn):
-    """The headline shape (B4 H32 N4096 d128, causal); the oracle checks two
-    whole (b, h) slices (each self-contained: Hkv = H)."""
+    """The headline shape (B4 H32 N4096 d128, causal, bf16 gradients); the
+    oracle checks eight whole (b, h) slices spread over the batch and heads
+    (each self-contained: Hkv = H), stacked into one oracle call."""
     w = workloads.WORKLOADS["llm_prefill"]
     inp = workloads.make(w)
     q, k, v = inp["q"], inp["k"], inp["v"]
     do = workloads.make_prefill(w.B, w.H, w.Hkv, w.N, w.d, seed=1)[0]
     dq, dk, dv = _run(attn, q, k, v, do, True, grad_dtype=torch.bfloat16)
-    for b, h in ((0, 0), (3, 31)):
-        sl = lambda t: t[b:b + 1, h:h + 1].contiguous()
-        ref = _ref(sl(q), sl(k), sl(v), sl(do), True, w.scale)
-        res = check_grads(dq[b:b + 1, h:h + 1], dk[b:b + 1, h:h + 1], dv[b:b + 1, h:h + 1], ref,
-                          "llm_prefill slice %d,%d" % (b, h))
+    slices = ((0, 0), (0, 17), (1, 5), (1, 31), (2, 9), (2, 22), (3, 0), (3, 31))
+    st = lambda t: torch.cat([t[b:b + 1, h:h + 1] for b, h in slices]).contiguous()
+    ref = _ref(st(q), st(k), st(v), st(do), True, w.scale)
+    for i, (b, h) in enumerate(slices):
+        one = tuple(r[i:i + 1] for r in ref)
+        res = check_grads(dq[b:b + 1, h:h + 1], dk[b:b + 1, h:h + 1], dv[b:b + 1, h:h + 1],
+                          one, "llm_prefill slice %d,%d" % (b, h))
         print("llm_prefill", b, h, res)
+
+
+def test_bwd_gqa_headline_size(attn):
+    """GQA at the headline size (B4 H32 Hkv8 N4096 d128 causal, bf16
+    gradients): a kv head's dK/dV sum the gradients of its 4 query heads.
+    Two whole groups, (b, kv head) = (0, 0) and (3, 7), against the oracle."""
+    B, H, Hkv, N, d = 4, 32, 8, 4096, 128
+    q, k, v, _ = workloads.make_prefill(B, H, Hkv, N, d, seed=11)
+    do = workloads.make_prefill(B, H, Hkv, N, d, seed=12)[0]
+    dq, dk, dv = _run(attn, q, k, v, do, True, grad_dtype=torch.bfloat16)
+    G = H // Hkv
+    groups = ((0, 0), (3, 7))
+    stq = lambda t: torch.cat([t[b:b + 1, g * G:(g + 1) * G] for b, g in groups]).contiguous()
+    stk = lambda t: torch.cat([t[b:b + 1, g:g + 1] for b, g in groups]).contiguous()
+    ref = _ref(stq(q), stk(k), stk(v), stq(do), True, 1 / math.sqrt(d))
+    for i, (b, g) in enumerate(groups):
+        one = tuple(r[i:i + 1] for r in ref)
+        res = check_grads(dq[b:b + 1, g * G:(g + 1) * G], dk[b:b + 1, g:g + 1],
+                          dv[b:b + 1, g:g + 1], one, "gqa group %d,%d" % (b, g))
+        print("gqa headline", b, g, res)
+
+
+def test_bwd_deterministic(attn):
+    """Every gradient element has one writer and a fixed accumulation order
+    (no atomics), so two calls on the same inputs agree bit for bit: the
+    headline shape with GQA (H32 Hkv8) and both gradient dtypes."""
+    B, H, Hkv, N, d = 4, 32, 8, 4096, 128
+    q, k, v, _ = workloads.make_prefill(B, H, Hkv, N, d, seed=13)
+    do = workloads.make_prefill(B, H, Hkv, N, d, seed=14)[0]
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    o, lse = attn.fwd(qd, kd, vd, causal=True)
+    for gd in (torch.bfloat16, torch.float32):
+        first = attn.bwd(qd, kd, vd, o, lse, dod, causal=True, grad_dtype=gd)
+        first = [t.clone() for t in first]
+        for _ in range(2):
+            again = attn.bwd(qd, kd, vd, o, lse, dod, causal=True, grad_dtype=gd)
+            torch.cuda.synchronize()
+            for a, b_, name in zip(first, again, ("dq", "dk", "dv")):
+                assert torch.equal(a, b_), (gd, name)

@@ -71,7 +71,7 @@ def test_tiny_exact_workload(attn):
     inp = workloads.make(w)
     o, lse = _run(attn, inp["q"], inp["k"], inp["v"], w.causal, torch.float32)
     o_ref, lse_ref = _oracle_full(inp["q"], inp["k"], inp["v"], w.causal, w.scale)
-    res = check_exact(o, o_ref, lse, lse_ref, bf16_out=False, what=w.name)
+    res = check_exact(o, o_ref, lse, lse_ref, bf16_out=False, what=w.name, literal=True)
     print(w.name, res)
 
 
@@ -171,7 +171,7 @@ def test_lse_optional(attn):
     check_exact(o.float().cpu().numpy(), o_ref, None, None, bf16_out=True, what="no lse")
 
 
-def _sampled_check(attn, w, rows, out_dtype=torch.bfloat16):
+def _sampled_check(attn, w, rows, out_dtype=torch.bfloat16, literal=True):
     """The workload's output against the oracle on the given flat (b, h, i)
     rows, or on every row when rows is None."""
     inp = workloads.make(w)
@@ -185,7 +185,7 @@ def _sampled_check(attn, w, rows, out_dtype=torch.bfloat16):
     o_ref, lse_ref = _oracle_full(q, k, v, w.causal, w.scale, rows=rows)
     o_ref, lse_ref = o_ref.reshape(-1, w.d), lse_ref.reshape(-1)
     return check_exact(o, o_ref, lse, lse_ref, bf16_out=out_dtype == torch.bfloat16,
-                       what=w.name), inp
+                       what=w.name, literal=literal), inp
 
 
 def test_llm_prefill_workload_full(attn):
@@ -201,7 +201,10 @@ def test_long_prefill_workload_sampled(attn):
     """Outlier keys (x20) stress the running-max rescaling; the sample holds
     the rows within 2 of every outlier of head 0, the tile-edge and last rows of
     every head, and 4096 seeded random rows.
-    The fp32-store instantiation must meet max |dO| <= 1e-2 literally."""
+    The fp32-store instantiation must meet max |dO| <= 1e-2 literally; the
+    bf16 store gets half a bf16 ulp on top (a correctly rounded bf16 copy of
+    the exact output already misses 1e-2 wherever |O| >= 4, which this
+    workload's outlier rows reach), and both meet the LSE gate literally."""
     w = workloads.WORKLOADS["long_prefill"]
     base = workloads.sample_rows(w.B, w.H, w.N, n_random=4096, whole_slices=())
     # every row within 2 of an outlier key of kv head 0, in query head 0 (the
@@ -219,7 +222,12 @@ def test_long_prefill_workload_sampled(attn):
         o = o.float().cpu().numpy().reshape(-1, w.d)[rows]
         lse = lse.cpu().numpy().reshape(-1)[rows]
         res = check_exact(o, o_ref, lse, lse_ref, bf16_out=out_dtype == torch.bfloat16,
-                          what="%s %s" % (w.name, out_dtype))
+                          what="%s %s" % (w.name, out_dtype),
+                          literal=out_dtype == torch.float32)
+        if out_dtype == torch.bfloat16:
+            # the LSE gate holds literally for the bf16 store too
+            check_exact(o_ref, o_ref, lse, lse_ref, bf16_out=False, literal=True,
+                        what="%s lse" % w.name)
         print(w.name, out_dtype, len(rows), "rows", res)
         del o, lse
     torch.cuda.empty_cache()

@@ -110,27 +110,101 @@ def test_bf16_output_and_no_lse_bias(attn):
     assert np.abs(lse - lse_ex).max() < 0.05
 
 
-def test_sage_prefill_workload_sampled(attn):
+@pytest.fixture(scope="module")
+def sage_sample(attn):
+    """The quantised-prefill workload (B2 H24 N16384 d128) run with both
+    stores, and the emulator's and the exact oracle's rows on a declared
+    sample: two whole (b, h) slices, the tile-edge and last rows of every
+    slice and 4096 seeded random rows (37 003 rows)."""
     w = workloads.WORKLOADS["sage_prefill"]
     inp = workloads.make(w)
     q, k, v = inp["q"], inp["k"], inp["v"]
-    o, lse = attn.fwd(q.cuda(), k.cuda(), v.cuda(), causal=w.causal, mode="sage",
-                      out_dtype=torch.bfloat16)
-    torch.cuda.synchronize()
-    # two whole (b, h) slices, the tile-edge and last rows of every slice and
-    # 4096 seeded random rows
     rows = workloads.sample_rows(w.B, w.H, w.N, n_random=4096,
                                  whole_slices=((0, 0), (w.B - 1, w.H - 1)))
-    o = o.float().cpu().numpy().reshape(-1, w.d)[rows]
-    lse = lse.cpu().numpy().reshape(-1)[rows]
+    out = {"w": w, "rows": rows}
+    for name, dt in (("bf16", torch.bfloat16), ("fp32", torch.float32)):
+        o, lse = attn.fwd(q.cuda(), k.cuda(), v.cuda(), causal=w.causal, mode="sage",
+                          out_dtype=dt)
+        torch.cuda.synchronize()
+        out[name] = (o.float().cpu().numpy().reshape(-1, w.d)[rows],
+                     lse.cpu().numpy().reshape(-1)[rows])
+        del o, lse
+    torch.cuda.empty_cache()
     qb, kb, vb = _bits(q, k, v)
-    o_emu, lse_emu = oracle.sage_rows(qb, kb, vb, causal=w.causal, scale=w.scale, rows=rows)
-    cos_e, rel_e = cos_rel_l1(o, o_emu)
-    assert cos_e >= EMU_COS and rel_e <= 5e-3, (cos_e, rel_e)
-    assert np.abs(lse - lse_emu).max() <= EMU_LSE
+    out["emu"] = oracle.sage_rows(qb, kb, vb, causal=w.causal, scale=w.scale, rows=rows)
     o_ex, lse_ex, _ = oracle.attn_rows(qb, kb, vb, causal=w.causal, scale=w.scale, rows=rows)
-    cos, rel = cos_rel_l1(o, o_ex)
-    print("sage_prefill %d rows: vs emulator cos %.6f rel-L1 %.2e; vs exact cos %.6f rel-L1 %.4f;"
-          " max |dlse| vs exact %.3g" % (len(rows), cos_e, rel_e, cos, rel,
-                                         np.abs(lse - lse_ex).max()))
-    assert cos >= 0.999, (cos, rel)
+    out["exact"] = (o_ex, lse_ex)
+    return out
+
+
+# Largest per-row rel-L1 against the emulator.  The kernel and the emulator
+# differ only where fp32 arithmetic and the exponent's error of up to half a
+# unit of the integer score (c/2 in log2 units, c the score scale times
+# log2 e) flip an E4M3 rounding of P.  A flip moves one key's weight by one
+# E4M3 step (1/16 to 1/8 of it); on this workload's near-uniform rows |O| is
+# only ~1e-2 of |V|, so one flip of a top-weight key already moves a row by a
+# per-cent.  Measured with the emulator's own arithmetic on the sample's worst
+# row (b 1, h 23, i 6933): perturbing every exponent uniformly within +-c/2
+# moves the row by up to 1.6e-2 (median 2.4e-3), while dropping one 64-key
+# tile of the row moves it by 7.9e-2 to 8.4e-2.  The gate, 2^-5, sits at twice
+# the first and under half the second.
+EMU_ROW_REL = 2.0 ** -5
+
+
+def _row_rel_l1(o, ref):
+    return np.abs(o - ref).sum(axis=1) / np.abs(ref).sum(axis=1)
+
+
+def test_sage_workload_fp32_store_vs_emulator(sage_sample):
+    """fp32 store: the emulator gate of the small cases (cos >= 0.99999,
+    rel-L1 <= 2e-3, |dlse| <= 1e-3) at workload size, plus a per-row bound."""
+    o, lse = sage_sample["fp32"]
+    o_emu, lse_emu = sage_sample["emu"]
+    cos, rel, dl = _check_vs_emulator(o, lse, o_emu, lse_emu, "sage_prefill fp32 store")
+    row = _row_rel_l1(o, o_emu)
+    print("sage_prefill fp32 store vs emulator, %d rows: cos %.7f rel-L1 %.2e max |dlse| %.2e "
+          "per-row rel-L1 max %.2e (row %d) median %.2e" % (
+              len(o), cos, rel, dl, row.max(), sage_sample["rows"][row.argmax()],
+              np.median(row)))
+    assert row.max() <= EMU_ROW_REL, (row.max(), sage_sample["rows"][row.argmax()])
+
+
+def test_sage_workload_bf16_store_vs_emulator(sage_sample):
+    """bf16 store: the same, with the bf16 rounding of O on top (half an ulp
+    is 2^-9 relative, about 1e-3 of rel-L1 on average)."""
+    o, lse = sage_sample["bf16"]
+    o_emu, lse_emu = sage_sample["emu"]
+    cos, rel = cos_rel_l1(o, o_emu)
+    row = _row_rel_l1(o, o_emu)
+    print("sage_prefill bf16 store vs emulator: cos %.7f rel-L1 %.2e per-row max %.2e" % (
+        cos, rel, row.max()))
+    assert cos >= EMU_COS and rel <= 5e-3, (cos, rel)
+    assert np.abs(lse - lse_emu).max() <= EMU_LSE
+    assert row.max() <= EMU_ROW_REL + 2.0 ** -8, row.max()
+
+
+def test_sage_workload_vs_exact_cos(sage_sample):
+    """Against exact attention on the unquantised inputs: cos >= 0.999 in both
+    stores (the stated gate of the quantised mode)."""
+    o_ex, lse_ex = sage_sample["exact"]
+    for name in ("bf16", "fp32"):
+        o, lse = sage_sample[name]
+        cos, rel = cos_rel_l1(o, o_ex)
+        print("sage_prefill %s store vs exact: cos %.6f rel-L1 %.4f max |dlse| %.3g" % (
+            name, cos, rel, np.abs(lse - lse_ex).max()))
+        assert cos >= 0.999, (name, cos, rel)
+
+
+@pytest.mark.xfail(strict=True, reason=(
+    "the recipe's own error: rel-L1 0.039 against exact attention (0.0393 measured on this "
+    "sample), over the 0.03 bound.  The oracle's emulator attributes it on this workload to "
+    "E4M3 P (0.026 alone), E4M3 V (0.026 alone) and INT8 Q/K after Smooth-K (0.013 alone); "
+    "normalising O by the sum of the quantised P leaves it at 0.039 "
+    "(tests/golden/sage_error_budget.json)"))
+def test_sage_workload_vs_exact_rel_l1(sage_sample):
+    """The stated rel-L1 <= 0.03 bound against exact attention (fp32 store, so
+    no output rounding is added)."""
+    o, _ = sage_sample["fp32"]
+    o_ex, _ = sage_sample["exact"]
+    _, rel = cos_rel_l1(o, o_ex)
+    assert rel <= 0.03, rel
