@@ -369,7 +369,7 @@ def bench_decode(args, stream):
     del inp
     o = torch.empty((w.B, w.H, w.d), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((w.B, w.H), dtype=torch.float32, device="cuda")
-    ws = torch.empty((A.attn_decode_workspace_size(w.B, w.H, w.N, w.d, w.split_tokens),),
+    ws = torch.empty((A.attn_decode_workspace_size(w.B, w.H, w.Hkv, w.d),),
                      dtype=torch.uint8, device="cuda")
 
     def step():

@@ -171,11 +171,18 @@ attn_status attn_fwd_varlen(const void *q, const void *k, const void *v, void *o
 /*
  * One-token decode against per-sequence KV caches with split-KV
  * (Flash-Decoding, "flashattention-kernels" page §3): the valid keys
- * [0, seqlens[b]) of each sequence are cut into chunks of split_tokens keys,
- * each chunk's partial attention (O_s, lse_s) is computed in parallel, and the
- * partials are merged by log-sum-exp weights:
+ * [0, seqlens[b]) of each sequence are split into pieces whose partial
+ * attention (O_s, lse_s) is computed in parallel, and the partials are merged
+ * by log-sum-exp weights:
  *     M = max_s lse_s,  w_s = exp(lse_s - M),
  *     O = sum_s w_s O_s / sum_s w_s,  lse = M + ln sum_s w_s.
+ * The valid keys of all (sequence, kv head) pairs, in that order, are divided
+ * into equal contiguous ranges among a fixed set of resident waves, so the
+ * work is balanced whatever the length mix.  Inside a range, the keys of each
+ * (sequence, kv head) form chunks of split_tokens keys (chunk c holds keys
+ * [c*split_tokens, (c+1)*split_tokens)); each chunk's partial is folded into
+ * the wave's running partial by the same merge, and a second kernel merges
+ * the partials of the waves that share a (sequence, kv head).
  * The single query of sequence b sits at position seqlens[b] - 1 and sees every
  * valid key, so there is no causal argument.
  *   q          device bf16 [B, H, d].
@@ -188,7 +195,10 @@ attn_status attn_fwd_varlen(const void *q, const void *k, const void *v, void *o
  *   mode       only ATTN_MODE_EXACT_BF16 (others return ATTN_ERR_UNSUPPORTED).
  *   split_tokens   chunk length; a positive multiple of 64.
  *   workspace  at least attn_decode_workspace_size() bytes: fp32 partial
- *              outputs and LSEs of every (b, h, chunk).
+ *              outputs and LSEs of every (wave, sequence, kv head) piece.
+ *              Its content on entry is irrelevant.
+ * The result does not depend on the order in which waves run: every partial
+ * has one writer and the merge order is fixed, so calls are deterministic.
  */
 attn_status attn_decode(const void *q, const void *k_cache, const void *v_cache,
                         const int32_t *seqlens, void *o, float *lse, int B, int H, int Hkv,
@@ -196,8 +206,9 @@ attn_status attn_decode(const void *q, const void *k_cache, const void *v_cache,
                         int split_tokens, void *workspace, size_t workspace_bytes,
                         void *stream);
 
-/* Bytes of workspace attn_decode needs (0 for invalid sizes). */
-size_t attn_decode_workspace_size(int B, int H, int N_max, int d, int split_tokens);
+/* Bytes of workspace attn_decode and attn_decode_paged need (0 for invalid
+ * sizes): independent of the cache length and the chunk length. */
+size_t attn_decode_workspace_size(int B, int H, int Hkv, int d);
 
 /*
  * attn_decode over paged KV caches: the cache is a pool of fixed-size pages
@@ -205,27 +216,24 @@ size_t attn_decode_workspace_size(int B, int H, int N_max, int d, int split_toke
  * page_size key positions (the non-contiguous KV layout of paged serving
  * caches: "flashattention-kernels" page §3, a library interface covering
  * paged KV; "GPU kernel overview" page, the open gaps on decode with paged,
- * non-contiguous KV memory).  The computation, the chunking into
- * split_tokens keys and the merge are those of attn_decode: for the same keys
- * and values it returns bit-identical results.
+ * non-contiguous KV memory).  The computation, the work split, the chunking
+ * into split_tokens keys and the merge are those of attn_decode: for the same
+ * keys and values it returns bit-identical results.
  *   k_pages, v_pages   device bf16 [num_pages, Hkv, page_size, d].
  *   block_table  device int32 [B, max_pages]: key position n of sequence b
  *              (0 <= n < seqlens[b]) is row n % page_size of page
  *              block_table[b * max_pages + n / page_size].  Entries beyond a
- *              sequence's last page are never read.  Entries must lie in
+ *              sequence's last page are never used.  Entries must lie in
  *              [0, num_pages); the kernels clamp others into that range
  *              (the result is then unspecified, but no access leaves the pool).
  *   seqlens    device int32 [B]; values are clamped to [1, max_pages * page_size].
- *   page_size  a power of two, >= 16, such that a chunk touches at most 64
- *              pages: ceil((split_tokens + page_size - g) / page_size) <= 64
- *              with g = gcd(split_tokens, page_size).
+ *   page_size  a power of two, >= 16.
  *   other arguments as for attn_decode (N_max = max_pages * page_size).
- *   workspace  at least attn_decode_workspace_size(B, H, max_pages * page_size,
- *              d, split_tokens) bytes.
+ *   workspace  at least attn_decode_workspace_size(B, H, Hkv, d) bytes.
  * Errors: those of attn_decode; ATTN_ERR_INVALID_ARG for a null block_table,
  * non-positive num_pages or max_pages, or a page_size that is not a power of
- * two; ATTN_ERR_UNSUPPORTED for a page_size below the limits above or
- * max_pages * page_size beyond 2^31 - 1.
+ * two; ATTN_ERR_UNSUPPORTED for a page_size below 16 or max_pages * page_size
+ * beyond 2^31 - 1.
  */
 attn_status attn_decode_paged(const void *q, const void *k_pages, const void *v_pages,
                               const int32_t *block_table, const int32_t *seqlens, void *o,

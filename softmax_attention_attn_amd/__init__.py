@@ -67,7 +67,7 @@ def _load():
     lib.attn_decode.restype = i
     lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, sz, vp]
     lib.attn_decode_workspace_size.restype = sz
-    lib.attn_decode_workspace_size.argtypes = [i, i, i, i, i]
+    lib.attn_decode_workspace_size.argtypes = [i, i, i, i]
     lib.attn_decode_paged.restype = i
     lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i,
                                       i, vp, sz, vp]
@@ -123,8 +123,8 @@ def attn_fwd_workspace_size(B, H, Hkv, N, d, mode) -> int:
     return int(_lib.attn_fwd_workspace_size(B, H, Hkv, N, d, mode))
 
 
-def attn_decode_workspace_size(B, H, N_max, d, split_tokens) -> int:
-    return int(_lib.attn_decode_workspace_size(B, H, N_max, d, split_tokens))
+def attn_decode_workspace_size(B, H, Hkv, d) -> int:
+    return int(_lib.attn_decode_workspace_size(B, H, Hkv, d))
 
 
 def attn_fwd(q, k, v, o, lse, B, H, Hkv, N, d, causal, scale, mode, o_dtype, workspace,
@@ -418,8 +418,7 @@ def decode(q, k_cache, v_cache, seqlens, *, scale: float | None = None,
         if t.device != dev:
             raise ValueError("%s is on %s, q on %s" % (name, t.device, dev))
     o, lse = _decode_outputs(o, lse, with_lse, out_dtype, B, H, d, dev)
-    workspace, ws_len = _workspace(
-        workspace, attn_decode_workspace_size(B, H, N_max, d, split_tokens), dev)
+    workspace, ws_len = _workspace(workspace, attn_decode_workspace_size(B, H, Hkv, d), dev)
     st = _lib.attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(o),
                           _ptr(lse), B, H, Hkv, N_max, d, float(scale), ATTN_MODE_EXACT_BF16,
                           o_code, int(split_tokens), _ptr(workspace), ws_len,
@@ -456,8 +455,7 @@ def decode_paged(q, k_pages, v_pages, block_table, seqlens, *, scale: float | No
         if t.device != dev:
             raise ValueError("%s is on %s, q on %s" % (name, t.device, dev))
     o, lse = _decode_outputs(o, lse, with_lse, out_dtype, B, H, d, dev)
-    workspace, ws_len = _workspace(
-        workspace, attn_decode_workspace_size(B, H, max_pages * page_size, d, split_tokens), dev)
+    workspace, ws_len = _workspace(workspace, attn_decode_workspace_size(B, H, Hkv, d), dev)
     st = _lib.attn_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
                                 _ptr(seqlens), _ptr(o), _ptr(lse), B, H, Hkv, num_pages,
                                 page_size, max_pages, d, float(scale), ATTN_MODE_EXACT_BF16,

@@ -142,11 +142,12 @@ attn_status decode_common(const void *q, const void *k_cache, const void *v_cach
     if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
         return fail(ATTN_ERR_UNSUPPORTED,
                     "query heads per kv head %d (supported: 1, 2, 4, 8, 16)", G);
-    const long long splits = ((long long)N_max + split_tokens - 1) / split_tokens;
-    // one wave per possible chunk and one merge wave per (b, h), as int indices
-    if ((long long)B * Hkv * splits > 0x7fffff00LL || (long long)B * H > 0x7fffff00LL)
-        return fail(ATTN_ERR_UNSUPPORTED, "problem too large for the grid mapping");
-    const size_t need = attn_decode_workspace_size(B, H, N_max, d, split_tokens);
+    // global key offsets (Hkv * sum of lengths) and slot indices stay far
+    // inside 64-bit and 32-bit arithmetic
+    if ((long long)B * Hkv * (long long)N_max > (1LL << 40) || (long long)B * H > 0x7fffff00LL ||
+        (long long)B * Hkv > 0x7fff0000LL)
+        return fail(ATTN_ERR_UNSUPPORTED, "problem too large for the work split");
+    const size_t need = attn_decode_workspace_size(B, H, Hkv, d);
     if (!workspace || workspace_bytes < need)
         return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                     workspace ? workspace_bytes : (size_t)0);
@@ -166,10 +167,10 @@ attn_status decode_common(const void *q, const void *k_cache, const void *v_cach
     a.scale = scale;
     a.out_fp32 = o_dtype == ATTN_OUT_FP32;
     a.split_tokens = split_tokens;
-    a.max_splits = (int)splits;
+    const size_t slots = attn::decode_partial_slots(B, Hkv);
     a.part_o = (float *)workspace;
     a.part_lse = (float *)((char *)workspace +
-                           align_up(sizeof(float) * (size_t)B * H * splits * d, 256));
+                           align_up(sizeof(float) * slots * (H / Hkv) * d, 256));
     return ATTN_OK;
 }
 
@@ -344,14 +345,13 @@ attn_status attn_bwd(const void *q, const void *k, const void *v, const void *o,
     return from_hip(attn::launch_bwd(a, (hipStream_t)stream), "backward launch");
 }
 
-size_t attn_decode_workspace_size(int B, int H, int N_max, int d, int split_tokens)
+size_t attn_decode_workspace_size(int B, int H, int Hkv, int d)
 {
-    if (B <= 0 || H <= 0 || N_max <= 0 || d <= 0 || split_tokens <= 0)
+    if (B <= 0 || H <= 0 || Hkv <= 0 || d <= 0 || H % Hkv != 0)
         return 0;
-    const size_t splits = ((size_t)N_max + split_tokens - 1) / split_tokens;
-    const size_t o_bytes = align_up(sizeof(float) * (size_t)B * H * splits * d, 256);
-    const size_t l_bytes = align_up(sizeof(float) * (size_t)B * H * splits, 256);
-    return o_bytes + l_bytes;
+    const size_t slots = attn::decode_partial_slots(B, Hkv);
+    const size_t G = (size_t)(H / Hkv);
+    return align_up(sizeof(float) * slots * G * d, 256) + align_up(sizeof(float) * slots * G, 256);
 }
 
 attn_status attn_decode(const void *q, const void *k_cache, const void *v_cache,
@@ -384,22 +384,6 @@ attn_status attn_decode_paged(const void *q, const void *k_pages, const void *v_
         return fail(ATTN_ERR_INVALID_ARG, "page_size=%d is not a power of two", page_size);
     if (page_size < 16)
         return fail(ATTN_ERR_UNSUPPORTED, "page_size=%d (supported: >= 16)", page_size);
-    if (split_tokens > 0) {
-        // pages touched by a chunk [c*S, c*S + S) in the worst case over c:
-        // ceil((S + P - gcd(S, P)) / P); a chunk's page numbers are held one
-        // per lane, so at most 64
-        long long g = split_tokens, r = page_size;
-        while (r) {
-            const long long t = g % r;
-            g = r;
-            r = t;
-        }
-        const long long span = (split_tokens + page_size - g + page_size - 1) / page_size;
-        if (span > 64)
-            return fail(ATTN_ERR_UNSUPPORTED,
-                        "page_size=%d with split_tokens=%d: a chunk can touch %lld pages "
-                        "(supported: 64)", page_size, split_tokens, span);
-    }
     const long long n_max = (long long)max_pages * page_size;
     if (n_max > 0x7fffffffLL)
         return fail(ATTN_ERR_UNSUPPORTED, "max_pages * page_size = %lld exceeds 2^31 - 1", n_max);

@@ -32,9 +32,10 @@ struct DecodeArgs {
     float scale;
     int out_fp32;
     int split_tokens;
-    int max_splits;   // ceil(N_max / split_tokens)
-    float *part_o;    // [B, H, max_splits, d]
-    float *part_lse;  // [B, H, max_splits]
+    // partials of the split kernel, one slot per (wave, segment) piece:
+    // slot = b * Hkv + kvh + wave, decode_partial_slots(B, Hkv) slots
+    float *part_o;    // [slots, H / Hkv, d]
+    float *part_lse;  // [slots, H / Hkv], log2 units
     // Paged caches (block_table non-null): k and v are [num_pages, Hkv,
     // page_size, d] with page_size = 1 << page_shift, and key position n of
     // sequence b lives in page block_table[b * max_pages + (n >> page_shift)].
@@ -65,6 +66,10 @@ struct SageArgs {
 // arguments and return the launch status.
 hipError_t launch_prefill_exact(const PrefillArgs &a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);  // contiguous or paged caches
+// The split-KV decode divides the keys of a call among at most this many
+// waves (four per CU of a 256-CU MI355X, all resident at once).
+constexpr int kDecodeWaves = 1024;
+size_t decode_partial_slots(int B, int Hkv);
 hipError_t launch_sage(const SageArgs &a, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t s);
 size_t sage_workspace_bytes(int B, int H, int Hkv, int N, int d);

@@ -1,31 +1,50 @@
 // Split-KV GQA decode for gfx950 (Flash-Decoding, "flashattention-kernels"
 // page §3; GQA from the "cuda-kernel-pretrain" page §3).
 //
-// decode_split_kernel: each wave owns one chunk of split_tokens keys of one
-// (sequence, kv head) and computes the chunk's partial attention for all
-// G = H/Hkv query heads of the group at once: each K/V cache byte is read
-// once per group, not once per query head (the GQA saving).  It writes the
-// partial output O_s (normalised by the chunk's own row sum) and its log2
-// LSE.  Chunks starting at or beyond the sequence length do no work.
+// The valid keys of all (sequence, kv head) segments, taken in (sequence,
+// kv head, position) order, form one list of K = Hkv * sum_b L_b keys.  A
+// fixed set of resident waves (kDecodeWaves, fewer on small problems) splits
+// that list into equal contiguous ranges, so every wave -- and every XCD --
+// streams the same number of bytes whatever the length mix, and each wave
+// reads long contiguous runs of the caches.
+//
+// decode_split_kernel: a wave walks its range sub-tile by sub-tile (32
+// keys, aligned to multiples of 32 within the sequence).  Within one
+// (sequence, kv head) segment the keys form split_tokens-key chunks (chunk c
+// is [c * split_tokens, (c + 1) * split_tokens)); the wave computes each
+// chunk's partial attention for all G = H/Hkv query heads of the group at
+// once (each K/V byte is read once per group, the GQA saving) and folds it
+// into its running partial for the segment with log-sum-exp weights.  Where
+// its range leaves a segment it writes that partial (O normalised by its own
+// row sum, and its log2 LSE) to the slot (segment index + wave index).  A
+// chunk cut by a range boundary contributes a partial to each of the two
+// waves.
+//
+// decode_merge_kernel: one wave per (sequence, query head) merges the
+// partials of the waves whose ranges met its segment -- consecutive slots --
+// with log-sum-exp weights into O and the natural-log LSE.
 //
 // The caches are either contiguous per sequence ([B, Hkv, N_max, d]) or a
 // pool of fixed-size pages named by a per-sequence page table (the paged KV
-// layout of serving caches, "flashattention-kernels" page §3).  A paged
-// wave reads its chunk's page numbers once, one per lane, and looks up the
-// page of each row it loads with a lane shuffle; everything else is shared.
+// layout of serving caches, "flashattention-kernels" page §3).  A paged wave
+// reads the page numbers of each sub-tile two load groups ahead of its K/V
+// loads (a sub-tile touches at most two pages, as pages hold >= 16 rows) and
+// finds each row's page with a lane shuffle; everything else is shared.
 //
-// decode_merge_kernel: one wave per (sequence, query head) combines the
-// chunk partials with log-sum-exp weights into O and the natural-log LSE.
-//
-// The path is HBM bound (a few FLOPs per byte): the split kernel keeps two
-// sub-tiles of K and V in flight per wave (about 32 KB), uses the matrix
-// cores for the small products so the VALU stays free, and never stalls on
-// other waves.
+// The path is HBM bound (a few FLOPs per byte): each wave keeps two sub-tiles
+// of K and V in flight (about 32 KB), uses the matrix cores for the small
+// products so the VALU stays free, and never waits on other waves.
 #include "attn_internal.hpp"
 #include "cdna4.hpp"
 
 namespace attn {
 namespace {
+
+constexpr int kSub = 32;  // keys per sub-tile
+constexpr int kVStages = 3;
+constexpr int kWavesPerWG = 4;
+constexpr int kMinKeysPerWave = 256;  // a small problem uses fewer waves
+static_assert(kDecodeWaves % kWavesPerWG == 0, "whole workgroups");
 
 __device__ __forceinline__ int clamp_len(const int32_t *seqlens, int b, int n_max)
 {
@@ -33,63 +52,23 @@ __device__ __forceinline__ int clamp_len(const int32_t *seqlens, int b, int n_ma
     return L < 1 ? 1 : (L > n_max ? n_max : L);
 }
 
-// Work items are the non-empty chunks, ordered by sequence, then kv head,
-// then chunk, and item i goes to wave i of the grid.  Consecutive workgroups
-// land on consecutive XCDs, so every XCD gets an equal share of the chunks
-// whatever the length mix (a grid over (chunk, kv head, sequence) would give
-// the XCDs that own high chunk indices nothing to do on short sequences).
-// The wave maps its item to (b, kvh, split) with a wave-wide prefix sum of
-// the per-sequence item counts, 64 sequences at a time.
-__device__ __forceinline__ bool locate_item(const DecodeArgs &a, int item, int lane, int &b,
-                                            int &kvh, int &split, int &L)
+// s_waitcnt for the vector-memory counter only (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt and lgkmcnt left at their maxima), through the
+// builtin so that the compiler's own wait insertion sees it
+template <int N>
+__device__ __forceinline__ void vm_wait()
 {
-    const int S = a.split_tokens;
-    int base = 0;  // items of the sequences before b0
-    for (int b0 = 0; b0 < a.B; b0 += 64) {
-        const int bb = b0 + lane;
-        const int nch = bb < a.B ? (clamp_len(a.seqlens, bb, a.N_max) + S - 1) / S : 0;
-        const int cnt = a.Hkv * nch;
-        int inc = cnt;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int t = __shfl_up(inc, off, 64);
-            if (lane >= off)
-                inc += t;
-        }
-        const int total = __shfl(inc, 63, 64);
-        if (item < base + total) {
-            const unsigned long long m = __ballot(base + inc > item);
-            const int l = __builtin_ctzll(m);  // first sequence whose items reach past item
-            const int excl = __shfl(inc - cnt, l, 64);
-            const int nch_l = __shfl(nch, l, 64);
-            b = b0 + l;
-            L = clamp_len(a.seqlens, b, a.N_max);
-            const int r = item - base - excl;
-            kvh = r / nch_l;
-            split = r - kvh * nch_l;
-            return true;
-        }
-        base += total;
-    }
-    return false;
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
-
-// One 512-token (split_tokens) chunk per wave.  The wave streams its chunk
-// in sub-tiles of kSub keys: K straight into the registers of the MFMA A
-// operand, V into a 3-stage LDS ring of this wave through direct loads; both
-// run two sub-tiles ahead.  S^T = K q^T and O^T += V^T P^T run on
-// v_mfma_f32_16x16x32_bf16 with the G query heads of the group as the MFMA
-// columns (columns >= G are zero), so the chunk's keys are read once for all
-// G heads.  Waves never synchronise with each other.
-constexpr int kSub = 32;       // keys per sub-tile
-constexpr int kVStages = 3;
-constexpr int kWavesPerWG = 4;
 
 template <int D>
 struct DCfg {
-    static constexpr int kVBytes = kSub * D * 2;   // one V sub-tile
-    static constexpr int kChunks = D / 8;          // 16-byte chunks per row
+    static constexpr int kVBytes = kSub * D * 2;  // one V sub-tile
+    static constexpr int kChunks = D / 8;         // 16-byte chunks per row
     static constexpr int kVPieces = kVBytes / 1024;
+    static constexpr int kQLoads = D / 32;                  // q fragments per lane
+    static constexpr int kKVLoads = 2 * (D / 32) + kVPieces;  // K rows + V pieces per lane
 };
 
 // V sub-tile: 16-byte chunk c of row r is stored at chunk c ^ (2 * (r & 7))
@@ -101,158 +80,271 @@ __device__ __forceinline__ int dvswz(int r)
     return (2 * (r & 7)) & (DCfg<D>::kChunks - 1);
 }
 
+__device__ __forceinline__ long long uniform64(long long x)
+{
+    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)x);
+    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)((unsigned long long)x >> 32));
+    return (long long)(((unsigned long long)hi << 32) | lo);
+}
+
+// The key list and its split among the waves.  Every wave of both kernels
+// computes the same K and the same number of working waves W.
+struct KeySplit {
+    long long K;  // total valid keys, Hkv * sum_b L_b
+    int W;        // waves with work: min(kDecodeWaves, max(1, K / kMinKeysPerWave))
+    __device__ long long start(int w) const { return (long long)w * K / W; }
+    // the wave whose range holds global key x: the largest w with start(w) <= x
+    __device__ int wave_of(long long x) const
+    {
+        return (int)(((x + 1) * W - 1) / K);
+    }
+};
+
+__device__ __forceinline__ KeySplit key_split(const DecodeArgs &a, int lane)
+{
+    long long s = 0;
+    for (int b0 = 0; b0 < a.B; b0 += 64) {
+        const int bb = b0 + lane;
+        s += bb < a.B ? clamp_len(a.seqlens, bb, a.N_max) : 0;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        s += __shfl_xor(s, off, 64);
+    KeySplit ks;
+    ks.K = uniform64(s * a.Hkv);
+    const long long w = ks.K / kMinKeysPerWave;
+    ks.W = (int)(w < 1 ? 1 : (w > kDecodeWaves ? kDecodeWaves : w));
+    return ks;
+}
+
+// The segment holding global key x: its sequence b, the global offset of its
+// sequence's first key (Hkv * sum_{b' < b} L_b'), and L_b.  A wave-wide
+// prefix sum over the sequences, 64 at a time.
+__device__ __forceinline__ void locate_key(const DecodeArgs &a, long long x, int lane, int &b,
+                                           long long &seq0, int &L)
+{
+    long long base = 0;
+    b = a.B - 1;
+    seq0 = 0;
+    L = 1;
+    for (int b0 = 0; b0 < a.B; b0 += 64) {
+        const int bb = b0 + lane;
+        const int len = bb < a.B ? clamp_len(a.seqlens, bb, a.N_max) : 0;
+        long long inc = (long long)len * a.Hkv;
+        const long long cnt = inc;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const long long t = __shfl_up(inc, off, 64);
+            if (lane >= off)
+                inc += t;
+        }
+        const long long total = __shfl(inc, 63, 64);
+        if (x < base + total) {
+            const unsigned long long m = __ballot(base + inc > x);
+            const int l = __builtin_ctzll(m);
+            b = b0 + l;
+            seq0 = base + __shfl(inc - cnt, l, 64);
+            L = __shfl(len, l, 64);
+            return;
+        }
+        base += total;
+    }
+}
+
+// Walks the sub-tiles of a wave's key range in order.  All fields are
+// wave-uniform (scalar registers).
+struct Cursor {
+    int b, kvh, L;
+    long long seg0;  // global offset of the current segment's key 0
+    int pos;         // first key of the next sub-tile, within the segment
+    long long end;   // global end of the wave's range
+    bool first;      // the next sub-tile starts a new piece
+    bool done;
+};
+
+// One sub-tile: keys [lo, hi) of segment (b, kvh), inside the 32-aligned
+// block that starts at base.
+struct SubTile {
+    int b, kvh;
+    int base, lo, hi;
+    bool valid, first, last, chunk_end;
+};
+
+// Running (unnormalised) attention state of one chunk or one piece: the
+// reference max m of score * scale * log2(e) (per head column), this lane's
+// parts of the row sums over the unrounded p (l, for the LSE) and over the
+// bf16-rounded p that enter the PV MFMA (lp, for normalising O), and O^T.
+template <int D>
+struct State {
+    float m, l, lp;
+    f32x4 o[D / 16];
+    __device__ void reset()
+    {
+        m = -INFINITY;
+        l = lp = 0.f;
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c)
+            o[c] = f32x4{};
+    }
+};
+
+// acc <- the log-sum-exp merge of acc and part (both relative to their own
+// reference max); the empty acc (m = -inf) takes part as it is.
+template <int D>
+__device__ __forceinline__ void fold(State<D> &acc, const State<D> &part)
+{
+    const float mn = fmaxf(acc.m, part.m);
+    const float a1 = fast_exp2(acc.m - mn), a2 = fast_exp2(part.m - mn);
+    acc.l = acc.l * a1 + part.l * a2;
+    acc.lp = acc.lp * a1 + part.lp * a2;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+        acc.o[c] = acc.o[c] * a1 + part.o[c] * a2;
+    acc.m = mn;
+}
+
 template <int D, int G, bool PAGED>
 __global__ __launch_bounds__(64 * kWavesPerWG) void decode_split_kernel(DecodeArgs a)
 {
     __shared__ __attribute__((aligned(1024)))
     unsigned char vlds[kWavesPerWG][kVStages][DCfg<D>::kVBytes];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int S = a.split_tokens;
-    int b, kvh, split, L;
-    if (!locate_item(a, (int)blockIdx.x * kWavesPerWG + wave, lane, b, kvh, split, L))
-        return;  // past the last chunk (no barrier follows)
-    const int c0 = split * S;
-    const int n = min(S, L - c0);
-    const int nsub = (n + kSub - 1) / kSub;
+    constexpr int KVL = DCfg<D>::kKVLoads, QL = DCfg<D>::kQLoads;
+    constexpr int kGroup = KVL + QL + (PAGED ? 1 : 0);  // loads per group
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const KeySplit ks = key_split(a, lane);
+    const int w = (int)blockIdx.x * kWavesPerWG + wave;
+    if (w >= ks.W)
+        return;  // no barrier follows
+    const long long g0 = ks.start(w), g1 = ks.start(w + 1);
+
     const int col = lane & 15, G4 = lane >> 4;  // MFMA column (head) and lane group
     unsigned char *vst = &vlds[wave][0][0];
-    // Element offset of key row r (0 <= r < n) of the chunk in the K and V
-    // caches.  Paged: lane l holds the page of the chunk's l-th page slot
-    // (a chunk spans at most 64 pages; out-of-range page numbers are clamped
-    // into the pool), and a row's page is read from its lane.
-    size_t cache_off = 0;
-    int first_page = 0, my_page = 0;
-    if constexpr (PAGED) {
-        first_page = c0 >> a.page_shift;
-        const int npc = ((c0 + n - 1) >> a.page_shift) - first_page + 1;
-        if (lane < npc) {
-            const int pg = a.block_table[(size_t)b * a.max_pages + first_page + lane];
-            my_page = pg < 0 ? 0 : (pg >= a.num_pages ? a.num_pages - 1 : pg);
-        }
-    } else {
-        cache_off = ((size_t)(b * a.Hkv + kvh) * a.N_max + c0) * D;
-    }
-    auto row_off = [&](int r) -> size_t {
+    const uint16_t *kcache = (const uint16_t *)a.k, *vcache = (const uint16_t *)a.v;
+    const int pmask = (1 << a.page_shift) - 1;
+    const float cs = a.scale * kLog2e;
+    // per-lane transposing-read offset: lane 4j + q of its 16-lane group
+    // reads key row (base + j), features 16c + 4q .. +3
+    const int trl = lane & 15, trj = trl >> 2, trq = trl & 3;
+
+    // element offset of key `key` of segment (b, kvh); paged: `tab` holds (in
+    // lanes 0 and 1) the pages of the sub-tile's 32-aligned block at `base`
+    auto row_off = [&](int b, int kvh, int base, int key, int tab) -> size_t {
         if constexpr (PAGED) {
-            const int pos = c0 + r;
-            const int pg = __shfl(my_page, (pos >> a.page_shift) - first_page, 64);
-            const int in_page = pos & ((1 << a.page_shift) - 1);
-            return ((((size_t)pg * a.Hkv + kvh) << a.page_shift) + in_page) * D;
+            const int pg = __shfl(tab, (key >> a.page_shift) - (base >> a.page_shift), 64);
+            return ((((size_t)pg * a.Hkv + kvh) << a.page_shift) + (key & pmask)) * D;
         } else {
-            return cache_off + (size_t)r * D;
+            return ((size_t)(b * a.Hkv + kvh) * a.N_max + key) * D;
         }
     };
-    const uint16_t *kc = (const uint16_t *)a.k, *vc = (const uint16_t *)a.v;
-
-    // q^T fragments (B operand of QK): lane holds q[head col][32*ks + 8*G4 .. +7]
-    bf16x8 qf[D / 32];
+    // page numbers of a sub-tile's block (lanes 0 and 1: its first and second
+    // page; a page holds >= 16 rows, so 32 aligned keys touch at most two),
+    // clamped into the table row and the pool
+    auto load_tab = [&](const SubTile &s) -> int {
+        const int pi = min((s.base >> a.page_shift) + (lane & 1), a.max_pages - 1);
+        const int pg = a.block_table[(size_t)s.b * a.max_pages + pi];
+        return pg < 0 ? 0 : (pg >= a.num_pages ? a.num_pages - 1 : pg);
+    };
+    // q^T fragments (B operand of QK): lane holds q[head col][32*j + 8*G4 .. +7]
+    // (lanes of columns >= G load head 0's row; their q is zeroed when used)
+    auto load_q = [&](const SubTile &s, u32x4 (&qd)[D / 32]) {
+        const uint16_t *qrow =
+            (const uint16_t *)a.q + ((size_t)s.b * a.H + s.kvh * G + (col < G ? col : 0)) * D;
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks)
-        qf[ks] = as_bf16x8(col < G ? ld16((const uint16_t *)a.q +
-                                          ((size_t)b * a.H + kvh * G + col) * D + 32 * ks + 8 * G4)
-                                   : u32x4{0, 0, 0, 0});
-
-    // K sub-tile into registers: MFMA (blk, ks) A operand = row 16*blk + col,
-    // features 32*ks + 8*G4 .. +7.  Rows past the chunk re-read its last row.
-    auto load_k = [&](int i, u32x4 (&kr)[2][D / 32]) {
+        for (int j = 0; j < D / 32; ++j)
+            qd[j] = ld16(qrow + 32 * j + 8 * G4);
+    };
+    // K sub-tile into registers: MFMA (blk, j) A operand = row 16*blk + col,
+    // features 32*j + 8*G4 .. +7; V sub-tile into LDS stage `stage` (row-major
+    // rows of D bf16, swizzled).  Rows outside [lo, hi) re-read a valid row
+    // (their scores are masked).
+    auto load_kv = [&](const SubTile &s, int tab, u32x4 (&kr)[2][D / 32], int stage) {
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
-            const uint16_t *krow = kc + row_off(min(i * kSub + 16 * blk + col, n - 1));
+            const int key = min(max(s.base + 16 * blk + col, s.lo), s.hi - 1);
+            const uint16_t *krow = kcache + row_off(s.b, s.kvh, s.base, key, tab);
 #pragma unroll
-            for (int ks = 0; ks < D / 32; ++ks)
-                kr[blk][ks] = ld16(krow + 32 * ks + 8 * G4);
+            for (int j = 0; j < D / 32; ++j)
+                kr[blk][j] = ld16(krow + 32 * j + 8 * G4);
         }
-    };
-    // V sub-tile into LDS stage i % 3 (row-major rows of D bf16, swizzled)
-    auto load_v = [&](int i) {
-        unsigned char *dst = vst + (i % kVStages) * DCfg<D>::kVBytes;
+        unsigned char *dst = vst + stage * DCfg<D>::kVBytes;
         constexpr int C = DCfg<D>::kChunks;
 #pragma unroll
         for (int piece = 0; piece < DCfg<D>::kVPieces; ++piece) {
             const int p = piece * 64 + lane;
             const int r = p / C;
             const int c = (p % C) ^ dvswz<D>(r);
-            dma16(vc + row_off(min(i * kSub + r, n - 1)) + c * 8, dst + piece * 1024);
+            const int key = min(max(s.base + r, s.lo), s.hi - 1);
+            dma16(vcache + row_off(s.b, s.kvh, s.base, key, tab) + c * 8, dst + piece * 1024);
         }
     };
 
-    u32x4 kr0[2][D / 32], kr1[2][D / 32], kr2[2][D / 32];
-    load_k(0, kr0);
-    load_v(0);
-    if (nsub > 1) {
-        load_k(1, kr1);
-        load_v(1);
-    }
-    const float cs = a.scale * kLog2e;
-    // l: row sum of the unrounded p (for the LSE); lp: of the bf16-rounded p
-    // that enter the PV MFMA (normalises O, so the weights on V sum to one)
-    float m = -INFINITY, l = 0.f, lp = 0.f;
-    f32x4 o[D / 16];
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c)
-        o[c] = f32x4{};
-    // per-lane transposing-read offset: lane 4j + q of its 16-lane group
-    // reads key row (base + j), features 16c + 4q .. +3
-    const int trl = lane & 15, trj = trl >> 2, trq = trl & 3;
+    State<D> ch, pc;  // the current chunk's state and the current piece's
+    ch.reset();
+    pc.reset();
+    bf16x8 qf[D / 32];
 
-    // sub-tile i: K in registers k (loaded two sub-tiles earlier), V in LDS
-    // stage i % 3; the loads of sub-tile i+2 go to kn and stage (i+2) % 3
-    auto step = [&](int i, const u32x4(&k)[2][D / 32], u32x4(&kn)[2][D / 32]) {
-        // sub-tile i has landed when at most the loads of sub-tile i+1 are pending
-        if (i + 1 < nsub)
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (D / 32) + DCfg<D>::kVPieces) : "memory");
-        else
-            vm_wait_all();
-        if (i + 2 < nsub) {
-            load_k(i + 2, kn);
-            load_v(i + 2);
-        }
-        // S^T = K q^T: lane holds head col, keys 16*blk + 4*G4 + r
-        f32x4 s[2] = {f32x4{}, f32x4{}};
+    // sub-tile i: descriptor s, K in kr, q in qd, V in stage i % 3
+    auto compute = [&](const SubTile &s, const u32x4(&kr)[2][D / 32], const u32x4(&qd)[D / 32],
+                       int stage) {
+        // every group loads q, so its registers are read here on every path
+        // (a load whose result is dropped would make the compiler wait for
+        // all loads before reusing its registers)
 #pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks)
+        for (int j = 0; j < D / 32; ++j)
+            asm volatile("" ::"v"(qd[j]));
+        if (s.first) {
+            // the piece's query rows (lanes of columns >= G hold zeros)
+#pragma unroll
+            for (int j = 0; j < D / 32; ++j)
+                qf[j] = as_bf16x8(col < G ? qd[j] : u32x4{0, 0, 0, 0});
+        }
+        // S^T = K q^T: lane holds head col, keys 16*blk + 4*G4 + r of the block
+        f32x4 sc[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+        for (int j = 0; j < D / 32; ++j)
 #pragma unroll
             for (int blk = 0; blk < 2; ++blk)
-                s[blk] = mfma_bf16_16x16x32(as_bf16x8(k[blk][ks]), qf[ks], s[blk]);
+                sc[blk] = mfma_bf16_16x16x32(as_bf16x8(kr[blk][j]), qf[j], sc[blk]);
         float mx = -INFINITY;
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int key = i * kSub + 16 * blk + 4 * G4 + r;
-                s[blk][r] = key < n ? s[blk][r] * cs : -INFINITY;
-                mx = fmaxf(mx, s[blk][r]);
+                const int key = s.base + 16 * blk + 4 * G4 + r;
+                sc[blk][r] = key >= s.lo && key < s.hi ? sc[blk][r] * cs : -INFINITY;
+                mx = fmaxf(mx, sc[blk][r]);
             }
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        // lazy rescale (the reference max moves only by more than 2^8); the
-        // first sub-tile always has a visible key
-        if (__any(mx > m + 8.f)) {
-            const float m_new = mx > m + 8.f ? mx : m;
-            const float alpha = fast_exp2(m - m_new);
-            l *= alpha;
-            lp *= alpha;
+        // lazy rescale (the reference max moves only by more than 2^8); every
+        // sub-tile has a visible key, so a chunk's first sub-tile sets m
+        if (__any(mx > ch.m + 8.f)) {
+            const float m_new = mx > ch.m + 8.f ? mx : ch.m;
+            const float alpha = fast_exp2(ch.m - m_new);
+            ch.l *= alpha;
+            ch.lp *= alpha;
 #pragma unroll
             for (int c = 0; c < D / 16; ++c)
-                o[c] *= alpha;
-            m = m_new;
+                ch.o[c] *= alpha;
+            ch.m = m_new;
         }
         // P^T B operand: element e is key 16*(e/4) + 4*G4 + e%4
         float p[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            p[e] = fast_exp2(s[e >> 2][e & 3] - m);
-            l += p[e];
+            p[e] = fast_exp2(sc[e >> 2][e & 3] - ch.m);
+            ch.l += p[e];
         }
         const u32x4 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
                           pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            lp = add_bf16x2(pw[e], lp);
+            ch.lp = add_bf16x2(pw[e], ch.lp);
         // O^T += V^T P^T: per 16-feature block c, the A operand is keys
         // 4*G4 + 0..3 and 16 + 4*G4 + 0..3 of features 16c + col, gathered by
         // two transposing reads
-        const uint32_t vbase = lds_addr(vst + (i % kVStages) * DCfg<D>::kVBytes);
+        const uint32_t vbase = lds_addr(vst + stage * DCfg<D>::kVBytes);
         auto vaddr = [&](int row, int c) {
             const int chunk = 2 * c + (trq >> 1);
             return vbase + row * (D * 2) + ((chunk ^ dvswz<D>(row)) << 4) + (trq & 1) * 8;
@@ -272,39 +364,172 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void decode_split_kernel(DecodeAr
             } else {
                 lgkm_wait<0>(va[c & 1]);
             }
-            o[c] = mfma_bf16_16x16x32(as_bf16x8(va[c & 1]), as_bf16x8(pw), o[c]);
+            ch.o[c] = mfma_bf16_16x16x32(as_bf16x8(va[c & 1]), as_bf16x8(pw), ch.o[c]);
+        }
+        if (s.chunk_end) {
+            fold(pc, ch);
+            ch.reset();
+        }
+        if (s.last) {
+            // the piece's partial: O_s = acc / lp, lse_s = m + log2 l (log2
+            // units); lane holds head col, features 16c + 4*G4 + r
+            float lt = pc.l + __shfl_xor(pc.l, 16, 64);
+            lt += __shfl_xor(lt, 32, 64);
+            float ltp = pc.lp + __shfl_xor(pc.lp, 16, 64);
+            ltp += __shfl_xor(ltp, 32, 64);
+            if (col < G) {
+                const float inv = 1.f / ltp;
+                const size_t slot = (size_t)(s.b * a.Hkv + s.kvh) + w;
+                float *po = a.part_o + (slot * G + col) * D;
+#pragma unroll
+                for (int c = 0; c < D / 16; ++c)
+                    *(f32x4 *)(po + 16 * c + 4 * G4) = pc.o[c] * inv;
+                if (G4 == 0)
+                    a.part_lse[slot * G + col] = pc.m + log2f(lt);
+            }
+            pc.reset();
         }
     };
-    for (int i = 0; i < nsub; i += 3) {
-        step(i, kr0, kr2);
-        if (i + 1 < nsub)
-            step(i + 1, kr1, kr0);
-        if (i + 2 < nsub)
-            step(i + 2, kr2, kr1);
-    }
 
-    // partial of this chunk: O_s = acc / lp, lse_s = m + log2 l (log2 units);
-    // lane holds head col, features 16c + 4*G4 + r
-    float lt = l + __shfl_xor(l, 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
-    float ltp = lp + __shfl_xor(lp, 16, 64);
-    ltp += __shfl_xor(ltp, 32, 64);
-    if (col < G) {
-        const float inv = 1.f / ltp;
-        const size_t pidx = ((size_t)b * a.H + kvh * G + col) * a.max_splits + split;
-        float *po = a.part_o + pidx * D;
+    // The wave's range in windows of at most 64 sequences, so that a lane can
+    // hold each sequence length of the window and the pipelined loop issues no
+    // load but its load groups (a range crosses more than 64 sequences only
+    // when they are short).  The pipeline drains between windows.
+    int b, L;
+    long long seq0;
+    locate_key(a, g0, lane, b, seq0, L);
+    b = __builtin_amdgcn_readfirstlane(b);
+    seq0 = uniform64(seq0);
+    long long x = g0;  // first key of the next window's part of the range
+    while (x < g1) {
+        // window: sequences b .. b+63 (lane i: length of sequence b + i)
+        const int wb = b;
+        const int len = wb + lane < a.B ? clamp_len(a.seqlens, wb + lane, a.N_max) : 0;
+        long long wend = (long long)len * a.Hkv;
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c)
-            *(f32x4 *)(po + 16 * c + 4 * G4) =
-                f32x4{o[c][0] * inv, o[c][1] * inv, o[c][2] * inv, o[c][3] * inv};
-        if (G4 == 0)
-            a.part_lse[pidx] = m + log2f(lt);
+        for (int off = 32; off > 0; off >>= 1)
+            wend += __shfl_xor(wend, off, 64);
+        wend = uniform64(seq0 + wend);  // global end of the window's last sequence
+        const long long x1 = wend < g1 ? wend : g1;
+
+        Cursor kc;  // the K/V load cursor
+        {
+            L = __builtin_amdgcn_readlane(len, b - wb);
+            const long long off = x - seq0;
+            kc.b = b;
+            kc.L = L;
+            kc.kvh = (int)(off / L);
+            kc.seg0 = seq0 + (long long)kc.kvh * L;
+            kc.pos = (int)(x - kc.seg0);
+            kc.end = x1;
+            kc.first = true;
+            kc.done = false;
+        }
+        Cursor tc = kc;  // the page-table cursor, two sub-tiles ahead of kc
+        auto advance = [&](Cursor &c) -> SubTile {
+            SubTile st;
+            st.valid = !c.done;
+            if (c.done) {
+                // past the range: a stand-in that names key 0 of segment
+                // (0, 0), so that every load group keeps its size (its loads
+                // are never used)
+                st.b = st.kvh = st.base = st.lo = 0;
+                st.hi = 1;
+                st.first = st.last = st.chunk_end = false;
+                return st;
+            }
+            const long long rem = c.end - c.seg0;
+            const int pend = rem < c.L ? (int)rem : c.L;  // the piece ends here
+            st.b = c.b;
+            st.kvh = c.kvh;
+            st.base = c.pos & ~(kSub - 1);
+            st.lo = c.pos;
+            st.hi = min(st.base + kSub, pend);
+            st.first = c.first;
+            st.last = st.hi == pend;
+            st.chunk_end = st.last || st.hi % a.split_tokens == 0;
+            c.first = false;
+            c.pos = st.hi;
+            if (st.last) {
+                c.seg0 += c.L;
+                c.pos = 0;
+                c.first = true;
+                if (c.seg0 >= c.end) {
+                    c.done = true;
+                } else if (++c.kvh == a.Hkv) {
+                    c.kvh = 0;
+                    ++c.b;
+                    c.L = __builtin_amdgcn_readlane(len, c.b - wb);
+                }
+            }
+            return st;
+        };
+
+        // sub-tile descriptors, their K registers, q fragments and page
+        // numbers rotate over three slots (sub-tile i in slot i % 3)
+        SubTile st0, st1, st2;
+        u32x4 kr0[2][D / 32], kr1[2][D / 32], kr2[2][D / 32];
+        u32x4 qb0[D / 32], qb1[D / 32], qb2[D / 32];
+        int tb0 = 0, tb1 = 0, tb2 = 0;
+
+        // group of sub-tile j: [the page numbers of sub-tile j + 2], q of j's
+        // (sequence, kv head), K and V of j; issued two steps before sub-tile
+        // j is computed.  Every group issues the same loads whether or not j
+        // exists or starts a piece (stand-ins past the range), so the number
+        // of loads in flight is the same on every path and the wait for a
+        // group is exact.
+        auto issue_group = [&](const SubTile &s, int tab, u32x4(&kr)[2][D / 32],
+                               u32x4(&qd)[D / 32], int stage, int &tnext) {
+            if constexpr (PAGED)
+                tnext = load_tab(advance(tc));
+            load_q(s, qd);
+            load_kv(s, tab, kr, stage);
+        };
+        // step i: wait for sub-tile i's group (at most sub-tile i+1's group
+        // pending), issue sub-tile i+2's group, compute sub-tile i
+        auto step = [&](const SubTile &s, const u32x4(&kr)[2][D / 32],
+                        const u32x4(&qd)[D / 32], int stage, SubTile &s2,
+                        u32x4(&kr2)[2][D / 32], u32x4(&qd2)[D / 32], int stage2, int tab2,
+                        int &tab4) {
+            vm_wait<kGroup>();
+            s2 = advance(kc);
+            issue_group(s2, tab2, kr2, qd2, stage2, tab4);
+            compute(s, kr, qd, stage);
+        };
+
+        // prologue: sub-tiles 0 and 1 (paged: their page numbers first)
+        st0 = advance(kc);
+        st1 = advance(kc);
+        if constexpr (PAGED) {
+            tb0 = load_tab(advance(tc));
+            tb1 = load_tab(advance(tc));
+            vm_wait<0>();
+        }
+        issue_group(st0, tb0, kr0, qb0, 0, tb2);  // + sub-tile 2's page numbers
+        issue_group(st1, tb1, kr1, qb1, 1, tb0);  // + sub-tile 3's (slot 3 % 3)
+        for (;;) {
+            if (!st0.valid)
+                break;
+            step(st0, kr0, qb0, 0, st2, kr2, qb2, 2, tb2, tb1);
+            if (!st1.valid)
+                break;
+            step(st1, kr1, qb1, 1, st0, kr0, qb0, 0, tb0, tb2);
+            if (!st2.valid)
+                break;
+            step(st2, kr2, qb2, 2, st1, kr1, qb1, 1, tb1, tb0);
+        }
+        vm_wait<0>();  // the stand-ins' loads: nothing stays in flight
+        // next window: the sequence after this window's last one
+        x = x1;
+        b = wb + 64;
+        seq0 = wend;
     }
 }
 
-// One wave per (sequence, query head): lanes take the chunk LSEs 64 at a
-// time for the max and the weight sum, then each lane accumulates D/64
-// features over the chunks, with the rows of 64 chunks in flight at once.
+// One wave per (sequence, query head): the partials of the waves whose
+// ranges met the head's segment sit in consecutive slots; lanes take their
+// LSEs 64 at a time for the max and the weight sum, then each lane
+// accumulates D/64 features over the partials.
 constexpr int kMergeWaves = 4;
 
 template <int D, bool OUT_F32>
@@ -315,37 +540,48 @@ __global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(DecodeAr
     const int bh = (int)blockIdx.x * kMergeWaves + (int)(threadIdx.x >> 6);
     if (bh >= a.B * a.H)
         return;
-    const int b = bh / a.H;
+    const KeySplit ks = key_split(a, lane);
+    const int G = a.H / a.Hkv;
+    const int b = bh / a.H, h = bh % a.H, kvh = h / G, g = h % G;
+    // global offset of the segment (b, kvh): locate its sequence's first key
+    long long seq0 = 0;
+    {
+        long long base = 0;
+        for (int b0 = 0; b0 < b; b0 += 64) {
+            const int bb = b0 + lane;
+            long long len = bb < b ? clamp_len(a.seqlens, bb, a.N_max) : 0;
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1)
+                len += __shfl_xor(len, off, 64);
+            base += len;
+        }
+        seq0 = base * a.Hkv;
+    }
     const int L = clamp_len(a.seqlens, b, a.N_max);
-    const int ns = (L + a.split_tokens - 1) / a.split_tokens;
-    const float *pl = a.part_lse + (size_t)bh * a.max_splits;
-    const float *po = a.part_o + (size_t)bh * a.max_splits * D + F * lane;
+    const long long s0 = seq0 + (long long)kvh * L;
+    const int seg = b * a.Hkv + kvh;
+    const int first = seg + ks.wave_of(s0), last = seg + ks.wave_of(s0 + L - 1);
+    const int n = last - first + 1;
+    const float *pl = a.part_lse + g;             // slot s: pl[s * G]
+    const float *po = a.part_o + (size_t)g * D + F * lane;  // slot s: po[s * G * D]
     float M = -INFINITY;
-    for (int s = lane; s < ns; s += 64)
-        M = fmaxf(M, pl[s]);
+    for (int j = lane; j < n; j += 64)
+        M = fmaxf(M, pl[(size_t)(first + j) * G]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1)
         M = fmaxf(M, __shfl_xor(M, off, 64));
     float wsum = 0.f;
     float acc[F] = {};
-    for (int s0 = 0; s0 < ns; s0 += 64) {
-        const float w = s0 + lane < ns ? fast_exp2(pl[s0 + lane] - M) : 0.f;
-        wsum += w;
-        const int n = min(64, ns - s0);
-        // all 64 chunk rows of the batch in flight at once (rows past the
-        // last chunk re-read it and carry weight 0)
-        float x[64][F];
-#pragma unroll
-        for (int j = 0; j < 64; ++j)
+    for (int j0 = 0; j0 < n; j0 += 64) {
+        const float wj_l = j0 + lane < n ? fast_exp2(pl[(size_t)(first + j0 + lane) * G] - M) : 0.f;
+        wsum += wj_l;
+        const int m = min(64, n - j0);
+        for (int j = 0; j < m; ++j) {
+            const float wj = __shfl(wj_l, j, 64);
+            const float *row = po + (size_t)(first + j0 + j) * G * D;
 #pragma unroll
             for (int f = 0; f < F; ++f)
-                x[j][f] = po[(size_t)(s0 + min(j, n - 1)) * D + f];
-#pragma unroll
-        for (int j = 0; j < 64; ++j) {
-            const float wj = __shfl(w, j, 64);
-#pragma unroll
-            for (int f = 0; f < F; ++f)
-                acc[f] = fmaf(wj, x[j][f], acc[f]);
+                acc[f] = fmaf(wj, row[f], acc[f]);
         }
     }
 #pragma unroll
@@ -367,9 +603,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(DecodeAr
 template <int D, int G>
 hipError_t launch_split(const DecodeArgs &a, hipStream_t s)
 {
-    // one wave per possible chunk; waves past the last non-empty chunk exit
-    const long long items = (long long)a.B * a.Hkv * a.max_splits;
-    dim3 grid((unsigned)((items + kWavesPerWG - 1) / kWavesPerWG));
+    const dim3 grid(kDecodeWaves / kWavesPerWG);
     ProfScope ps(a.block_table ? "decode_split_paged" : "decode_split", s);
     if (a.block_table)
         hipLaunchKernelGGL((decode_split_kernel<D, G, true>), grid, dim3(64 * kWavesPerWG), 0, s,
@@ -403,6 +637,8 @@ hipError_t launch_d(const DecodeArgs &a, hipStream_t s)
 }
 
 }  // namespace
+
+size_t decode_partial_slots(int B, int Hkv) { return (size_t)B * Hkv + kDecodeWaves; }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s)
 {

@@ -138,10 +138,6 @@ def _decp(A, **kw):
     (dict(num_pages=0), -1), (dict(max_pages=-1), -1),
     (dict(page_size=0), -1), (dict(page_size=24), -1), (dict(page_size=-16), -1),
     (dict(page_size=8), -2),                                   # below 16
-    (dict(page_size=16, split_tokens=2048), -2),               # a chunk would span 128 pages
-    # 256-row pages do not divide 16320-key chunks: chunk 1 starts 192 rows into
-    # a page and touches 65 pages
-    (dict(page_size=256, split_tokens=16320), -2),
     (dict(page_size=1 << 20, max_pages=4096), -2),             # 2^32 positions
     (dict(H=7), -1), (dict(split_tokens=100), -1), (dict(mode=1), -2), (dict(d=80), -2),
     (dict(workspace=None), -3), (dict(workspace_bytes=1000), -3),
@@ -152,19 +148,25 @@ def test_decode_paged_validation(A, kw, status):
 
 
 def test_decode_paged_workspace_is_decode_workspace(A):
-    # the paged call needs exactly the contiguous call's workspace for N_max = max_pages * page_size
-    need = A.attn_decode_workspace_size(2, 8, 64 * 16, 128, 512)
+    # the paged call needs exactly the contiguous call's workspace
+    need = A.attn_decode_workspace_size(2, 8, 2, 128)
     assert _decp(A, workspace_bytes=need - 1) == -3
+    assert _dec(A, workspace_bytes=need - 1) == -3
 
 
 def test_workspace_sizes(A):
-    # partial O fp32 [B,H,splits,d] + partial lse fp32 [B,H,splits], each 256-B aligned
-    B, H, N, d, s = 64, 32, 32768, 128, 512
-    splits = N // s
-    o_b = 4 * B * H * splits * d
-    l_b = 4 * B * H * splits
-    assert A.attn_decode_workspace_size(B, H, N, d, s) == o_b + ((l_b + 255) // 256) * 256
-    assert A.attn_decode_workspace_size(0, H, N, d, s) == 0
+    # one partial per (wave, sequence, kv head) piece: B*Hkv + 1024 slots of
+    # G = H/Hkv rows, partial O fp32 [slots, G, d] + partial lse fp32
+    # [slots, G], each 256-B aligned; independent of N_max and split_tokens
+    B, H, Hkv, d = 64, 32, 8, 128
+    slots = B * Hkv + 1024
+    G = H // Hkv
+    o_b = 4 * slots * G * d
+    l_b = 4 * slots * G
+    r = lambda x: (x + 255) // 256 * 256
+    assert A.attn_decode_workspace_size(B, H, Hkv, d) == r(o_b) + r(l_b)
+    assert A.attn_decode_workspace_size(0, H, Hkv, d) == 0
+    assert A.attn_decode_workspace_size(B, H, 5, d) == 0
     assert A.attn_fwd_workspace_size(1, 4, 2, 16, 128, 0) == 0
 
 

@@ -111,7 +111,7 @@ def test_decode_rejects_bad_outputs(attn):
                                                  device="cuda"))
     with pytest.raises(ValueError):
         attn.decode(q, kc, kc, sl, lse=torch.empty((B, H), dtype=torch.float32))
-    need = attn.attn_decode_workspace_size(B, H, N, d, 64)
+    need = attn.attn_decode_workspace_size(B, H, Hkv, d)
     with pytest.raises(ValueError):
         attn.decode(q, kc, kc, sl, split_tokens=64,
                     workspace=torch.empty((need - 1,), dtype=torch.uint8, device="cuda"))
@@ -157,7 +157,7 @@ def test_decode_workspace_contents_do_not_matter(attn):
     vc = torch.randn((B, Hkv, N, d), generator=g).to(torch.bfloat16).cuda()
     sl = torch.tensor([1, 777, 2000], dtype=torch.int32, device="cuda")
     for split in (64, 512):
-        need = attn.attn_decode_workspace_size(B, H, N, d, split)
+        need = attn.attn_decode_workspace_size(B, H, Hkv, d)
         a = attn.decode(q, kc, vc, sl, split_tokens=split, out_dtype=torch.float32,
                         workspace=torch.zeros((need,), dtype=torch.uint8, device="cuda"))
         b = attn.decode(q, kc, vc, sl, split_tokens=split, out_dtype=torch.float32,

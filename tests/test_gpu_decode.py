@@ -223,3 +223,48 @@ def test_paged_decode_clamps_bad_page_numbers(attn):
     torch.cuda.synchronize()
     # the pool holds only real rows (no spare pages, no partial last page)
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
+# ------------------------------------------------- the work split's edge cases
+
+def _decode_vs_oracle(attn, B, H, Hkv, N, d, lens, split, seed, what):
+    q, k, v, _ = workloads.make_prefill(B, H, Hkv, N, d, seed=seed)
+    q = q[:, :, 0].contiguous()
+    seqlens = torch.tensor(lens, dtype=torch.int32)
+    for b, L in enumerate(lens):
+        k[b, :, L:] = float("nan")
+        v[b, :, L:] = float("nan")
+    o, lse = attn.decode(q.cuda(), k.cuda(), v.cuda(), seqlens.cuda(), split_tokens=split,
+                         out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = _oracle(q, k, v, seqlens, 1 / math.sqrt(d))
+    return check_exact(o.cpu().numpy(), o_ref, lse.cpu().numpy(), lse_ref, bf16_out=False,
+                       what=what)
+
+
+def test_decode_many_short_sequences(attn):
+    """300 sequences of 1 to 8 keys with one kv head: a wave's range crosses
+    hundreds of sequences (its window of 64 sequence lengths is reloaded) and
+    most pieces are shorter than a sub-tile."""
+    g = torch.Generator().manual_seed(5)
+    lens = torch.randint(1, 9, (300,), generator=g).tolist()
+    res = _decode_vs_oracle(attn, 300, 4, 1, 8, 128, lens, 64, 41, "300 short sequences")
+    print(res)
+
+
+def test_decode_one_long_sequence(attn):
+    """One sequence of 70000 keys over two kv heads: every wave's range lies in
+    one segment, and each head merges hundreds of partials (the merge's
+    64-at-a-time loop)."""
+    res = _decode_vs_oracle(attn, 1, 8, 2, 70000, 128, (70000,), 512, 42, "one long sequence")
+    print(res)
+
+
+def test_decode_ragged_lengths_all_group_sizes(attn):
+    """Lengths that are not multiples of the 32-key sub-tile, for every group
+    size, at d 64 and 128."""
+    for G in (1, 2, 4, 8, 16):
+        for d in (64, 128):
+            lens = (33, 1000, 4097, 31, 555)
+            _decode_vs_oracle(attn, 5, 2 * G, 2, 4200, d, lens, 128, G + d,
+                              "G%d d%d" % (G, d))
