@@ -211,6 +211,26 @@ attn_status attn_decode(const void *q, const void *k_cache, const void *v_cache,
 size_t attn_decode_workspace_size(int B, int H, int Hkv, int d);
 
 /*
+ * attn_decode without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  The same kernels and the same result as attn_decode
+ * (bit for bit); the partials live in a fixed array of the library,
+ * ATTN_DECODE_SCRATCH_BYTES on every GPU it runs on, held until the process
+ * ends.  Nothing is allocated or freed.  The caller still passes the inputs
+ * and outputs; every partial the merge reads is written by the same call, so
+ * the array needs no clearing.
+ * Calls on one GPU share its array: calls that overlap in time on one GPU
+ * (other streams, other threads) race and must be serialised by the caller.
+ * Errors: those of attn_decode (no workspace error), and ATTN_ERR_UNSUPPORTED
+ * when attn_decode_workspace_size(B, H, Hkv, d) exceeds the array.
+ */
+#define ATTN_DECODE_SCRATCH_BYTES ((size_t)16 << 20)
+attn_status attn_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                const int32_t *seqlens, void *o, float *lse, int B, int H,
+                                int Hkv, int N_max, int d, float scale, int mode, int o_dtype,
+                                int split_tokens, void *stream);
+
+/*
  * attn_decode over paged KV caches: the cache is a pool of fixed-size pages
  * and a per-sequence page table names the page holding each run of
  * page_size key positions (the non-contiguous KV layout of paged serving

@@ -39,7 +39,7 @@ EXPORTS = ("attn_fwd", "attn_fwd_workspace_size", "attn_fwd_varlen", "attn_bwd",
            "attn_bwd_workspace_size", "attn_decode", "attn_decode_workspace_size",
            "attn_decode_paged", "attn_status_string", "attn_last_error",
            "attn_profiler_enable", "attn_profiler_read", "attn_profiler_launches",
-           "attn_sage_workspace_layout")
+           "attn_sage_workspace_layout", "attn_decode_noalloc")
 
 
 class AttnError(RuntimeError):
@@ -66,6 +66,8 @@ def _load():
     lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, vp]
     lib.attn_decode.restype = i
     lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, sz, vp]
+    lib.attn_decode_noalloc.restype = i
+    lib.attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp]
     lib.attn_decode_workspace_size.restype = sz
     lib.attn_decode_workspace_size.argtypes = [i, i, i, i]
     lib.attn_decode_paged.restype = i
@@ -155,6 +157,16 @@ def attn_decode(q, k_cache, v_cache, seqlens, o, lse, B, H, Hkv, N_max, d, scale
     return int(_lib.attn_decode(q, k_cache, v_cache, seqlens, o, lse, B, H, Hkv, N_max, d,
                                 scale, mode, o_dtype, split_tokens, workspace,
                                 workspace_bytes, stream))
+
+
+def attn_decode_noalloc(q, k_cache, v_cache, seqlens, o, lse, B, H, Hkv, N_max, d, scale, mode,
+                        o_dtype, split_tokens, stream) -> int:
+    return int(_lib.attn_decode_noalloc(q, k_cache, v_cache, seqlens, o, lse, B, H, Hkv, N_max,
+                                        d, scale, mode, o_dtype, split_tokens, stream))
+
+
+# the size of the library's fixed decode array (ATTN_DECODE_SCRATCH_BYTES)
+DECODE_SCRATCH_BYTES = 16 << 20
 
 
 def attn_decode_paged(q, k_pages, v_pages, block_table, seqlens, o, lse, B, H, Hkv, num_pages,
@@ -423,6 +435,42 @@ def decode(q, k_cache, v_cache, seqlens, *, scale: float | None = None,
                           _ptr(lse), B, H, Hkv, N_max, d, float(scale), ATTN_MODE_EXACT_BF16,
                           o_code, int(split_tokens), _ptr(workspace), ws_len,
                           _stream(stream))
+    _check(st)
+    return o, lse
+
+
+def decode_noalloc(q, k_cache, v_cache, seqlens, o, lse=None, *, scale: float | None = None,
+                   split_tokens: int = 512, stream=None):
+    """``decode`` without a workspace: the partials live in the library's
+    fixed array on the GPU (see ``attn_decode_noalloc`` in attn.h), so the
+    call allocates nothing.  The caller passes o (bf16 or fp32 [B,H,d]) and,
+    optionally, lse (fp32 [B,H]); returns (o, lse)."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, 4)
+    _need(seqlens, "seqlens", torch.int32, 1)
+    B, H, d = q.shape
+    _, Hkv, N_max, _ = k_cache.shape
+    if tuple(k_cache.shape) != (B, Hkv, N_max, d) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("cache shapes do not match q")
+    if seqlens.shape[0] != B:
+        raise ValueError("seqlens must have B entries")
+    if not isinstance(o, torch.Tensor):
+        raise TypeError("o must be a torch tensor")
+    o_code = _out_code(o.dtype, "o.dtype")
+    dev = q.device
+    for t, name in ((k_cache, "k_cache"), (v_cache, "v_cache"), (seqlens, "seqlens")):
+        if t.device != dev:
+            raise ValueError("%s is on %s, q on %s" % (name, t.device, dev))
+    _need_out(o, "o", o.dtype, (B, H, d), dev)
+    if lse is not None:
+        _need_out(lse, "lse", torch.float32, (B, H), dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = _lib.attn_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(o),
+                                  _ptr(lse), B, H, Hkv, N_max, d, float(scale),
+                                  ATTN_MODE_EXACT_BF16, o_code, int(split_tokens),
+                                  _stream(stream))
     _check(st)
     return o, lse
 

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdint>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -110,6 +111,16 @@ void prof_end(hipStream_t s)
 
 namespace {
 
+// The partial outputs and LSEs of the split kernel, carved from `base` (the
+// layout attn_decode_workspace_size counts).
+void set_partials(attn::DecodeArgs &a, void *base)
+{
+    const size_t slots = attn::decode_partial_slots(a.B, a.Hkv);
+    a.part_o = (float *)base;
+    a.part_lse =
+        (float *)((char *)base + align_up(sizeof(float) * slots * (a.H / a.Hkv) * a.d, 256));
+}
+
 // Checks shared by the contiguous and the paged decode; fills everything of
 // DecodeArgs but the cache layout.
 attn_status decode_common(const void *q, const void *k_cache, const void *v_cache,
@@ -167,10 +178,7 @@ attn_status decode_common(const void *q, const void *k_cache, const void *v_cach
     a.scale = scale;
     a.out_fp32 = o_dtype == ATTN_OUT_FP32;
     a.split_tokens = split_tokens;
-    const size_t slots = attn::decode_partial_slots(B, Hkv);
-    a.part_o = (float *)workspace;
-    a.part_lse = (float *)((char *)workspace +
-                           align_up(sizeof(float) * slots * (H / Hkv) * d, 256));
+    set_partials(a, workspace);
     return ATTN_OK;
 }
 
@@ -365,6 +373,32 @@ attn_status attn_decode(const void *q, const void *k_cache, const void *v_cache,
                                          workspace_bytes, a);
     if (st != ATTN_OK)
         return st;
+    return from_hip(attn::launch_decode(a, (hipStream_t)stream), "decode launch");
+}
+
+attn_status attn_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                const int32_t *seqlens, void *o, float *lse, int B, int H,
+                                int Hkv, int N_max, int d, float scale, int mode, int o_dtype,
+                                int split_tokens, void *stream)
+{
+    attn::DecodeArgs a;
+    // every check of attn_decode but the workspace's (a stand-in pointer
+    // that is never used: the partials are re-pointed below)
+    attn_status st = decode_common(q, k_cache, v_cache, seqlens, o, lse, B, H, Hkv, N_max, d,
+                                   scale, mode, o_dtype, split_tokens, (void *)q, SIZE_MAX, a);
+    if (st != ATTN_OK)
+        return st;
+    const size_t need = attn_decode_workspace_size(B, H, Hkv, d);
+    if (need > ATTN_DECODE_SCRATCH_BYTES)
+        return fail(ATTN_ERR_UNSUPPORTED,
+                    "attn_decode_noalloc: the partials need %zu bytes, the library's fixed "
+                    "array holds %zu (use attn_decode with a workspace)",
+                    need, (size_t)ATTN_DECODE_SCRATCH_BYTES);
+    void *scratch = nullptr;
+    st = from_hip(attn::decode_scratch(&scratch), "attn_decode_noalloc scratch address");
+    if (st != ATTN_OK)
+        return st;
+    set_partials(a, scratch);
     return from_hip(attn::launch_decode(a, (hipStream_t)stream), "decode launch");
 }
 

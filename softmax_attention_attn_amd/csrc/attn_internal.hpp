@@ -70,6 +70,9 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);  // contiguous or 
 // waves (four per CU of a 256-CU MI355X, all resident at once).
 constexpr int kDecodeWaves = 1024;
 size_t decode_partial_slots(int B, int Hkv);
+// Device address, on the current device, of the fixed array that holds the
+// partials of attn_decode_noalloc (ATTN_DECODE_SCRATCH_BYTES bytes).
+hipError_t decode_scratch(void **ptr);
 hipError_t launch_sage(const SageArgs &a, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t s);
 size_t sage_workspace_bytes(int B, int H, int Hkv, int N, int d);

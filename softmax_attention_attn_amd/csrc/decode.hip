@@ -34,6 +34,9 @@
 // The path is HBM bound (a few FLOPs per byte): each wave keeps two sub-tiles
 // of K and V in flight (about 32 KB), uses the matrix cores for the small
 // products so the VALU stays free, and never waits on other waves.
+#include <mutex>
+
+#include "../../include/attn.h"
 #include "attn_internal.hpp"
 #include "cdna4.hpp"
 
@@ -636,9 +639,39 @@ hipError_t launch_d(const DecodeArgs &a, hipStream_t s)
     return hipGetLastError();
 }
 
+// The partials of attn_decode_noalloc: a fixed array on every GPU the library
+// runs on, held until the process ends.  In host code `scratch` names a
+// host-side stand-in, never the device array: its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+static __device__ __align__(256) unsigned char scratch[ATTN_DECODE_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
 }  // namespace
 
 size_t decode_partial_slots(int B, int Hkv) { return (size_t)B * Hkv + kDecodeWaves; }
+
+hipError_t decode_scratch(void **ptr)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s)
 {

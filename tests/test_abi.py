@@ -125,6 +125,36 @@ def test_decode_validation(A, kw, status):
     assert _dec(A, **kw) == status
 
 
+def _decn(A, **kw):
+    args = dict(q=P, k_cache=P, v_cache=P, seqlens=P, o=P, lse=None, B=2, H=8, Hkv=2,
+                N_max=1024, d=128, scale=0.1, mode=0, o_dtype=0, split_tokens=512, stream=None)
+    args.update(kw)
+    return A.attn_decode_noalloc(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(seqlens=None), -1), (dict(o=None), -1), (dict(B=0), -1), (dict(H=7), -1),
+    (dict(H=6), -2), (dict(scale=-1.0), -1), (dict(split_tokens=100), -1), (dict(mode=1), -2),
+    (dict(d=80), -2),
+    # the partials of B1024 H64 Hkv8 d128 need 37.7 MB, beyond the 16 MiB array
+    (dict(B=1024, H=64, Hkv=8), -2),
+])
+def test_decode_noalloc_validation(A, kw, status):
+    assert _decn(A, **kw) == status
+    assert A.attn_last_error() != ""
+
+
+def test_decode_noalloc_rejects_beyond_the_array(A):
+    # the first B at H32 Hkv8 d128 whose partials exceed the fixed array is
+    # rejected before any HIP call (the GPU test runs the largest that fits)
+    lim = A.DECODE_SCRATCH_BYTES
+    B = 1
+    while A.attn_decode_workspace_size(B + 1, 32, 8, 128) <= lim:
+        B += 1
+    assert _decn(A, B=B + 1, H=32, Hkv=8) == -2
+    assert "fixed array" in A.attn_last_error()
+
+
 def _decp(A, **kw):
     args = dict(q=P, k_pages=P, v_pages=P, block_table=P, seqlens=P, o=P, lse=None, B=2, H=8,
                 Hkv=2, num_pages=40, page_size=16, max_pages=64, d=128, scale=0.1, mode=0,
