@@ -30,7 +30,13 @@ What each routine follows:
   Q/K per 64-token block, E4M3 P and per-channel E4M3 V, fp32 accumulation)
   emulated step by step ("GPU kernel overview" page, SageAttention chain and
   its insight that QK suits INT8 while PV suits FP8).
-* ``e4m3_decode`` / ``e4m3_encode`` -- the OCP E4M3 ("fn") format.
+* ``mxfp4_rows`` -- the MXFP4 variant of the quantised recipe (SageAttention3's
+  FP4 microscaling on CDNA4's MX formats: E2M1 elements with a power-of-two
+  E8M0 scale per block of 32, for Q, K, V and P; "gpu-kernel-porting-with-ai-agents"
+  page, SageAttention 3 section; "GPU kernel overview" page, insights on FP4).
+* ``e4m3_decode`` / ``e4m3_encode`` -- the OCP E4M3 ("fn") format;
+  ``e2m1_decode`` / ``e2m1_encode`` / ``mx_scale_exp`` -- the MX FP4 element
+  format and the choice of a block's scale.
 * ``gather_pages`` -- the paged KV layout (a pool of fixed-size pages named by
   a per-sequence page table) turned back into contiguous caches, so that
   paged decode is checked against ``attn_rows`` ("flashattention-kernels"
@@ -102,6 +108,17 @@ def _load():
     lib.oracle_e4m3_encode.argtypes = [ctypes.c_double]
     lib.oracle_quant_i8.restype = ctypes.c_int
     lib.oracle_quant_i8.argtypes = [ctypes.c_double, ctypes.c_double]
+    lib.oracle_e2m1_decode.restype = ctypes.c_double
+    lib.oracle_e2m1_decode.argtypes = [ctypes.c_uint8]
+    lib.oracle_e2m1_encode.restype = ctypes.c_uint8
+    lib.oracle_e2m1_encode.argtypes = [ctypes.c_double]
+    lib.oracle_mx_scale_exp.restype = ctypes.c_int
+    lib.oracle_mx_scale_exp.argtypes = [ctypes.c_double]
+    lib.oracle_mxfp4_rows.restype = ctypes.c_double
+    lib.oracle_mxfp4_rows.argtypes = [
+        _u16p, _u16p, _u16p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_int, ctypes.c_int, _i64p, ctypes.c_int64, _f64p, _f64p, ctypes.c_int]
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -297,6 +314,60 @@ def sage_quantise(q, k, v, *, blk: int = 64, smooth_k: bool = True):
     if r < 0:
         raise ValueError("oracle_sage_quantise rejected its arguments")
     return out
+
+
+def mxfp4_rows(q, k, v, *, causal: bool, scale: float, rows=None, tile_n: int = 64,
+               smooth_k: bool = True, quant_qk: bool = True, quant_p: bool = True,
+               quant_v: bool = True, threads: int | None = None):
+    """MXFP4 quantised attention (SageAttention3-style, MX block formats)
+    emulated step by step in fp64; see ``oracle_mxfp4_rows`` in oracle.c.
+    Same shapes and ``rows`` convention as :func:`sage_rows`.  Returns
+    (o, lse)."""
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, N, d) or v.shape != k.shape:
+        raise ValueError("shape mismatch")
+    if rows is None:
+        nrows = B * H * N
+        rows_p = None
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        nrows = rows.size
+        rows_p = _ptr(rows, _i64p)
+    o = np.empty((nrows, d), dtype=np.float64)
+    lse = np.empty((nrows,), dtype=np.float64)
+    r = _load().oracle_mxfp4_rows(_ptr(q, _u16p), _ptr(k, _u16p), _ptr(v, _u16p), B, H, Hkv, N,
+                                  d, int(bool(causal)), float(scale), int(tile_n),
+                                  int(smooth_k), int(quant_qk), int(quant_p), int(quant_v),
+                                  rows_p, nrows, _ptr(o, _f64p), _ptr(lse, _f64p),
+                                  int(threads or default_threads()))
+    if r < 0:
+        raise ValueError("oracle_mxfp4_rows rejected its arguments")
+    if rows is None:
+        o = o.reshape(B, H, N, d)
+        lse = lse.reshape(B, H, N)
+    return o, lse
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    lib = _load()
+    codes = np.asarray(codes, dtype=np.uint8)
+    return np.array([lib.oracle_e2m1_decode(int(c)) for c in codes.ravel()]).reshape(codes.shape)
+
+
+def e2m1_encode(x) -> np.ndarray:
+    lib = _load()
+    x = np.asarray(x, dtype=np.float64)
+    return np.array([lib.oracle_e2m1_encode(float(t)) for t in x.ravel()],
+                    dtype=np.uint8).reshape(x.shape)
+
+
+def mx_scale_exp(amax) -> np.ndarray:
+    lib = _load()
+    a = np.asarray(amax, dtype=np.float64)
+    return np.array([lib.oracle_mx_scale_exp(float(t)) for t in a.ravel()],
+                    dtype=np.int64).reshape(a.shape)
 
 
 def e4m3_decode(codes) -> np.ndarray:

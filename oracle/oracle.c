@@ -643,6 +643,252 @@ int oracle_sage_quantise(const uint16_t *q, const uint16_t *k, const uint16_t *v
     return 0;
 }
 
+/* ------------------------------------------------------------------------ */
+/* MXFP4 quantised attention (SageAttention3-style, MX block formats)        */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * OCP MX FP4 E2M1: 1 sign bit, 2 exponent bits (bias 1), 1 mantissa bit, no
+ * infinities or NaN.  Exponent field 0 is subnormal (0 or 0.5); otherwise
+ * 2^(E-1) * (1 + M/2).  Magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+ */
+double oracle_e2m1_decode(uint8_t code)
+{
+    int s = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+    double mag = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return s ? -mag : mag;
+}
+
+/* Nearest E2M1 code, ties to the even code, saturating at +-6 (the positive
+ * codes 0..7 are increasing in value). */
+uint8_t oracle_e2m1_encode(double x)
+{
+    uint8_t sign = x < 0 ? 8 : 0;
+    double a = fabs(x);
+    if (a >= 6.0)
+        return sign | 7;
+    int c = 0;
+    while (c < 7 && oracle_e2m1_decode((uint8_t)(c + 1)) <= a)
+        ++c;
+    if (c < 7) {
+        double db = a - oracle_e2m1_decode((uint8_t)c);
+        double da = oracle_e2m1_decode((uint8_t)(c + 1)) - a;
+        if (da < db || (da == db && ((c + 1) & 1) == 0))
+            c = c + 1;
+    }
+    return sign | (uint8_t)c;
+}
+
+/*
+ * Exponent e of the shared E8M0 scale 2^e of one MX block: the smallest
+ * power of two with amax <= 6 * 2^e, so that the block's largest element
+ * lands on E2M1's largest magnitude or below it and nothing saturates (the
+ * block's maximum maps into [0, 6 * 2^e], as SageAttention3 maps each block
+ * onto the FP4 range).  Clamped to E8M0's range [-127, 127]; an all-zero
+ * block gets e = 0.
+ */
+int oracle_mx_scale_exp(double amax)
+{
+    if (!(amax > 0.0))
+        return 0;
+    int e = -127;
+    while (e < 127 && amax > ldexp(6.0, e))
+        ++e;
+    return e;
+}
+
+typedef struct {
+    double *kmean; /* [B*Hkv][d] (fp32 values) */
+    double *qd;    /* [B*H][N][d]   dequantised MXFP4 Q */
+    double *kd;    /* [B*Hkv][N][d] dequantised MXFP4 K - kmean */
+    double *vd;    /* [B*Hkv][N][d] dequantised MXFP4 V */
+} mx_state;
+
+/* Dequantised value of x in an MX block with shared exponent e. */
+static double mx_round(double x, int e)
+{
+    return ldexp(oracle_e2m1_decode(oracle_e2m1_encode(ldexp(x, -e))), e);
+}
+
+static void mx_prepare(const uint16_t *q, const uint16_t *k, const uint16_t *v, int B, int H,
+                       int Hkv, int N, int d, int smooth_k, int quant_qk, int quant_v,
+                       mx_state *st)
+{
+    /*
+     * Q and K - kmean: blocks of 32 consecutive channels of one token (the
+     * contraction dimension of Q K^T); V: blocks of 32 consecutive tokens of
+     * one channel (the contraction dimension of P V).  K - kmean is formed
+     * in fp32 (as the kernel does); every other value is exact.
+     */
+    st->kmean = (double *)calloc((size_t)B * Hkv * d, sizeof(double));
+    st->qd = (double *)malloc(sizeof(double) * (size_t)B * H * N * d);
+    st->kd = (double *)malloc(sizeof(double) * (size_t)B * Hkv * N * d);
+    st->vd = (double *)malloc(sizeof(double) * (size_t)B * Hkv * N * d);
+#pragma omp parallel for
+    for (int64_t bg = 0; bg < (int64_t)B * Hkv; ++bg) {
+        const uint16_t *kb = k + bg * (int64_t)N * d, *vb = v + bg * (int64_t)N * d;
+        if (smooth_k) {
+            for (int c = 0; c < d; ++c) {
+                double s = 0.0;
+                for (int64_t n = 0; n < N; ++n)
+                    s += bf16_to_f64(kb[n * d + c]);
+                st->kmean[bg * d + c] = (double)(float)(s / N);
+            }
+        }
+        for (int64_t n = 0; n < N; ++n)
+            for (int c0 = 0; c0 < d; c0 += 32) {
+                double x[32], amax = 0.0;
+                for (int c = 0; c < 32; ++c) {
+                    x[c] = (double)((float)bf16_to_f64(kb[n * d + c0 + c]) -
+                                    (float)st->kmean[bg * d + c0 + c]);
+                    if (fabs(x[c]) > amax)
+                        amax = fabs(x[c]);
+                }
+                int e = oracle_mx_scale_exp(amax);
+                /* without quantisation K - kmean is taken exactly */
+                for (int c = 0; c < 32; ++c)
+                    st->kd[(bg * N + n) * d + c0 + c] =
+                        quant_qk ? mx_round(x[c], e)
+                                 : bf16_to_f64(kb[n * d + c0 + c]) - st->kmean[bg * d + c0 + c];
+            }
+        for (int c = 0; c < d; ++c)
+            for (int64_t n0 = 0; n0 < N; n0 += 32) {
+                int64_t n1 = n0 + 32 < N ? n0 + 32 : N;
+                double amax = 0.0;
+                for (int64_t n = n0; n < n1; ++n)
+                    if (fabs(bf16_to_f64(vb[n * d + c])) > amax)
+                        amax = fabs(bf16_to_f64(vb[n * d + c]));
+                int e = oracle_mx_scale_exp(amax);
+                for (int64_t n = n0; n < n1; ++n) {
+                    double x = bf16_to_f64(vb[n * d + c]);
+                    st->vd[(bg * N + n) * d + c] = quant_v ? mx_round(x, e) : x;
+                }
+            }
+    }
+#pragma omp parallel for
+    for (int64_t bh = 0; bh < (int64_t)B * H; ++bh) {
+        const uint16_t *qb = q + bh * (int64_t)N * d;
+        for (int64_t n = 0; n < N; ++n)
+            for (int c0 = 0; c0 < d; c0 += 32) {
+                double amax = 0.0;
+                for (int c = 0; c < 32; ++c)
+                    if (fabs(bf16_to_f64(qb[n * d + c0 + c])) > amax)
+                        amax = fabs(bf16_to_f64(qb[n * d + c0 + c]));
+                int e = oracle_mx_scale_exp(amax);
+                for (int c = 0; c < 32; ++c) {
+                    double x = bf16_to_f64(qb[n * d + c0 + c]);
+                    st->qd[(bh * N + n) * d + c0 + c] = quant_qk ? mx_round(x, e) : x;
+                }
+            }
+    }
+}
+
+/*
+ * MXFP4 quantised attention for the listed rows, the steps in order:
+ *   1. Smooth-K: K' = K - mean_n K (per channel, all tokens of the kv head);
+ *   2. Q and K' to MXFP4 in blocks of 32 channels, V in blocks of 32 tokens
+ *      (E2M1 elements, shared power-of-two scale, oracle_mx_scale_exp);
+ *   3. S_ij = scale * (q^_i . k^_j);
+ *   4. keys in tiles of tile_n (a multiple of 32) from key 0 upward, with the
+ *      exact running max m: m' = max(m, the tile's max visible score),
+ *      p_j = exp(S_ij - m') in (0, 1] (the per-row normalisation), l =
+ *      l * exp(m - m') + sum_j p_j, and P^ = MXFP4(p) in blocks of 32
+ *      consecutive keys (the block's max sets its scale), acc = acc *
+ *      exp(m - m') + sum_j P^_j V^_j;
+ *   5. O = acc / l;  lse = m + ln l + scale * (q_i . kmean).
+ * quant_qk / quant_p / quant_v = 0 skip a quantisation step.
+ */
+double oracle_mxfp4_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v, int B, int H,
+                         int Hkv, int N, int d, int causal, double scale, int tile_n,
+                         int smooth_k, int quant_qk, int quant_p, int quant_v,
+                         const int64_t *rows, int64_t nrows, double *o, double *lse,
+                         int nthreads)
+{
+    if (B <= 0 || H <= 0 || Hkv <= 0 || H % Hkv != 0 || N <= 0 || d <= 0 || d % 32 != 0 ||
+        tile_n <= 0 || tile_n % 32 != 0)
+        return -1.0;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    if (!rows)
+        nrows = (int64_t)B * H * N;
+    mx_state st;
+    mx_prepare(q, k, v, B, H, Hkv, N, d, smooth_k, quant_qk, quant_v, &st);
+#pragma omp parallel
+    {
+        double *S = (double *)malloc(sizeof(double) * (size_t)tile_n);
+        double *P = (double *)malloc(sizeof(double) * (size_t)tile_n);
+        double *acc = (double *)malloc(sizeof(double) * (size_t)d);
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t r = 0; r < nrows; ++r) {
+            int64_t row = rows ? rows[r] : r;
+            int64_t i = row % N, bh = row / N, h = bh % H, b = bh / H;
+            int64_t g = h / (H / Hkv), bg = b * Hkv + g;
+            const double *qr = st.qd + (bh * N + i) * d;
+            const uint16_t *qraw = q + (bh * N + i) * d;
+            int64_t nvis = causal ? i + 1 : N;
+            double m = -INFINITY, l = 0.0;
+            for (int c = 0; c < d; ++c)
+                acc[c] = 0.0;
+            for (int64_t j0 = 0; j0 < nvis; j0 += tile_n) {
+                int64_t j1 = j0 + tile_n < nvis ? j0 + tile_n : nvis;
+                double tmax = -INFINITY;
+                for (int64_t j = j0; j < j1; ++j) {
+                    const double *kr = st.kd + (bg * N + j) * d;
+                    double dot = 0.0;
+                    for (int c = 0; c < d; ++c)
+                        dot += qr[c] * kr[c];
+                    S[j - j0] = scale * dot;
+                    if (S[j - j0] > tmax)
+                        tmax = S[j - j0];
+                }
+                double mnew = tmax > m ? tmax : m;
+                double alpha = exp(m - mnew);
+                l *= alpha;
+                for (int c = 0; c < d; ++c)
+                    acc[c] *= alpha;
+                for (int64_t j = j0; j < j1; ++j) {
+                    P[j - j0] = exp(S[j - j0] - mnew);
+                    l += P[j - j0];
+                }
+                /* P^ per block of 32 consecutive keys (masked keys are 0) */
+                for (int64_t u0 = j0; u0 < j1; u0 += 32) {
+                    int64_t u1 = u0 + 32 < j1 ? u0 + 32 : j1;
+                    double pmax = 0.0;
+                    for (int64_t j = u0; j < u1; ++j)
+                        if (P[j - j0] > pmax)
+                            pmax = P[j - j0];
+                    int e = oracle_mx_scale_exp(pmax);
+                    for (int64_t j = u0; j < u1; ++j) {
+                        double ph = quant_p ? mx_round(P[j - j0], e) : P[j - j0];
+                        const double *vr = st.vd + (bg * N + j) * d;
+                        for (int c = 0; c < d; ++c)
+                            acc[c] += ph * vr[c];
+                    }
+                }
+                m = mnew;
+            }
+            double qk = 0.0;
+            for (int c = 0; c < d; ++c)
+                qk += bf16_to_f64(qraw[c]) * st.kmean[bg * d + c];
+            for (int c = 0; c < d; ++c)
+                o[r * d + c] = acc[c] / l;
+            lse[r] = m + log(l) + scale * qk;
+        }
+        free(S);
+        free(P);
+        free(acc);
+    }
+    free(st.kmean);
+    free(st.qd);
+    free(st.kd);
+    free(st.vd);
+    return 0.0;
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP
