@@ -18,11 +18,12 @@ workload has a bound worth stating:
   varlen     a packed batch of variable-length sequences;
   sage       the quantised prefill B2 H24 N16384 d128, with its quantisation
              statistics read back from the workspace;
+  mxfp4      the same inputs in the MXFP4 mode (FP4 MFMA);
   decode     GQA split-KV decode, contiguous caches and 16-row pages;
 and the fp64 CPU oracle timed on a bounded sample of the headline workload.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                  [--only prefill|noncausal|tiny|long|bwd|varlen|sage|decode]
+                  [--only prefill|noncausal|tiny|long|bwd|varlen|sage|mxfp4|decode]
                   [--calibrate-copy]
 """
 from __future__ import annotations
@@ -44,11 +45,12 @@ import workloads  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_FP8_TFLOPS = 5033.2    # fp8 / int8 dense
+PEAK_FP4_TFLOPS = 10066.3   # fp4 / fp6 dense (MX, scaled MFMA)
 PEAK_HBM_GBS = 8000.0       # HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 UTIL_FILE = os.path.join(ROOT, "profiles", "mfma_util.json")
 CSRC = os.path.join(ROOT, "softmax_attention_attn_amd", "csrc")
-LEGS = ("prefill", "noncausal", "tiny", "long", "bwd", "varlen", "sage", "decode")
+LEGS = ("prefill", "noncausal", "tiny", "long", "bwd", "varlen", "sage", "mxfp4", "decode")
 
 
 def log(*a):
@@ -348,6 +350,37 @@ def bench_sage(args, stream):
     }
 
 
+def bench_mxfp4(args, stream):
+    """The quantised-prefill inputs (B2 H24 N16384 d128) in the MXFP4 mode:
+    roofline for the fused FP4 kernel against the dense FP4 peak."""
+    import softmax_attention_attn_amd as A
+    w = workloads.WORKLOADS["sage_prefill"]
+    inp = workloads.make(w)
+    q, k, v = inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda()
+    del inp
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    ws = torch.empty((A.attn_fwd_workspace_size(w.B, w.H, w.Hkv, w.N, w.d, A.MODES["mxfp4"]),),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        A.fwd(q, k, v, causal=w.causal, mode="mxfp4", o=o, lse=lse, workspace=ws, stream=stream)
+
+    st, per_kernel = time_calls(step, args.steps, args.warmup, stream)
+    ops = w.flops()
+    files = ["mxfp4.hip", "cdna4.hpp"]
+    return {
+        "workload": w.name + "_mxfp4", "value": ops / (st["mean"] * 1e-3) / 1e12, "unit": "TOP/s",
+        "ms_per_step": st["mean"], "step_ms": st,
+        "note": "MXFP4 Q/K/V/P on the FP4 MFMA; value includes the quantisation prologue "
+                "kernels, the roofline the fused attention kernel",
+        "kernels_ms": per_kernel,
+        "roofline": roofline("mfma", "mx_attn", ops, per_kernel["mx_attn"], PEAK_FP4_TFLOPS,
+                             "TOP/s", traffic=measured_traffic("mx_attn", files),
+                             counters=measured_util("mx_attn", files)),
+    }
+
+
 def sage_error_budget():
     """The quantised recipe's error against exact attention split by source,
     as stored by tests/golden/make_sage_error_budget.py (oracle runs on the
@@ -534,6 +567,13 @@ def main():
         log("sage %.3f ms/step, %.1f TOP/s (attention kernel %.1f TOP/s)" % (
             sg["ms_per_step"], sg["value"], sg["roofline"]["achieved"]))
         out["sage"] = sg
+        torch.cuda.empty_cache()
+    if want("mxfp4"):
+        log("mxfp4: sage_prefill inputs, MXFP4 mode")
+        mx = bench_mxfp4(args, stream)
+        log("mxfp4 %.3f ms/step, %.1f TOP/s (attention kernel %.1f TOP/s)" % (
+            mx["ms_per_step"], mx["value"], mx["roofline"]["achieved"]))
+        out["mxfp4"] = mx
         torch.cuda.empty_cache()
     if want("decode"):
         log("decode: gqa_decode")

@@ -71,7 +71,19 @@ typedef enum {
      * channel) with scale max|V|/448; PV by an FP8 MFMA with fp32
      * accumulation.  lse is the true LSE (the Smooth-K shift q_i . kmean is
      * added back).  Needs a workspace. */
-    ATTN_MODE_SAGE_QK_I8_BLK64_PV_FP8_E4M3 = 1
+    ATTN_MODE_SAGE_QK_I8_BLK64_PV_FP8_E4M3 = 1,
+    /* SageAttention3-style FP4 microscaling on the MX block formats of the
+     * gfx950 matrix cores ("gpu-kernel-porting-with-ai-agents" page,
+     * SageAttention 3 section; "GPU kernel overview" page, insights on FP4
+     * attention): Smooth-K as above; Q and K' in MXFP4 blocks of 32
+     * consecutive channels of a token, V in blocks of 32 consecutive tokens
+     * of a channel, P = exp(S - m_running) (<= 1 per row) in blocks of 32
+     * consecutive keys: OCP E2M1 elements (nearest, ties to even) with one
+     * E8M0 scale 2^e per block, e the smallest exponent with
+     * max|x| <= 6 * 2^e (no element saturates); S = Q^ K^^T and O = P^ V^ on
+     * the FP4 MFMA with fp32 accumulation; l sums the unquantised P; lse is
+     * the true LSE.  Prefill only; needs a workspace. */
+    ATTN_MODE_SAGE3_QK_MXFP4_PV_MXFP4 = 2
 } attn_mode;
 
 typedef enum { ATTN_OUT_BF16 = 0, ATTN_OUT_FP32 = 1 } attn_dtype;

@@ -144,8 +144,10 @@ attn_status decode_common(const void *q, const void *k_cache, const void *v_cach
         return fail(ATTN_ERR_INVALID_ARG, "split_tokens=%d must be a positive multiple of 64",
                     split_tokens);
     if (mode != ATTN_MODE_EXACT_BF16)
-        return fail(mode == ATTN_MODE_SAGE_QK_I8_BLK64_PV_FP8_E4M3 ? ATTN_ERR_UNSUPPORTED
-                                                                   : ATTN_ERR_INVALID_ARG,
+        return fail(mode == ATTN_MODE_SAGE_QK_I8_BLK64_PV_FP8_E4M3 ||
+                            mode == ATTN_MODE_SAGE3_QK_MXFP4_PV_MXFP4
+                        ? ATTN_ERR_UNSUPPORTED
+                        : ATTN_ERR_INVALID_ARG,
                     "decode supports only the exact bf16 mode (mode=%d)", mode);
     if (d != 64 && d != 128)
         return fail(ATTN_ERR_UNSUPPORTED, "head dim d=%d (supported: 64, 128)", d);
@@ -206,6 +208,8 @@ size_t attn_fwd_workspace_size(int B, int H, int Hkv, int N, int d, int mode)
         return 0;
     if (mode == ATTN_MODE_SAGE_QK_I8_BLK64_PV_FP8_E4M3)
         return attn::sage_workspace_bytes(B, H, Hkv, N, d);
+    if (mode == ATTN_MODE_SAGE3_QK_MXFP4_PV_MXFP4)
+        return attn::mxfp4_workspace_bytes(B, H, Hkv, N, d);
     return 0;
 }
 
@@ -235,7 +239,8 @@ attn_status attn_fwd(const void *q, const void *k, const void *v, void *o, float
         return fail(ATTN_ERR_INVALID_ARG, "scale must be finite and > 0");
     if (o_dtype != ATTN_OUT_BF16 && o_dtype != ATTN_OUT_FP32)
         return fail(ATTN_ERR_INVALID_ARG, "unknown output dtype %d", o_dtype);
-    if (mode != ATTN_MODE_EXACT_BF16 && mode != ATTN_MODE_SAGE_QK_I8_BLK64_PV_FP8_E4M3)
+    if (mode != ATTN_MODE_EXACT_BF16 && mode != ATTN_MODE_SAGE_QK_I8_BLK64_PV_FP8_E4M3 &&
+        mode != ATTN_MODE_SAGE3_QK_MXFP4_PV_MXFP4)
         return fail(ATTN_ERR_INVALID_ARG, "unknown mode %d", mode);
     if (d != 64 && d != 128)
         return fail(ATTN_ERR_UNSUPPORTED, "head dim d=%d (supported: 64, 128)", d);
@@ -255,6 +260,8 @@ attn_status attn_fwd(const void *q, const void *k, const void *v, void *o, float
     if (mode == ATTN_MODE_EXACT_BF16)
         return from_hip(attn::launch_prefill_exact(a, s), "prefill launch");
     attn::SageArgs sa{a, workspace, workspace_bytes};
+    if (mode == ATTN_MODE_SAGE3_QK_MXFP4_PV_MXFP4)
+        return from_hip(attn::launch_mxfp4(sa, s), "mxfp4 launch");
     return from_hip(attn::launch_sage(sa, s), "sage launch");
 }
 
@@ -277,8 +284,10 @@ attn_status attn_fwd_varlen(const void *q, const void *k, const void *v, void *o
     if (o_dtype != ATTN_OUT_BF16 && o_dtype != ATTN_OUT_FP32)
         return fail(ATTN_ERR_INVALID_ARG, "unknown output dtype %d", o_dtype);
     if (mode != ATTN_MODE_EXACT_BF16)
-        return fail(mode == ATTN_MODE_SAGE_QK_I8_BLK64_PV_FP8_E4M3 ? ATTN_ERR_UNSUPPORTED
-                                                                   : ATTN_ERR_INVALID_ARG,
+        return fail(mode == ATTN_MODE_SAGE_QK_I8_BLK64_PV_FP8_E4M3 ||
+                            mode == ATTN_MODE_SAGE3_QK_MXFP4_PV_MXFP4
+                        ? ATTN_ERR_UNSUPPORTED
+                        : ATTN_ERR_INVALID_ARG,
                     "the packed variable-length call supports only the exact mode (mode=%d)",
                     mode);
     if (d != 64 && d != 128)

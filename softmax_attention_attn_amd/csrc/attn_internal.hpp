@@ -74,6 +74,8 @@ size_t decode_partial_slots(int B, int Hkv);
 // partials of attn_decode_noalloc (ATTN_DECODE_SCRATCH_BYTES bytes).
 hipError_t decode_scratch(void **ptr);
 hipError_t launch_sage(const SageArgs &a, hipStream_t s);
+hipError_t launch_mxfp4(const SageArgs &a, hipStream_t s);  // the MXFP4 mode (same arguments)
+size_t mxfp4_workspace_bytes(int B, int H, int Hkv, int N, int d);
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t s);
 size_t sage_workspace_bytes(int B, int H, int Hkv, int N, int d);
 // byte offset of each piece of the quantised mode's workspace (attn.h's

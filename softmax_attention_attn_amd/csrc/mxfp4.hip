@@ -1,0 +1,617 @@
+// MXFP4 quantised attention forward for gfx950: SageAttention3's FP4
+// microscaling ("gpu-kernel-porting-with-ai-agents" page, SageAttention 3
+// section: P normalised per token, then FP4 with per-block scales; "GPU
+// kernel overview" page, insights: FP4 attention on CDNA4) on the MX block
+// formats the gfx950 matrix cores take: E2M1 elements with one power-of-two
+// E8M0 scale per block of 32 along the contraction dimension.
+//
+// The recipe:
+//   1. Smooth-K: K' = K - kmean (per channel over all N tokens, fp32);
+//   2. Q and K' to MXFP4 in blocks of 32 consecutive channels of a token, V
+//      in blocks of 32 consecutive tokens of a channel; a block's scale is
+//      2^e with e the smallest exponent such that max|x| <= 6 * 2^e (E2M1's
+//      largest magnitude is 6, so nothing saturates); elements are the
+//      nearest E2M1 value of x / 2^e (ties to even);
+//   3. S = scale * Q^ K^^T on v_mfma_scale_f32_32x32x64_f8f6f4 (FP4 x FP4,
+//      the per-lane scale byte applied in the MFMA);
+//   4. online softmax over 64-key tiles with the exact running max m:
+//      p = 2^(S log2e - m) in (0, 1] (the per-token normalisation), l sums
+//      the unquantised p, and P^ = MXFP4(p) per block of 32 consecutive keys
+//      (v_cvt_scalef32_pk_fp4_f32 with the block's scale);
+//   5. O += P^ V^ on the FP4 MFMA; O / l at the end, lse = m + ln l +
+//      scale * (q . kmean).
+//
+// Kernels: mx_ksum (partial per-channel K sums, fp64) and mx_kmean, mx_quant_qk
+// (Q and K' blocks and q . kmean), mx_quant_v (V blocks, written feature-major
+// through LDS), mx_attn (the fused attention).
+//
+// mx_attn: 8 waves x 32 queries per workgroup; S^T = K^ Q^^T (keys are MFMA
+// rows).  Key rows are fed to the two 32-row MFMA blocks of a tile in the
+// order that leaves lane half g holding keys 32g .. 32g+31 of the tile in its
+// 32 accumulator registers: those are one P block, so a lane quantises its
+// block alone, and its FP4 words are directly the B operand of
+// O^T += V^^T P^^T (lane half g supplies keys 32g .. 32g+31, one block, one
+// scale byte).  K^, V^^T and their scales go global -> LDS through direct
+// loads into two stages, one workgroup barrier per tile.
+#include "../../include/attn.h"
+#include "attn_internal.hpp"
+#include "cdna4.hpp"
+
+namespace attn {
+namespace {
+
+constexpr int kTile = 64;  // keys per tile; token padding of the quantised tensors
+constexpr int kNCh = 16;   // sequence chunks of the K-mean pass
+constexpr int kThreads = 256;
+
+// E8M0 exponent of a block scale from the block's max magnitude (bits of a
+// non-negative float): the smallest e with amax <= 6 * 2^e.  For amax =
+// f * 2^k (f in [1, 2)), 6 * 2^(k-2) = 1.5 * 2^k, so e = k - 2 when f <= 1.5
+// and k - 1 otherwise; zero (and subnormal) maxima clamp into E8M0's range.
+__device__ __forceinline__ int mx_exp(float amax)
+{
+    if (!(amax > 0.f))
+        return 0;
+    const uint32_t b = __float_as_uint(amax);
+    const int k = (int)((b >> 23) & 0xff) - 127;
+    const int e = k - 2 + ((b & 0x7fffff) > 0x400000 ? 1 : 0);
+    return e < -126 ? -126 : (e > 127 ? 127 : e);
+}
+
+// the float 2^e (e in [-126, 127])
+__device__ __forceinline__ float pow2f(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
+
+// Two values to two E2M1 codes in byte `sel` of w: nearest (ties to even)
+// of a / scale and b / scale (scale a power of two), a in the low nibble.
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2(uint32_t w, float a, float b, float scale)
+{
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a, b, scale, SEL);
+}
+
+// 32 values (v[0..31]) to 32 E2M1 codes in four words (element i in nibble
+// i % 8 of word i / 8, low nibble first), with the scale 2^e.
+__device__ __forceinline__ u32x4 fp4x32(const float (&v)[32], int e)
+{
+    const float s = pow2f(e);
+    u32x4 out;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        uint32_t x = 0;
+        x = fp4x2<0>(x, v[8 * w + 0], v[8 * w + 1], s);
+        x = fp4x2<1>(x, v[8 * w + 2], v[8 * w + 3], s);
+        x = fp4x2<2>(x, v[8 * w + 4], v[8 * w + 5], s);
+        x = fp4x2<3>(x, v[8 * w + 6], v[8 * w + 7], s);
+        out[w] = x;
+    }
+    return out;
+}
+
+// FP4 x FP4 32x32x64 MFMA with per-lane E8M0 scale bytes (sa for A's lane
+// block, sb for B's).
+__device__ __forceinline__ f32x16 mfma_fp4(u32x4 a, u32x4 b, f32x16 c, int sa, int sb)
+{
+    const i32x8 av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
+    const i32x8 bv = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 4, 4, 0, sa, 0, sb);
+}
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Workspace pieces (byte-addressed; Npad = N rounded up to kTile).
+struct MxWs {
+    double *ksum_part;  // [BG][kNCh][D]
+    float *kmean;       // [BG][D]
+    float *qkdot;       // [BH][N]
+    uint8_t *qhat;      // [BH][Npad][D/2]   E2M1 pairs, channel 2i in the low nibble
+    uint8_t *qsc;       // [BH][Npad][D/32]  E8M0 scale bytes
+    uint8_t *khat;      // [BG][Npad][D/2]
+    uint8_t *ksc;       // [BG][Npad][D/32]
+    uint8_t *vhatT;     // [BG][D][Npad/2]   feature-major, key 2i in the low nibble
+    uint8_t *vscT;      // [BG][Npad/32][D]  block-major scale bytes
+};
+
+void mx_layout(int B, int H, int Hkv, int N, int d, size_t (&off)[10])
+{
+    const size_t BH = (size_t)B * H, BG = (size_t)B * Hkv;
+    const size_t Npad = (size_t)(N + kTile - 1) / kTile * kTile;
+    const size_t bytes[9] = {sizeof(double) * BG * kNCh * d, sizeof(float) * BG * d,
+                             sizeof(float) * BH * N,       BH * Npad * d / 2,
+                             BH * Npad * d / 32,           BG * Npad * d / 2,
+                             BG * Npad * d / 32,           BG * d * Npad / 2,
+                             BG * Npad / 32 * d};
+    size_t p = 0;
+    for (int i = 0; i < 9; ++i) {
+        off[i] = p;
+        p += align256(bytes[i]);
+    }
+    off[9] = p;
+}
+
+MxWs mx_carve(void *base, int B, int H, int Hkv, int N, int d)
+{
+    size_t off[10];
+    mx_layout(B, H, Hkv, N, d, off);
+    char *p = (char *)base;
+    MxWs w;
+    w.ksum_part = (double *)(p + off[0]);
+    w.kmean = (float *)(p + off[1]);
+    w.qkdot = (float *)(p + off[2]);
+    w.qhat = (uint8_t *)(p + off[3]);
+    w.qsc = (uint8_t *)(p + off[4]);
+    w.khat = (uint8_t *)(p + off[5]);
+    w.ksc = (uint8_t *)(p + off[6]);
+    w.vhatT = (uint8_t *)(p + off[7]);
+    w.vscT = (uint8_t *)(p + off[8]);
+    return w;
+}
+
+// ----------------------------------------------------------------- prologue
+
+// Partial per-channel sums of K over one sequence chunk (fp64).
+template <int D>
+__global__ __launch_bounds__(kThreads) void mx_ksum_kernel(const uint16_t *k, MxWs w, int N)
+{
+    constexpr int TPR = D / 8, RPP = kThreads / TPR;
+    __shared__ double red[RPP][D];
+    const int bg = blockIdx.x, chunk = blockIdx.y, tid = threadIdx.x;
+    const int fc = tid % TPR, rg = tid / TPR;
+    const int len = (N + kNCh - 1) / kNCh;
+    const int r0 = chunk * len, r1 = min(N, r0 + len);
+    const uint16_t *kb = k + (size_t)bg * N * D;
+    double s[8] = {};
+    for (int r = r0 + rg; r < r1; r += RPP) {
+        const u32x4 kw = ld16(kb + (size_t)r * D + fc * 8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            s[2 * e] += bf16_lo(kw[e]);
+            s[2 * e + 1] += bf16_hi(kw[e]);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        red[rg][fc * 8 + e] = s[e];
+    __syncthreads();
+    for (int c = tid; c < D; c += kThreads) {
+        double t = 0.0;
+        for (int r = 0; r < RPP; ++r)
+            t += red[r][c];
+        w.ksum_part[((size_t)bg * kNCh + chunk) * D + c] = t;
+    }
+}
+
+// kmean = sum / N in fp64, rounded to fp32.
+template <int D>
+__global__ __launch_bounds__(D) void mx_kmean_kernel(MxWs w, int N)
+{
+    const int bg = blockIdx.x, c = threadIdx.x;
+    double s = 0.0;
+    for (int i = 0; i < kNCh; ++i)
+        s += w.ksum_part[((size_t)bg * kNCh + i) * D + c];
+    w.kmean[(size_t)bg * D + c] = (float)(s / (double)N);
+}
+
+// One thread per (row, 32-channel block) of Q (rows of BH*Npad) or of
+// K' = K - kmean (rows of BG*Npad); rows past N are zero (codes 0, scale 1).
+// A Q row's four threads also sum q . kmean for the LSE correction.
+template <int D>
+__global__ __launch_bounds__(kThreads) void mx_quant_qk_kernel(const uint16_t *q, const uint16_t *k,
+                                                               MxWs w, int B, int H, int Hkv, int N)
+{
+    constexpr int NB = D / 32;  // blocks per row
+    const int Npad = (N + kTile - 1) / kTile * kTile;
+    const long long t = (long long)blockIdx.x * kThreads + threadIdx.x;
+    const long long nq = (long long)B * H * Npad * NB, nk = (long long)B * Hkv * Npad * NB;
+    if (t >= nq + nk)
+        return;
+    const bool is_q = t < nq;
+    const long long u = is_q ? t : t - nq;
+    const int blk = (int)(u % NB);
+    const long long row = u / NB;  // seq * Npad + tok
+    const int tok = (int)(row % Npad);
+    const long long seq = row / Npad;  // b*H + h or b*Hkv + g
+    const int g = is_q ? (int)((seq / H) * Hkv + (seq % H) / (H / Hkv)) : (int)seq;
+    const float *km = w.kmean + (size_t)g * D + 32 * blk;
+    float x[32];
+    if (tok < N) {
+        const uint16_t *src = (is_q ? q : k) + ((size_t)seq * N + tok) * D + 32 * blk;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const u32x4 v = ld16(src + 8 * j);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x[8 * j + 2 * e] = bf16_lo(v[e]);
+                x[8 * j + 2 * e + 1] = bf16_hi(v[e]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+            x[i] = 0.f;
+    }
+    if (is_q) {
+        float dot = 0.f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+            dot = fmaf(x[i], km[i], dot);
+        // the row's NB threads are consecutive lanes
+#pragma unroll
+        for (int off = 1; off < NB; off <<= 1)
+            dot += __shfl_xor(dot, off, 64);
+        if (blk == 0 && tok < N)
+            w.qkdot[(size_t)seq * N + tok] = dot;
+    } else if (tok < N) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+            x[i] -= km[i];
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+        amax = fmaxf(amax, fabsf(x[i]));
+    const int e = mx_exp(amax);
+    const u32x4 codes = fp4x32(x, e);
+    uint8_t *dst = (is_q ? w.qhat : w.khat) + (size_t)row * (D / 2) + 16 * blk;
+    st16(dst, codes);
+    (is_q ? w.qsc : w.ksc)[(size_t)row * NB + blk] = (uint8_t)(e + 127);
+}
+
+// One 64-key tile of V for one (batch, kv head): thread (c, h) turns the 32
+// keys 32h .. 32h+31 of channel c into one block: 16 bytes of vhatT and its
+// scale byte.  The tile is staged through LDS to read it by channel.
+template <int D>
+__global__ __launch_bounds__(kThreads) void mx_quant_v_kernel(const uint16_t *v, MxWs w, int N)
+{
+    static_assert(2 * D <= kThreads, "one thread per (channel, half tile)");
+    __shared__ float tile[kTile][D + 1];
+    const int Npad = (N + kTile - 1) / kTile * kTile;
+    const int bg = blockIdx.x, tt = blockIdx.y, tid = threadIdx.x;
+    for (int i = tid; i < kTile * D / 8; i += kThreads) {
+        const int r = i / (D / 8), c8 = (i % (D / 8)) * 8;
+        const int tok = tt * kTile + r;
+        u32x4 u = {0, 0, 0, 0};
+        if (tok < N)
+            u = ld16(v + ((size_t)bg * N + tok) * D + c8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            tile[r][c8 + 2 * e] = bf16_lo(u[e]);
+            tile[r][c8 + 2 * e + 1] = bf16_hi(u[e]);
+        }
+    }
+    __syncthreads();
+    if (tid < 2 * D) {
+        const int c = tid % D, h = tid / D;
+        float x[32];
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            x[i] = tile[32 * h + i][c];
+            amax = fmaxf(amax, fabsf(x[i]));
+        }
+        const int e = mx_exp(amax);
+        st16(w.vhatT + ((size_t)bg * D + c) * (Npad / 2) + tt * (kTile / 2) + 16 * h,
+             fp4x32(x, e));
+        w.vscT[((size_t)bg * (Npad / 32) + 2 * tt + h) * D + c] = (uint8_t)(e + 127);
+    }
+}
+
+// ----------------------------------------------------------------- attention
+
+constexpr int kWaves = 8;
+constexpr int kAThreads = 64 * kWaves;
+constexpr int kQW = 32;
+constexpr int kBM = kQW * kWaves;
+
+template <int D>
+struct MCfg {
+    static constexpr int kRow = D / 2;                // bytes of a K^ row
+    static constexpr int kNB = D / 32;                // scale blocks of a K^ row
+    static constexpr int kKBytes = kTile * kRow;      // K^ tile
+    static constexpr int kKScBytes = kTile * kNB;     // its scales
+    static constexpr int kVBytes = D * kTile / 2;     // V^^T tile (feature rows of 32 bytes)
+    static constexpr int kVScBytes = 2 * D;           // its scales (two key blocks of D)
+    // stage: K^ tile | V^^T tile | K^ scales (256 B) | V^ scales (256 B)
+    static constexpr int kKSc = kKBytes + kVBytes, kVSc = kKSc + 256;
+    static constexpr int kStage = kVSc + 256;
+    static constexpr int kKPieces = kKBytes / 1024, kVPieces = kVBytes / 1024;
+    static constexpr int kKH = D / 64;                // QK MFMAs per key block (64 channels each)
+    static_assert(kKScBytes <= 256 && kVScBytes <= 256, "scale pieces");
+    static_assert(kKPieces + kVPieces <= kWaves, "one direct load per wave for the tiles");
+};
+
+// MFMA row rho of key block b reads key 32 ((rho >> 2) & 1) + 16 b +
+// 4 (rho >> 3) + (rho & 3): accumulator register r of lane half g then holds
+// key 32 g + 16 b + r.
+__device__ __forceinline__ int key_of_row(int rho, int b)
+{
+    return 32 * ((rho >> 2) & 1) + 16 * b + 4 * (rho >> 3) + (rho & 3);
+}
+
+// LDS reads of one byte (zero-extended), as asm for the reason given for the
+// other LDS reads (cdna4.hpp): completion is awaited with lgkm_wait.
+__device__ __forceinline__ uint32_t lds_read_u8(uint32_t addr)
+{
+    uint32_t r;
+    asm volatile("ds_read_u8 %0, %1" : "=v"(r) : "v"(addr) : "memory");
+    return r;
+}
+
+// One query tile of one (batch, head).
+template <int D, bool CAUSAL, bool OUT_F32>
+__device__ __forceinline__ void mx_qtile(const PrefillArgs &a, const MxWs &w, unsigned char *smem,
+                                         int bh, int qt, int wave, int lane)
+{
+    using C = MCfg<D>;
+    constexpr int NB = C::kNB, KH = C::kKH, NC = D / 32;
+    const int g = lane >> 5, n = lane & 31;
+    const int N = a.N, Npad = (N + kTile - 1) / kTile * kTile;
+    const int h = bh % a.H, b = bh / a.H;
+    const int bg = b * a.Hkv + h / (a.H / a.Hkv);
+    const int q0 = qt * kBM, qw0 = q0 + wave * kQW, my_q = qw0 + n;
+    const int kend = CAUSAL ? min(N, q0 + kBM) : N;
+    const int ntiles = (kend + kTile - 1) / kTile;
+    // tiles this wave computes (the rest lie above its causal diagonal)
+    const int ntw = CAUSAL ? min(ntiles, (qw0 + kQW - 1) / kTile + 1) : ntiles;
+    const uint8_t *khat = w.khat + (size_t)bg * Npad * C::kRow;
+    const uint8_t *ksc = w.ksc + (size_t)bg * Npad * NB;
+    const uint8_t *vhatT = w.vhatT + (size_t)bg * D * (Npad / 2);
+    const uint8_t *vscT = w.vscT + (size_t)bg * (Npad / 32) * D;
+    auto stage = [&](int t) { return smem + (t & 1) * C::kStage; };
+    // direct loads of tile t: waves 0 .. kKPieces-1 one 1 KB piece of K^
+    // each, the next kVPieces waves one of V^^T each (a tile's feature rows
+    // are 32 bytes, Npad/2 apart), and wave 0 also the scales: lanes 0..15
+    // the K^ scales of the tile's 64 keys, lanes 16..31 its two V^ scale rows
+    // (each contiguous; lane l writes LDS bytes 16 l .. 16 l + 15 of the
+    // scale area)
+    auto load = [&](int t) {
+        if (t >= ntiles)
+            return;
+        unsigned char *st = stage(t);
+        if (wave < C::kKPieces) {
+            dma16_rsrc(raw_rsrc(khat + (size_t)t * C::kKBytes, C::kKBytes),
+                       (uint32_t)(wave * 64 + lane) * 16, st + wave * 1024);
+        } else if (wave < C::kKPieces + C::kVPieces) {
+            const int pc = wave - C::kKPieces, i = pc * 64 + lane;  // 16-byte piece of the tile
+            dma16_rsrc(raw_rsrc(vhatT + (size_t)t * (kTile / 2),
+                                (uint32_t)((D - 1) * (Npad / 2) + kTile / 2)),
+                       (uint32_t)((i >> 1) * (Npad / 2) + (i & 1) * 16), st + C::kKBytes + pc * 1024);
+        }
+        if (wave == 0) {
+            if (lane < 16)
+                dma16_rsrc(raw_rsrc(ksc + (size_t)t * C::kKScBytes, C::kKScBytes), lane * 16,
+                           st + C::kKSc);
+            else if (lane < 32)
+                dma16_rsrc(raw_rsrc(vscT + (size_t)t * C::kVScBytes, C::kVScBytes),
+                           (lane - 16) * 16, st + C::kKSc);
+        }
+    };
+
+    // Q^ fragments (B operand of QK): lane holds query my_q, channels
+    // 64 hh + 32 g .. +31 for each 64-channel half hh, and their scales
+    u32x4 qf[KH];
+    int qs[KH];
+    {
+        const size_t qrow = (size_t)bh * Npad + min(my_q, Npad - 1);
+#pragma unroll
+        for (int hh = 0; hh < KH; ++hh) {
+            qf[hh] = ld16(w.qhat + qrow * C::kRow + (2 * hh + g) * 16);
+            qs[hh] = w.qsc[qrow * NB + 2 * hh + g];
+        }
+    }
+    const float cs = a.scale * kLog2e;
+    f32x16 o[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+        o[c] = f32x16{};
+    float m = -INFINITY, l = 0.f;
+
+    load(0);
+    for (int t = 0; t < ntiles; ++t) {
+        vm_wait_all();
+        __syncthreads();  // tile t is in its stage; every wave is done with tile t-1's
+        load(t + 1);
+        if (t >= ntw)
+            continue;  // above this wave's diagonal: keep the barrier cadence only
+        const uint32_t st = lds_addr(stage(t));
+        // operands: K^ rows of both key blocks, V^^T rows, and their scales
+        u32x4 kf[2][KH], vf[NC];
+        uint32_t ks[2][KH], vs[NC];
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb) {
+            const int key = key_of_row(n, bb);
+#pragma unroll
+            for (int hh = 0; hh < KH; ++hh) {
+                kf[bb][hh] = lds_read_b128<0>(st + key * C::kRow + (2 * hh + g) * 16);
+                ks[bb][hh] = lds_read_u8(st + C::kKSc + key * NB + 2 * hh + g);
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            vf[c] = lds_read_b128<0>(st + C::kKBytes + (32 * c + n) * (kTile / 2) + g * 16);
+            vs[c] = lds_read_u8(st + C::kVSc + g * D + 32 * c + n);
+        }
+        // S^T = K^ Q^^T
+        f32x16 s[2];
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb) {
+            s[bb] = f32x16{};
+#pragma unroll
+            for (int hh = 0; hh < KH; ++hh) {
+                lgkm_wait<0>(kf[bb][hh]);
+                asm volatile("" : "+v"(ks[bb][hh]));
+                s[bb] = mfma_fp4(kf[bb][hh], qf[hh], s[bb], (int)ks[bb][hh], qs[hh]);
+            }
+        }
+        // mask: keys past N, and above the diagonal (register r of block bb
+        // is key 32 g + 16 bb + r of the tile)
+        const int k0 = t * kTile;
+        if ((CAUSAL && k0 + kTile - 1 > qw0) || k0 + kTile > N) {
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = k0 + 32 * g + 16 * bb + r;
+                    if (key >= N || (CAUSAL && key > my_q))
+                        s[bb][r] = -INFINITY;
+                }
+        }
+        // exact running max (log2 units; the scale is positive)
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                tmax = fmaxf(tmax, s[bb][r]);
+        tmax = max_xor32(tmax) * cs;
+        if (__any(tmax > m)) {
+            const float m_new = fmaxf(m, tmax);
+            const float alpha = fast_exp2(m - m_new);
+            l *= alpha;
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+                o[c] *= alpha;
+            m = m_new;
+        }
+        // p for this lane's block (keys 32 g .. 32 g + 31 of the tile), its
+        // row sum, and the block's MXFP4 codes against its own max
+        float p[32];
+        float pmax = 0.f;
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                p[16 * bb + r] = fast_exp2(fmaf(s[bb][r], cs, -m));
+                l += p[16 * bb + r];
+                pmax = fmaxf(pmax, p[16 * bb + r]);
+            }
+        const int pe = mx_exp(pmax);
+        const u32x4 pf = fp4x32(p, pe);
+        // O^T += V^^T P^^T: feature block c, A operand = feature row 32 c + n,
+        // keys 32 g .. +31 of the tile with that block's scale
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            lgkm_wait<0>(vf[c]);
+            asm volatile("" : "+v"(vs[c]));
+            o[c] = mfma_fp4(vf[c], pf, o[c], (int)vs[c], pe + 127);
+        }
+    }
+    // O = O^T / l ; lse = (m + log2 l) ln 2 + scale * q . kmean
+    const float lt = sum_xor32(l);
+    if (my_q < N) {
+        const float inv = 1.f / lt;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                // register 4 j + i holds feature 32 c + 8 j + 4 g + i
+                const int f = 32 * c + 8 * j + 4 * g;
+                if constexpr (OUT_F32) {
+                    float *orow = (float *)a.o + ((size_t)bh * N + my_q) * D;
+                    *(f32x4 *)(orow + f) = f32x4{o[c][4 * j] * inv, o[c][4 * j + 1] * inv,
+                                                 o[c][4 * j + 2] * inv, o[c][4 * j + 3] * inv};
+                } else {
+                    uint16_t *orow = (uint16_t *)a.o + ((size_t)bh * N + my_q) * D;
+                    const u32x2 wv = {pack_bf16x2(o[c][4 * j] * inv, o[c][4 * j + 1] * inv),
+                                      pack_bf16x2(o[c][4 * j + 2] * inv, o[c][4 * j + 3] * inv)};
+                    *(u32x2 *)(orow + f) = wv;
+                }
+            }
+        }
+        if (a.lse && g == 0)
+            a.lse[(size_t)bh * N + my_q] =
+                (m + log2f(lt)) * kLn2 + a.scale * w.qkdot[(size_t)bh * N + my_q];
+    }
+}
+
+template <int D, bool CAUSAL, bool OUT_F32>
+__global__ __launch_bounds__(kAThreads) void mx_attn_kernel(PrefillArgs a, MxWs w)
+{
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * MCfg<D>::kStage];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nqt = (a.N + kBM - 1) / kBM;
+    // causal: workgroup j of a head takes query tiles nqt-1-j and j (equal work)
+    const int nw = CAUSAL ? (nqt + 1) / 2 : nqt;
+    const int BH = a.B * a.H;
+    int bh, j;
+    const int wg = blockIdx.x;
+    if ((BH & 7) == 0) {
+        // workgroup i runs on XCD i % 8: keep a head's workgroups on one XCD
+        const int xcd = wg & 7, slot = wg >> 3;
+        bh = xcd + 8 * (slot / nw);
+        j = slot % nw;
+    } else {
+        bh = wg / nw;
+        j = wg % nw;
+    }
+    if (CAUSAL) {
+        mx_qtile<D, CAUSAL, OUT_F32>(a, w, smem, bh, nqt - 1 - j, wave, lane);
+        if (j < nqt - 1 - j) {
+            __syncthreads();  // every wave is done with the LDS stages
+            mx_qtile<D, CAUSAL, OUT_F32>(a, w, smem, bh, j, wave, lane);
+        }
+    } else {
+        mx_qtile<D, CAUSAL, OUT_F32>(a, w, smem, bh, j, wave, lane);
+    }
+}
+
+template <int D>
+hipError_t launch_d(const SageArgs &sa, hipStream_t s)
+{
+    const PrefillArgs &a = sa.p;
+    const MxWs w = mx_carve(sa.workspace, a.B, a.H, a.Hkv, a.N, D);
+    const int Npad = (a.N + kTile - 1) / kTile * kTile;
+    const int BG = a.B * a.Hkv, BH = a.B * a.H;
+    const uint16_t *q = (const uint16_t *)a.q, *k = (const uint16_t *)a.k,
+                   *v = (const uint16_t *)a.v;
+    {
+        ProfScope ps("mx_ksum", s);
+        hipLaunchKernelGGL(mx_ksum_kernel<D>, dim3(BG, kNCh), dim3(kThreads), 0, s, k, w, a.N);
+    }
+    {
+        ProfScope ps("mx_kmean", s);
+        hipLaunchKernelGGL(mx_kmean_kernel<D>, dim3(BG), dim3(D), 0, s, w, a.N);
+    }
+    {
+        ProfScope ps("mx_quant_qk", s);
+        const long long items = (long long)(BH + BG) * Npad * (D / 32);
+        hipLaunchKernelGGL(mx_quant_qk_kernel<D>, dim3((unsigned)((items + kThreads - 1) / kThreads)),
+                           dim3(kThreads), 0, s, q, k, w, a.B, a.H, a.Hkv, a.N);
+    }
+    {
+        ProfScope ps("mx_quant_v", s);
+        hipLaunchKernelGGL(mx_quant_v_kernel<D>, dim3(BG, Npad / kTile), dim3(kThreads), 0, s, v, w,
+                           a.N);
+    }
+    const int nqt = (a.N + kBM - 1) / kBM;
+    const dim3 grid(BH * (a.causal ? (nqt + 1) / 2 : nqt)), block(kAThreads);
+    ProfScope ps("mx_attn", s);
+    if (a.causal) {
+        if (a.out_fp32)
+            hipLaunchKernelGGL((mx_attn_kernel<D, true, true>), grid, block, 0, s, a, w);
+        else
+            hipLaunchKernelGGL((mx_attn_kernel<D, true, false>), grid, block, 0, s, a, w);
+    } else {
+        if (a.out_fp32)
+            hipLaunchKernelGGL((mx_attn_kernel<D, false, true>), grid, block, 0, s, a, w);
+        else
+            hipLaunchKernelGGL((mx_attn_kernel<D, false, false>), grid, block, 0, s, a, w);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t mxfp4_workspace_bytes(int B, int H, int Hkv, int N, int d)
+{
+    size_t off[10];
+    mx_layout(B, H, Hkv, N, d, off);
+    return off[9];
+}
+
+hipError_t launch_mxfp4(const SageArgs &sa, hipStream_t s)
+{
+    return sa.p.d == 64 ? launch_d<64>(sa, s) : launch_d<128>(sa, s);
+}
+
+}  // namespace attn

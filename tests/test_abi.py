@@ -55,6 +55,17 @@ def test_fwd_validation(A, kw, status):
     assert A.attn_last_error() != ""
 
 
+def test_mxfp4_mode(A):
+    need = A.attn_fwd_workspace_size(1, 4, 2, 100, 128, A.ATTN_MODE_SAGE3_QK_MXFP4_PV_MXFP4)
+    # FP4 Q^, K^, V^^T (half a byte per value) and one scale byte per 32
+    # values, padded to 64 tokens, plus the K-mean partials and q . kmean
+    assert need > (4 + 2 + 2) * 128 * 128 // 2
+    assert _fwd(A, mode=2, N=100, workspace=None, workspace_bytes=0) == -3
+    assert _fwd(A, mode=2, N=100, workspace=P, workspace_bytes=need - 1) == -3
+    assert _fwd(A, mode=2, d=96) == -2
+    assert _dec(A, mode=2) == -2
+
+
 def test_fwd_sage_workspace_required(A):
     need = A.attn_fwd_workspace_size(1, 4, 2, 16, 128, A.ATTN_MODE_SAGE_QK_I8_BLK64_PV_FP8_E4M3)
     if need == 0:
