@@ -108,7 +108,9 @@ attn_status attn_fwd(const void *q, const void *k, const void *v, void *o, float
                      void *stream);
 
 /* Bytes of workspace attn_fwd needs for these sizes and mode (0 for the exact
- * mode).  Returns 0 for invalid sizes as well; attn_fwd then reports the error. */
+ * mode).  Returns 0 as well for sizes attn_fwd rejects (invalid, d other than
+ * 64 or 128, B*H beyond 2^31 - 1 or N beyond 2^24); attn_fwd then reports the
+ * error. */
 size_t attn_fwd_workspace_size(int B, int H, int Hkv, int N, int d, int mode);
 
 /*
@@ -144,8 +146,8 @@ typedef enum {
 } attn_sage_ws_piece;
 
 /* Fills offsets[0 .. ATTN_SAGE_WS_COUNT-1] with the byte offset of each piece
- * for these sizes.  ATTN_ERR_INVALID_ARG for a null offsets or invalid sizes
- * (as attn_fwd_workspace_size). */
+ * for these sizes.  ATTN_ERR_INVALID_ARG for a null offsets or for sizes
+ * attn_fwd rejects (as attn_fwd_workspace_size). */
 attn_status attn_sage_workspace_layout(int B, int H, int Hkv, int N, int d, size_t *offsets);
 
 /*

@@ -19,6 +19,8 @@ import os
 
 import torch  # loaded first so that the library binds to torch's HIP runtime
 
+from . import _abi
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libattn.so")
 
@@ -54,41 +56,7 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError("libattn.so is not built (%s); run __graft_entry__.build() or "
                           "python softmax_attention_attn_amd/_build.py" % LIB_PATH)
-    lib = ctypes.CDLL(LIB_PATH)
-    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
-    lib.attn_fwd.restype = i
-    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, sz, vp]
-    lib.attn_fwd_workspace_size.restype = sz
-    lib.attn_fwd_workspace_size.argtypes = [i, i, i, i, i, i]
-    lib.attn_bwd.restype = i
-    lib.attn_bwd.argtypes = [vp] * 9 + [i, i, i, i, i, i, f, i, vp, sz, vp]
-    lib.attn_bwd_workspace_size.restype = sz
-    lib.attn_bwd_workspace_size.argtypes = [i, i, i]
-    lib.attn_fwd_varlen.restype = i
-    lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, vp]
-    lib.attn_decode.restype = i
-    lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, sz, vp]
-    lib.attn_decode_noalloc.restype = i
-    lib.attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp]
-    lib.attn_decode_workspace_size.restype = sz
-    lib.attn_decode_workspace_size.argtypes = [i, i, i, i]
-    lib.attn_decode_paged.restype = i
-    lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i,
-                                      i, vp, sz, vp]
-    lib.attn_status_string.restype = ctypes.c_char_p
-    lib.attn_status_string.argtypes = [i]
-    lib.attn_last_error.restype = ctypes.c_char_p
-    lib.attn_last_error.argtypes = []
-    lib.attn_profiler_enable.restype = i
-    lib.attn_profiler_enable.argtypes = [i]
-    lib.attn_profiler_read.restype = i
-    lib.attn_profiler_read.argtypes = [ctypes.c_char_p, i, ctypes.POINTER(ctypes.c_double),
-                                       ctypes.POINTER(ctypes.c_int), i]
-    lib.attn_profiler_launches.restype = i
-    lib.attn_profiler_launches.argtypes = [ctypes.c_char_p, i, ctypes.POINTER(ctypes.c_float), i]
-    lib.attn_sage_workspace_layout.restype = i
-    lib.attn_sage_workspace_layout.argtypes = [i, i, i, i, i, ctypes.POINTER(sz)]
-    return lib
+    return _abi.declare(ctypes.CDLL(LIB_PATH))
 
 
 _lib = _load()

@@ -47,6 +47,17 @@ bool valid_scale(float s) { return std::isfinite(s) && s > 0.f; }
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// a * b * c <= limit for non-negative factors, decided without forming a
+// product that could overflow
+bool product_le(long long a, long long b, long long c, long long limit)
+{
+    if (a == 0 || b == 0 || c == 0)
+        return true;
+    if (a > limit / b)
+        return false;
+    return c <= limit / (a * b);
+}
+
 // ---------------------------------------------------------------- profiler
 // Events come from a pool created when the profiler is enabled, so that the
 // timed region itself creates no events; the pool grows only if a run
@@ -157,7 +168,7 @@ attn_status decode_common(const void *q, const void *k_cache, const void *v_cach
                     "query heads per kv head %d (supported: 1, 2, 4, 8, 16)", G);
     // global key offsets (Hkv * sum of lengths) and slot indices stay far
     // inside 64-bit and 32-bit arithmetic
-    if ((long long)B * Hkv * (long long)N_max > (1LL << 40) || (long long)B * H > 0x7fffff00LL ||
+    if (!product_le(B, Hkv, N_max, 1LL << 40) || (long long)B * H > 0x7fffff00LL ||
         (long long)B * Hkv > 0x7fff0000LL)
         return fail(ATTN_ERR_UNSUPPORTED, "problem too large for the work split");
     const size_t need = attn_decode_workspace_size(B, H, Hkv, d);
@@ -202,9 +213,18 @@ const char *attn_status_string(int status)
 
 const char *attn_last_error(void) { return g_last_error.c_str(); }
 
+// Sizes attn_fwd accepts (positive, H a multiple of Hkv, d of 64 or 128, and
+// within the grid mapping's limits); the workspace arithmetic below stays far
+// inside 64 bits for them.
+bool fwd_sizes_supported(int B, int H, int Hkv, int N, int d)
+{
+    return B > 0 && H > 0 && Hkv > 0 && N > 0 && H % Hkv == 0 && (d == 64 || d == 128) &&
+           (long long)B * H <= 0x7fffffffLL && N <= (1 << 24);
+}
+
 size_t attn_fwd_workspace_size(int B, int H, int Hkv, int N, int d, int mode)
 {
-    if (B <= 0 || H <= 0 || Hkv <= 0 || N <= 0 || d <= 0 || H % Hkv != 0)
+    if (!fwd_sizes_supported(B, H, Hkv, N, d))
         return 0;
     if (mode == ATTN_MODE_SAGE_QK_I8_BLK64_PV_FP8_E4M3)
         return attn::sage_workspace_bytes(B, H, Hkv, N, d);
@@ -217,7 +237,7 @@ attn_status attn_sage_workspace_layout(int B, int H, int Hkv, int N, int d, size
 {
     if (!offsets)
         return fail(ATTN_ERR_INVALID_ARG, "offsets must be non-null");
-    if (B <= 0 || H <= 0 || Hkv <= 0 || N <= 0 || d <= 0 || H % Hkv != 0)
+    if (!fwd_sizes_supported(B, H, Hkv, N, d))
         return fail(ATTN_ERR_INVALID_ARG, "invalid sizes (B=%d H=%d Hkv=%d N=%d d=%d)", B, H, Hkv,
                     N, d);
     attn::sage_workspace_layout(B, H, Hkv, N, d, offsets);
@@ -252,7 +272,7 @@ attn_status attn_fwd(const void *q, const void *k, const void *v, void *o, float
                     workspace ? workspace_bytes : (size_t)0);
 
     const long long nqt = ((long long)N + 255) / 256;
-    if ((long long)B * H * nqt > 0x7fffffffLL)
+    if (!product_le(B, H, nqt, 0x7fffffffLL))
         return fail(ATTN_ERR_UNSUPPORTED, "problem too large for the grid mapping");
     attn::PrefillArgs a{q, k, v, o, lse, B, H, Hkv, N, d, causal != 0, scale,
                         o_dtype == ATTN_OUT_FP32};
@@ -295,7 +315,7 @@ attn_status attn_fwd_varlen(const void *q, const void *k, const void *v, void *o
     const long long nqt = ((long long)max_seqlen + 255) / 256;
     // grid of B*H*(query tiles) workgroups; 64 key rows of one tile must stay
     // within the 32-bit offsets of a buffer resource
-    if ((long long)B * H * nqt > 0x7fffffffLL || (long long)H * d > (1 << 20) ||
+    if (!product_le(B, H, nqt, 0x7fffffffLL) || (long long)H * d > (1 << 20) ||
         max_seqlen > (1 << 24))
         return fail(ATTN_ERR_UNSUPPORTED, "problem too large for the grid mapping");
     attn::PrefillArgs a{q, k, v, o, lse, B, H, Hkv, max_seqlen, d, causal != 0, scale,
@@ -332,7 +352,7 @@ attn_status attn_bwd(const void *q, const void *k, const void *v, const void *o,
     if (d != 64 && d != 128)
         return fail(ATTN_ERR_UNSUPPORTED, "head dim d=%d (supported: 64, 128)", d);
     const long long nt = ((long long)N + 127) / 128;
-    if ((long long)B * H * nt > 0x7fffffffLL || (long long)B * H * N > 0x7fffffffLL ||
+    if (!product_le(B, H, nt, 0x7fffffffLL) || !product_le(B, H, N, 0x7fffffffLL) ||
         N > (1 << 24))
         return fail(ATTN_ERR_UNSUPPORTED, "problem too large for the grid mapping");
     const size_t need = attn_bwd_workspace_size(B, H, N);

@@ -199,6 +199,17 @@ __device__ __forceinline__ void store_rows(void *base, size_t row, int g, const 
         }
 }
 
+// The lane index, recomputed where it is used.  The instruction pair is
+// opaque to the compiler, so it neither keeps the value live across a loop
+// nor spills it: a spilled value reloaded inside the dK/dV loop made the
+// scratch load's wait also wait for the tile loads issued just before it.
+__device__ __forceinline__ uint32_t lane_here()
+{
+    uint32_t l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
+
 // Workgroup -> (outer index, tile) with the outer index's tiles kept on one
 // XCD (workgroup i runs on XCD i % 8) when the outer count is a multiple of 8.
 __device__ __forceinline__ void bwd_task(int wg, int ntile, int nouter, int &outer, int &tile)
@@ -288,6 +299,10 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     const int nqt = (N + kRows - 1) / kRows;
     int bh, qt;
     bwd_task(blockIdx.x, nqt, a.B * a.H, bh, qt);
+    // causal: a query tile's work grows with its index, so dispatch the
+    // longest first (the dK/dV kernel's key tiles already shrink with the index)
+    if (CAUSAL)
+        qt = nqt - 1 - qt;
     const int h = bh % a.H, b = bh / a.H, kvh = h / (a.H / a.Hkv);
     const int q0 = qt * kRows, qw0 = q0 + 32 * wave, my_q = qw0 + n;
     const uint16_t *kb = (const uint16_t *)a.k + (size_t)(b * a.Hkv + kvh) * N * D;
@@ -458,19 +473,23 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     const int nqt = (N + kTile - 1) / kTile;
     const int per_head = nqt - t0;
     const int nsteps = G * per_head;
-    const TileLanes<D> tl = tile_lanes<D>(wave, lane);
     auto stage = [&](int i) { return smem + (i & 1) * STAGE; };
     auto load_step = [&](int i) {
         const int hh = b * a.H + g_kv * G + i / per_head;
         const int q0 = (t0 + i % per_head) * kTile;
         unsigned char *st = stage(i);
+        // the lane offsets are recomputed per step (a few VALU instructions)
+        // rather than kept live: spilled, each reload's wait also waited for
+        // the loads issued before it
+        const TileLanes<D> tl = tile_lanes<D>(wave, lane_here());
         load_tile<D>(st, (const uint16_t *)a.q + (size_t)hh * N * D, q0, N, wave, tl);
         load_tile<D>(st + KB, (const uint16_t *)a.dout + (size_t)hh * N * D, q0, N, wave, tl);
         const int rows = min(kTile, N - q0);
         if (wave == 0)
-            dma4_rsrc(raw_rsrc(a.lse2 + (size_t)hh * N + q0, rows * 4), lane * 4, st + 2 * KB);
+            dma4_rsrc(raw_rsrc(a.lse2 + (size_t)hh * N + q0, rows * 4), lane_here() * 4,
+                      st + 2 * KB);
         else if (wave == 1)
-            dma4_rsrc(raw_rsrc(a.delta + (size_t)hh * N + q0, rows * 4), lane * 4,
+            dma4_rsrc(raw_rsrc(a.delta + (size_t)hh * N + q0, rows * 4), lane_here() * 4,
                       st + 2 * KB + kTile * 4);
     };
     if (nsteps > 0)

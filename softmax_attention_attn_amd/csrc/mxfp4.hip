@@ -114,7 +114,7 @@ struct MxWs {
 void mx_layout(int B, int H, int Hkv, int N, int d, size_t (&off)[10])
 {
     const size_t BH = (size_t)B * H, BG = (size_t)B * Hkv;
-    const size_t Npad = (size_t)(N + kTile - 1) / kTile * kTile;
+    const size_t Npad = ((size_t)N + kTile - 1) / kTile * kTile;
     const size_t bytes[9] = {sizeof(double) * BG * kNCh * d, sizeof(float) * BG * d,
                              sizeof(float) * BH * N,       BH * Npad * d / 2,
                              BH * Npad * d / 32,           BG * Npad * d / 2,

@@ -102,7 +102,7 @@ static_assert(ATTN_SAGE_WS_COUNT == kSageWsPieces, "workspace pieces");
 void layout(int B, int H, int Hkv, int N, int d, size_t (&off)[kSageWsPieces + 1])
 {
     const size_t BH = (size_t)B * H, BG = (size_t)B * Hkv;
-    const size_t nblk = (N + kBlk - 1) / kBlk, Npad = nblk * kBlk;
+    const size_t nblk = ((size_t)N + kBlk - 1) / kBlk, Npad = nblk * kBlk;
     const size_t bytes[kSageWsPieces] = {
         sizeof(double) * BG * kNCh * d,  // ATTN_SAGE_WS_KSUM_PART
         sizeof(float) * BG * kNCh * d,   // ATTN_SAGE_WS_VMAX_PART
