@@ -380,18 +380,32 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
                 s[I % 2] = mfma_bf16_32x32x16(as_bf16x8(x), qf[I / 2], s[I % 2]);
                 dp[I % 2] = mfma_bf16_32x32x16(as_bf16x8(y), df[I / 2], dp[I % 2]);
             });
-        // dS^T = P^T (dP^T - D), P^T = 2^(s cs - lse2), masked keys give 0
+        // dS^T = P^T (dP^T - D), P^T = 2^(s cs - lse2).  The mask is tested
+        // only on tiles that reach past N or past the wave's first query: a
+        // masked exponent becomes -inf, so its P and dS are 0.  Queries past
+        // N need no test (their Q, dO, lse2 and D read as zero, and their
+        // lane is not stored); keys past N are masked, as their zero K rows
+        // would meet a P that may overflow.
+        const int tend = (t + 1) * kTile;  // one past the tile's last key
+        const bool any_masked = tend > N || (CAUSAL && tend - 1 > qw0);
         uint32_t dsw[2][8];
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                s[blk][r] = s[blk][r] * cs - lse2;
+            if (any_masked) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = t * kTile + 32 * blk + 8 * (r >> 2) + 4 * g + (r & 3);
+                    const bool ok = key < N && (!CAUSAL || key <= my_q);
+                    s[blk][r] = ok ? s[blk][r] : -INFINITY;
+                }
+            }
             float ds[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = t * kTile + 32 * blk + 8 * (r >> 2) + 4 * g + (r & 3);
-                const bool ok = valid_q && key < N && (!CAUSAL || key <= my_q);
-                const float p = ok ? fast_exp2(s[blk][r] * cs - lse2) : 0.f;
-                ds[r] = p * (dp[blk][r] - dlt);
-            }
+            for (int r = 0; r < 16; ++r)
+                ds[r] = fast_exp2(s[blk][r]) * (dp[blk][r] - dlt);
             pack16(ds, dsw[blk]);
         }
         // dQ^T += K^T dS^T: contraction over the tile's keys, 16 per MFMA
@@ -525,6 +539,13 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
                     s = mfma_bf16_32x32x16(as_bf16x8(x), kf[ks], s);
                     dp = mfma_bf16_32x32x16(as_bf16x8(y), vf[ks], dp);
                 });
+            // P = 2^(s cs - lse2), dS = P (dP - D).  Only the causal mask is
+            // tested, and only on sub-steps with a query before the wave's
+            // last key.  Queries past N need no test: their Q, dO, lse2 and D
+            // rows read as zero, so P = 1 and dP - D = 0 and both products
+            // add nothing.  Keys past N touch only their own (unstored) lane.
+            const int qf = q0 + 32 * qs;  // the sub-step's first query
+            const bool diag = CAUSAL && qf < kw0 + 31;
             float p[16], ds[16];
 #pragma unroll
             for (int R = 0; R < 4; ++R) {
@@ -534,7 +555,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 4 * R + e, q = q0 + r0 + e;
-                    const bool ok = valid_k && q < N && (!CAUSAL || my_k <= q);
+                    const bool ok = !diag || my_k <= q;
                     p[r] = ok ? fast_exp2(s[r] * cs - l4[e]) : 0.f;
                     ds[r] = p[r] * (dp[r] - d4[e]);
                 }
