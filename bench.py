@@ -275,7 +275,8 @@ def bench_varlen(args, stream):
         "H": w.H, "Hkv": w.Hkv, "d": w.d, "causal": w.causal,
         "roofline": roofline("mfma", "prefill_exact_varlen", flops,
                              per_kernel["prefill_exact_varlen"], PEAK_BF16_TFLOPS, "TFLOP/s",
-                             traffic=measured_traffic("prefill_exact_varlen", files)),
+                             traffic=measured_traffic("prefill_exact_varlen", files),
+                             counters=measured_util("prefill_exact_varlen", files)),
     }
 
 
