@@ -25,7 +25,10 @@
 // (Q and K' blocks and q . kmean), mx_quant_v (V blocks, written feature-major
 // through LDS), mx_attn (the fused attention).
 //
-// mx_attn: 8 waves x 32 queries per workgroup; S^T = K^ Q^^T (keys are MFMA
+// mx_attn: 4 waves x 32 queries per workgroup, three workgroups per CU (the
+// kernel is held to 168 registers, three waves per SIMD: the per-score
+// vector work of one wave then hides behind two others; at two waves per
+// SIMD the kernel ran 25% slower); S^T = K^ Q^^T (keys are MFMA
 // rows).  Key rows are fed to the two 32-row MFMA blocks of a tile in the
 // order that leaves lane half g holding keys 32g .. 32g+31 of the tile in its
 // 32 accumulator registers: those are one P block, so a lane quantises its
@@ -297,10 +300,11 @@ __global__ __launch_bounds__(kThreads) void mx_quant_v_kernel(const uint16_t *v,
 
 // ----------------------------------------------------------------- attention
 
-constexpr int kWaves = 8;
+constexpr int kWaves = 4;
 constexpr int kAThreads = 64 * kWaves;
 constexpr int kQW = 32;
 constexpr int kBM = kQW * kWaves;
+constexpr int kStages = 2;  // LDS stages of K^ / V^^T tiles
 
 template <int D>
 struct MCfg {
@@ -315,9 +319,26 @@ struct MCfg {
     static constexpr int kStage = kVSc + 256;
     static constexpr int kKPieces = kKBytes / 1024, kVPieces = kVBytes / 1024;
     static constexpr int kKH = D / 64;                // QK MFMAs per key block (64 channels each)
+    static constexpr int kChunks = kRow / 16;         // 16-byte chunks of a K^ row
+    static constexpr int kPieceLoads = (kKPieces + kVPieces) / kWaves;
+    static_assert((kKPieces + kVPieces) % kWaves == 0, "whole pieces per wave");
     static_assert(kKScBytes <= 256 && kVScBytes <= 256, "scale pieces");
-    static_assert(kKPieces + kVPieces <= kWaves, "one direct load per wave for the tiles");
 };
+
+// K^ tile chunk swizzle: chunk c of key row `key` is stored at chunk
+// c ^ kswz(key).  A QK operand read takes one chunk of 16 rows per 16 lanes,
+// rows that differ in key bits 0-1, 2 and 5 (key_of_row below); with rows of
+// 64 bytes (d = 128) bits 0-1 already select distinct banks and bits 2 and 5
+// move the chunk, with rows of 32 bytes (d = 64) bits 0-2 do and bit 5 moves
+// it, so the 16 reads fall on distinct banks.
+template <int D>
+__device__ __forceinline__ int kswz(int key)
+{
+    if constexpr (D == 128)
+        return ((key >> 2) & 1) | (((key >> 5) & 1) << 1);
+    else
+        return (key >> 5) & 1;
+}
 
 // MFMA row rho of key block b reads key 32 ((rho >> 2) & 1) + 16 b +
 // 4 (rho >> 3) + (rho & 3): accumulator register r of lane half g then holds
@@ -356,25 +377,31 @@ __device__ __forceinline__ void mx_qtile(const PrefillArgs &a, const MxWs &w, un
     const uint8_t *ksc = w.ksc + (size_t)bg * Npad * NB;
     const uint8_t *vhatT = w.vhatT + (size_t)bg * D * (Npad / 2);
     const uint8_t *vscT = w.vscT + (size_t)bg * (Npad / 32) * D;
-    auto stage = [&](int t) { return smem + (t & 1) * C::kStage; };
-    // direct loads of tile t: waves 0 .. kKPieces-1 one 1 KB piece of K^
-    // each, the next kVPieces waves one of V^^T each (a tile's feature rows
-    // are 32 bytes, Npad/2 apart), and wave 0 also the scales: lanes 0..15
-    // the K^ scales of the tile's 64 keys, lanes 16..31 its two V^ scale rows
-    // (each contiguous; lane l writes LDS bytes 16 l .. 16 l + 15 of the
-    // scale area)
+    auto stage = [&](int t) { return smem + (t % kStages) * C::kStage; };
+    // direct loads of tile t: 1 KB piece j of the tile goes to wave j %
+    // kWaves; pieces 0 .. kKPieces-1 are K^ (lane l of piece j fills chunk
+    // l % kChunks of row (64 j + l) / kChunks, with the chunk swizzle), the
+    // next kVPieces are V^^T (a tile's feature rows are 32 bytes, Npad/2
+    // apart); wave 0 also loads the scales: lanes 0..15 the K^ scales of the
+    // tile's 64 keys, lanes 16..31 its two V^ scale rows (each contiguous;
+    // lane l writes LDS bytes 16 l .. 16 l + 15 of the scale area)
     auto load = [&](int t) {
         if (t >= ntiles)
             return;
         unsigned char *st = stage(t);
-        if (wave < C::kKPieces) {
-            dma16_rsrc(raw_rsrc(khat + (size_t)t * C::kKBytes, C::kKBytes),
-                       (uint32_t)(wave * 64 + lane) * 16, st + wave * 1024);
-        } else if (wave < C::kKPieces + C::kVPieces) {
-            const int pc = wave - C::kKPieces, i = pc * 64 + lane;  // 16-byte piece of the tile
-            dma16_rsrc(raw_rsrc(vhatT + (size_t)t * (kTile / 2),
-                                (uint32_t)((D - 1) * (Npad / 2) + kTile / 2)),
-                       (uint32_t)((i >> 1) * (Npad / 2) + (i & 1) * 16), st + C::kKBytes + pc * 1024);
+#pragma unroll
+        for (int u = 0; u < C::kPieceLoads; ++u) {
+            const int pc = wave + kWaves * u;
+            if (pc < C::kKPieces) {
+                const int i = pc * 64 + lane, row = i / C::kChunks, c = i % C::kChunks;
+                dma16_rsrc(raw_rsrc(khat + (size_t)t * C::kKBytes, C::kKBytes),
+                           (uint32_t)(row * C::kRow + ((c ^ kswz<D>(row)) * 16)), st + pc * 1024);
+            } else if (pc < C::kKPieces + C::kVPieces) {
+                const int i = (pc - C::kKPieces) * 64 + lane;  // 16-byte piece of the tile
+                dma16_rsrc(raw_rsrc(vhatT + (size_t)t * (kTile / 2),
+                                    (uint32_t)((D - 1) * (Npad / 2) + kTile / 2)),
+                           (uint32_t)((i >> 1) * (Npad / 2) + (i & 1) * 16), st + pc * 1024);
+            }
         }
         if (wave == 0) {
             if (lane < 16)
@@ -405,6 +432,8 @@ __device__ __forceinline__ void mx_qtile(const PrefillArgs &a, const MxWs &w, un
         o[c] = f32x16{};
     float m = -INFINITY, l = 0.f;
 
+    // two stages, loads one tile ahead (three stages, two tiles ahead,
+    // measured 5% slower)
     load(0);
     for (int t = 0; t < ntiles; ++t) {
         vm_wait_all();
@@ -421,7 +450,8 @@ __device__ __forceinline__ void mx_qtile(const PrefillArgs &a, const MxWs &w, un
             const int key = key_of_row(n, bb);
 #pragma unroll
             for (int hh = 0; hh < KH; ++hh) {
-                kf[bb][hh] = lds_read_b128<0>(st + key * C::kRow + (2 * hh + g) * 16);
+                kf[bb][hh] = lds_read_b128<0>(
+                    st + key * C::kRow + (((2 * hh + g) ^ kswz<D>(key)) * 16));
                 ks[bb][hh] = lds_read_u8(st + C::kKSc + key * NB + 2 * hh + g);
             }
         }
@@ -456,13 +486,13 @@ __device__ __forceinline__ void mx_qtile(const PrefillArgs &a, const MxWs &w, un
                 }
         }
         // exact running max (log2 units; the scale is positive)
-        float tmax = -INFINITY;
+        float smax = -INFINITY;  // this lane's 32 scores: its P block
 #pragma unroll
         for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                tmax = fmaxf(tmax, s[bb][r]);
-        tmax = max_xor32(tmax) * cs;
+                smax = fmaxf(smax, s[bb][r]);
+        const float tmax = max_xor32(smax) * cs;
         if (__any(tmax > m)) {
             const float m_new = fmaxf(m, tmax);
             const float alpha = fast_exp2(m - m_new);
@@ -473,18 +503,18 @@ __device__ __forceinline__ void mx_qtile(const PrefillArgs &a, const MxWs &w, un
             m = m_new;
         }
         // p for this lane's block (keys 32 g .. 32 g + 31 of the tile), its
-        // row sum, and the block's MXFP4 codes against its own max
+        // row sum, and the block's MXFP4 codes against its own max.  The
+        // exponent and the exponential are non-decreasing, so the block's
+        // largest p is the one of its largest score.
         float p[32];
-        float pmax = 0.f;
 #pragma unroll
         for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 p[16 * bb + r] = fast_exp2(fmaf(s[bb][r], cs, -m));
                 l += p[16 * bb + r];
-                pmax = fmaxf(pmax, p[16 * bb + r]);
             }
-        const int pe = mx_exp(pmax);
+        const int pe = mx_exp(fast_exp2(fmaf(smax, cs, -m)));
         const u32x4 pf = fp4x32(p, pe);
         // O^T += V^^T P^^T: feature block c, A operand = feature row 32 c + n,
         // keys 32 g .. +31 of the tile with that block's scale
@@ -524,9 +554,9 @@ __device__ __forceinline__ void mx_qtile(const PrefillArgs &a, const MxWs &w, un
 }
 
 template <int D, bool CAUSAL, bool OUT_F32>
-__global__ __launch_bounds__(kAThreads) void mx_attn_kernel(PrefillArgs a, MxWs w)
+__global__ __launch_bounds__(kAThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void mx_attn_kernel(PrefillArgs a, MxWs w)
 {
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * MCfg<D>::kStage];
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages * MCfg<D>::kStage];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nqt = (a.N + kBM - 1) / kBM;
