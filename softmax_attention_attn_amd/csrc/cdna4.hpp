@@ -78,23 +78,12 @@ __device__ __forceinline__ float add_bf16x2(uint32_t u, float acc)
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
-// v_max3_f32 without the NaN canonicalisation fmaxf requires (scores are
-// never NaN).
-__device__ __forceinline__ float vmax3(float a, float b, float c)
-{
-    float r;
-    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-    return r;
-}
-
 // v_exp_f32: 2^x (exp2(-inf) == 0).
-// max of three signed ints (v_max3_i32)
-__device__ __forceinline__ int vmax3_i32(int a, int b, int c)
-{
-    int r;
-    asm("v_max3_i32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-    return r;
-}
+// max of three signed ints (the compiler forms v_max3_i32).  Written in C,
+// not as inline asm: the compiler cannot see the operands of an asm
+// instruction, so it would not insert the wait states a VALU read of a
+// matrix-core result needs when the max directly follows the MFMA.
+__device__ __forceinline__ int vmax3_i32(int a, int b, int c) { return max(max(a, b), c); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
