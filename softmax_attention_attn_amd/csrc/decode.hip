@@ -268,7 +268,7 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void decode_split_kernel(DecodeAr
             const uint16_t *krow = kcache + row_off(s.b, s.kvh, s.base, key, tab);
 #pragma unroll
             for (int j = 0; j < D / 32; ++j)
-                kr[blk][j] = ld16(krow + 32 * j + 8 * G4);
+                kr[blk][j] = ld16_nt(krow + 32 * j + 8 * G4);
         }
         unsigned char *dst = vst + stage * DCfg<D>::kVBytes;
         constexpr int C = DCfg<D>::kChunks;
@@ -278,7 +278,7 @@ __global__ __launch_bounds__(64 * kWavesPerWG) void decode_split_kernel(DecodeAr
             const int r = p / C;
             const int c = (p % C) ^ dvswz<D>(r);
             const int key = min(max(s.base + r, s.lo), s.hi - 1);
-            dma16(vcache + row_off(s.b, s.kvh, s.base, key, tab) + c * 8, dst + piece * 1024);
+            dma16_nt(vcache + row_off(s.b, s.kvh, s.base, key, tab) + c * 8, dst + piece * 1024);
         }
     };
 
