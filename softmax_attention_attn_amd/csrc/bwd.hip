@@ -262,8 +262,8 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a)
     const long long nrows = (long long)a.B * a.H * a.N;
     float dot = 0.f;
     if (row < nrows) {
-        const u32x4 x = ld16((const uint16_t *)a.dout + row * D + sub * 8);
-        const u32x4 y = ld16((const uint16_t *)a.o + row * D + sub * 8);
+        const u32x4 x = ld16_nt((const uint16_t *)a.dout + row * D + sub * 8);
+        const u32x4 y = ld16_nt((const uint16_t *)a.o + row * D + sub * 8);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             dot += bf16_lo(x[e]) * bf16_lo(y[e]) + bf16_hi(x[e]) * bf16_hi(y[e]);

@@ -164,7 +164,7 @@ __global__ __launch_bounds__(kThreads) void mx_ksum_kernel(const uint16_t *k, Mx
     const uint16_t *kb = k + (size_t)bg * N * D;
     double s[8] = {};
     for (int r = r0 + rg; r < r1; r += RPP) {
-        const u32x4 kw = ld16(kb + (size_t)r * D + fc * 8);
+        const u32x4 kw = ld16_nt(kb + (size_t)r * D + fc * 8);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             s[2 * e] += bf16_lo(kw[e]);
@@ -274,7 +274,7 @@ __global__ __launch_bounds__(kThreads) void mx_quant_v_kernel(const uint16_t *v,
         const int tok = tt * kTile + r;
         u32x4 u = {0, 0, 0, 0};
         if (tok < N)
-            u = ld16(v + ((size_t)bg * N + tok) * D + c8);
+            u = ld16_nt(v + ((size_t)bg * N + tok) * D + c8);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             tile[r][c8 + 2 * e] = bf16_lo(u[e]);

@@ -163,8 +163,8 @@ __global__ __launch_bounds__(kThreads) void sage_stats_kernel(const uint16_t *k,
     double ks[8] = {};
     float vm[8] = {};
     for (int r = r0 + rg; r < r1; r += RPP) {
-        const u32x4 kw = ld16(kb + (size_t)r * D + fc * 8);
-        const u32x4 vw = ld16(vb + (size_t)r * D + fc * 8);
+        const u32x4 kw = ld16_nt(kb + (size_t)r * D + fc * 8);
+        const u32x4 vw = ld16_nt(vb + (size_t)r * D + fc * 8);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             ks[2 * e] += bf16_lo(kw[e]);
