@@ -291,7 +291,8 @@ attn_status attn_decode_paged(const void *q, const void *k_pages, const void *v_
  *   dq         device [B, H, N, d];  dk, dv  device [B, Hkv, N, d]; all of
  *              dtype grad_dtype (attn_dtype).
  *   workspace  at least attn_bwd_workspace_size() bytes (fp32 D and
- *              lse*log2(e) per row); overwritten.
+ *              lse*log2(e) per row, each head's rows padded to a multiple
+ *              of 64); overwritten.
  * Errors: as attn_fwd (d in {64, 128}); null lse or any null tensor is
  * ATTN_ERR_INVALID_ARG; a missing or short workspace ATTN_ERR_WORKSPACE.
  */

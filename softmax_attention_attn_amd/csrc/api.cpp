@@ -329,7 +329,7 @@ size_t attn_bwd_workspace_size(int B, int H, int N)
 {
     if (B <= 0 || H <= 0 || N <= 0)
         return 0;
-    return 2 * align_up(sizeof(float) * (size_t)B * H * N, 256);
+    return 2 * align_up(sizeof(float) * (size_t)B * H * attn::bwd_rows(N), 256);
 }
 
 attn_status attn_bwd(const void *q, const void *k, const void *v, const void *o,
@@ -378,7 +378,8 @@ attn_status attn_bwd(const void *q, const void *k, const void *v, const void *o,
     a.scale = scale;
     a.out_fp32 = grad_dtype == ATTN_OUT_FP32;
     a.delta = (float *)workspace;
-    a.lse2 = (float *)((char *)workspace + align_up(sizeof(float) * (size_t)B * H * N, 256));
+    a.lse2 = (float *)((char *)workspace +
+                       align_up(sizeof(float) * (size_t)B * H * attn::bwd_rows(N), 256));
     return from_hip(attn::launch_bwd(a, (hipStream_t)stream), "backward launch");
 }
 

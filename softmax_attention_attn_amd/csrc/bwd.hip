@@ -69,8 +69,9 @@ struct TileLanes {
 };
 
 // slot 64p + l of the tile is row q / (C + pad), physical chunk q % (C + pad);
-// a pad chunk re-reads chunk 0, a swizzled row's physical chunk c holds
-// logical chunk c ^ swz(row)
+// a swizzled row's physical chunk c holds logical chunk c ^ swz(row).  Pad
+// chunks are not loaded (offset kPadSlot): they stay free for other data.
+constexpr uint32_t kPadSlot = 0xffffffffu;
 template <int D, bool SWZ = false>
 __device__ __forceinline__ TileLanes<D, SWZ> tile_lanes(int wave, int lane)
 {
@@ -80,8 +81,7 @@ __device__ __forceinline__ TileLanes<D, SWZ> tile_lanes(int wave, int lane)
     for (int i = 0; i < BCfg<D, SWZ>::kPerWave; ++i) {
         const int q = (wave + kBWaves * i) * 64 + lane;
         const int row = q / W, c = q % W;
-        const int logical = c >= C ? 0 : SWZ ? c ^ swz(row) : c;
-        t.off[i] = row * (D * 2) + logical * 16;
+        t.off[i] = c >= C ? kPadSlot : row * (D * 2) + (SWZ ? c ^ swz(row) : c) * 16;
     }
     return t;
 }
@@ -95,7 +95,7 @@ __device__ __forceinline__ void load_tile(unsigned char *lds, const uint16_t *sr
 #pragma unroll
     for (int i = 0; i < BCfg<D, SWZ>::kPerWave; ++i) {
         const int piece = wave + kBWaves * i;
-        if (piece < BCfg<D, SWZ>::kPieces)
+        if (piece < BCfg<D, SWZ>::kPieces && tl.off[i] != kPadSlot)
             dma16_rsrc(r, tl.off[i], lds + piece * 1024);
     }
 }
@@ -252,16 +252,24 @@ __device__ __forceinline__ void operand_stream(Rd &&rd, Use &&use)
 
 // ---------------------------------------------------------------- D, lse2
 // One 16-lane group per row: D = dO . O (fp32), lse2 = lse * log2(e).
+// The arrays hold bwd_rows(N) rows per head; the rows past N get 0, so a
+// whole 64-row tile of them can be loaded and, with the zero Q and dO rows
+// the tile loads read past N, adds nothing to any product.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a)
 {
     constexpr int LPR = D / 8;  // lanes per row (16 bytes each)
     const int rows_per_block = 256 / LPR;
-    const long long row = (long long)blockIdx.x * rows_per_block + threadIdx.x / LPR;
+    const int NP = bwd_rows(a.N);
+    const long long prow = (long long)blockIdx.x * rows_per_block + threadIdx.x / LPR;
+    const long long bh = prow / NP;
+    const int qi = (int)(prow - bh * NP);
+    const long long row = bh * a.N + qi;  // the row in the [B,H,N] tensors
     const int sub = threadIdx.x % LPR;
-    const long long nrows = (long long)a.B * a.H * a.N;
+    const long long nprows = (long long)a.B * a.H * NP;
+    const bool real = prow < nprows && qi < a.N;
     float dot = 0.f;
-    if (row < nrows) {
+    if (real) {
         const u32x4 x = ld16_nt((const uint16_t *)a.dout + row * D + sub * 8);
         const u32x4 y = ld16_nt((const uint16_t *)a.o + row * D + sub * 8);
 #pragma unroll
@@ -271,9 +279,9 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a)
 #pragma unroll
     for (int off = LPR / 2; off > 0; off >>= 1)
         dot += __shfl_xor(dot, off, LPR);
-    if (row < nrows && sub == 0) {
-        a.delta[row] = dot;
-        a.lse2[row] = a.lse[row] * kLog2e;
+    if (prow < nprows && sub == 0) {
+        a.delta[prow] = dot;
+        a.lse2[prow] = real ? a.lse[row] * kLog2e : 0.f;
     }
 }
 
@@ -334,8 +342,9 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         df[ks] = as_bf16x8(valid_q ? ld16((const uint16_t *)a.dout + qrow * D + 16 * ks + 8 * g)
                                    : u32x4{0, 0, 0, 0});
     }
-    const float lse2 = valid_q ? a.lse2[qrow] : 0.f;
-    const float dlt = valid_q ? a.delta[qrow] : 0.f;
+    const size_t prow = (size_t)bh * bwd_rows(N) + my_q;  // row in the padded arrays
+    const float lse2 = valid_q ? a.lse2[prow] : 0.f;
+    const float dlt = valid_q ? a.delta[prow] : 0.f;
     const float cs = a.scale * kLog2e;
 
     f32x16 acc[NC];
@@ -441,20 +450,26 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 // Workgroup: 128 keys of one (b, kv head); wave w owns keys k0 + 32w .. +31
 // (lane n is key k0 + 32w + n).  For each query head of the group, query
 // tiles of 64 (with their lse2 and D rows) stream through a 2-stage LDS ring.
-// Two waves per SIMD (two workgroups per CU; 70 KB of LDS each): the
-// register budget of 256 then holds the dK/dV accumulators (128), the K/V
-// fragments (64) and one product of operand read-ahead, with a few values
-// spilled outside the inner loop; the second wave hides the LDS latency and
+// Two waves per SIMD (two workgroups per CU): the register budget of 256
+// then holds the dK/dV accumulators (128), the K/V fragments (64) and one
+// product of operand read-ahead; the second wave hides the LDS latency and
 // the score arithmetic, which the read-ahead of a single wave did not.
+// d = 128: the Q and dO tiles use the swizzled layout (rows of 320 bytes; the
+// row reads of S and dP and the transposing reads of dV and dK fall on
+// distinct banks), two stages fill 80 KB, so the tile's lse2 and D go into
+// the row padding: pad chunks 0 and 1 of row j hold lse2 and D of rows
+// 4j .. 4j+3.  d = 64: padded rows and a separate lse2 / D area.
 template <int D, bool CAUSAL, bool OUT_F32>
 __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkv_kernel(BwdArgs a)
 {
-    constexpr int KB = BCfg<D>::kBytes, KS = D / 16, NC = D / 32;
-    constexpr int STAGE = 2 * KB + 2 * kTile * 4;  // Q, dO, lse2, D
+    constexpr bool SW = D == 128;
+    using Cf = BCfg<D, SW>;
+    constexpr int KB = Cf::kBytes, KS = D / 16, NC = D / 32;
+    constexpr int STAGE = 2 * KB + (SW ? 0 : 2 * kTile * 4);  // Q, dO (, lse2, D)
     __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
     const int lane = threadIdx.x & 63, g = lane >> 5, n = lane & 31;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int N = a.N;
+    const int N = a.N, NP = bwd_rows(N);
     const int G = a.H / a.Hkv;
     const int nkt = (N + kRows - 1) / kRows;
     int bg, kt;
@@ -492,19 +507,51 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         const int hh = b * a.H + g_kv * G + i / per_head;
         const int q0 = (t0 + i % per_head) * kTile;
         unsigned char *st = stage(i);
-        // the lane offsets are recomputed per step (a few VALU instructions)
-        // rather than kept live: spilled, each reload's wait also waited for
-        // the loads issued before it
-        const TileLanes<D> tl = tile_lanes<D>(wave, lane_here());
-        load_tile<D>(st, (const uint16_t *)a.q + (size_t)hh * N * D, q0, N, wave, tl);
-        load_tile<D>(st + KB, (const uint16_t *)a.dout + (size_t)hh * N * D, q0, N, wave, tl);
-        const int rows = min(kTile, N - q0);
-        if (wave == 0)
-            dma4_rsrc(raw_rsrc(a.lse2 + (size_t)hh * N + q0, rows * 4), lane_here() * 4,
-                      st + 2 * KB);
-        else if (wave == 1)
-            dma4_rsrc(raw_rsrc(a.delta + (size_t)hh * N + q0, rows * 4), lane_here() * 4,
-                      st + 2 * KB + kTile * 4);
+        // the lane offsets are recomputed per piece from the lane index
+        // (lane_here: opaque, so the compiler neither keeps them live across
+        // the loop nor spills them; a spilled offset's reload would also wait
+        // for the loads issued before it)
+        const __amdgpu_buffer_rsrc_t rq =
+            raw_rsrc((const uint16_t *)a.q + ((size_t)hh * N + q0) * D,
+                     (uint32_t)min(kTile, N - q0) * D * 2);
+        const __amdgpu_buffer_rsrc_t rd =
+            raw_rsrc((const uint16_t *)a.dout + ((size_t)hh * N + q0) * D,
+                     (uint32_t)min(kTile, N - q0) * D * 2);
+#pragma unroll
+        for (int u = 0; u < Cf::kPerWave; ++u) {
+            constexpr int C = Cf::kChunks, W = C + Cf::kPad;
+            const int piece = wave + kBWaves * u;
+            if (piece < Cf::kPieces) {
+                const int q = piece * 64 + (int)lane_here();
+                const int row = q / W, c = q % W;
+                if (c < C) {  // pad chunks are not loaded
+                    const uint32_t off = row * (D * 2) + (SW ? c ^ swz(row) : c) * 16;
+                    dma16_rsrc(rq, off, st + piece * 1024);
+                    dma16_rsrc(rd, off, st + KB + piece * 1024);
+                }
+            }
+        }
+        const float *lsrc = a.lse2 + (size_t)hh * NP + q0, *dsrc = a.delta + (size_t)hh * NP + q0;
+        if constexpr (SW) {
+            // wave w fills the pads of rows 4w .. 4w+3: lane 20i + c writes
+            // pad chunk c of row 4w + i (rows are 20 chunks apart), 16 bytes
+            // of lse2 (c = 0) or D (c = 1) of rows 4(4w+i) .. +3; the other
+            // lanes are off
+            const int l = (int)lane_here(), li = l / 20, c = l - 20 * li;
+            const uint32_t off = 16 * (4 * wave + li);
+            unsigned char *pad = st + 4 * wave * Cf::kPitch + 2 * D;
+            if (li < 4 && c == 0)
+                dma16_rsrc(raw_rsrc(lsrc, kTile * 4), off, pad);
+            if (li < 4 && c == 1)
+                dma16_rsrc(raw_rsrc(dsrc, kTile * 4), off, pad);
+        } else {
+            const int rows = min(kTile, N - q0);
+            const int l = (int)lane_here();
+            if (wave == 0)
+                dma4_rsrc(raw_rsrc(lsrc, rows * 4), l * 4, st + 2 * KB);
+            else if (wave == 1)
+                dma4_rsrc(raw_rsrc(dsrc, rows * 4), l * 4, st + 2 * KB + kTile * 4);
+        }
     };
     if (nsteps > 0)
         load_step(0);
@@ -516,9 +563,6 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         const int q0 = (t0 + i % per_head) * kTile;
         unsigned char *st = stage(i);
         const uint32_t qa = lds_addr(st), da = lds_addr(st + KB);
-        const float *lse_s = (const float *)(st + 2 * KB);
-        const float *dl_s = lse_s + kTile;
-        const uint32_t qt_a = trans_addr<D>(qa, lane), dt_a = trans_addr<D>(da, lane);
         static_for<0, 2>([&](auto qc) {
             constexpr int qs = decltype(qc)::value;  // queries q0 + 32 qs .. +31
             // causal: skip when every query of the step precedes every key of the wave
@@ -526,13 +570,28 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
                 return;
             // S = Q K^T and dP = dO V^T: rows = queries 32 qs + 8(r/4) + 4g + r%4
             f32x16 s = f32x16{}, dp = f32x16{};
-            const uint32_t qd = direct_addr<D>(qa, 32 * qs, lane);
-            const uint32_t dd = direct_addr<D>(da, 32 * qs, lane);
+            // the lane parts of the swizzled addresses are recomputed here
+            // from the lane index (lane_here), not kept live across the loop:
+            // at the 256-register bound they spilled
+            const int lh = SW ? (int)lane_here() : lane;
+            const uint32_t lrow0 = SW ? swz_row_addr<0>(0, lh) : 0;
+            const uint32_t lrow1 = SW ? swz_row_addr<1>(0, lh) : 0;
+            const uint32_t qd = SW ? qa : direct_addr<D>(qa, 32 * qs, lane);
+            const uint32_t dd = SW ? da : direct_addr<D>(da, 32 * qs, lane);
             operand_stream<KS, 1, 2>(
                 [&](auto i, u32x4 &x, u32x4 &y) {
                     constexpr int ks = decltype(i)::value;
-                    x = lds_read_b128<32 * ks>(qd);
-                    y = lds_read_b128<32 * ks>(dd);
+                    if constexpr (SW) {
+                        // logical chunk 2ks + g of row 32qs + n: the lane part
+                        // for the parity of ks, 64 (ks / 2) bytes in the offset
+                        constexpr int off = 32 * qs * Cf::kPitch + 64 * (ks / 2);
+                        const uint32_t lr = (ks & 1) ? lrow1 : lrow0;
+                        x = lds_read_b128<off>(qd + lr);
+                        y = lds_read_b128<off>(dd + lr);
+                    } else {
+                        x = lds_read_b128<32 * ks>(qd);
+                        y = lds_read_b128<32 * ks>(dd);
+                    }
                 },
                 [&](auto i, const u32x4 &x, const u32x4 &y) {
                     constexpr int ks = decltype(i)::value;
@@ -549,9 +608,17 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
             float p[16], ds[16];
 #pragma unroll
             for (int R = 0; R < 4; ++R) {
-                const int r0 = 32 * qs + 8 * R + 4 * g;
-                const f32x4 l4 = *(const f32x4 *)(lse_s + r0);
-                const f32x4 d4 = *(const f32x4 *)(dl_s + r0);
+                const int r0 = 32 * qs + 8 * R + 4 * g;  // rows r0 .. r0+3 of the tile
+                f32x4 l4, d4;
+                if constexpr (SW) {
+                    const unsigned char *pad = st + (r0 / 4) * Cf::kPitch + 2 * D;
+                    l4 = *(const f32x4 *)pad;
+                    d4 = *(const f32x4 *)(pad + 16);
+                } else {
+                    const float *lse_s = (const float *)(st + 2 * KB);
+                    l4 = *(const f32x4 *)(lse_s + r0);
+                    d4 = *(const f32x4 *)(lse_s + kTile + r0);
+                }
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 4 * R + e, q = q0 + r0 + e;
@@ -566,11 +633,22 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
             // dV^T += dO^T P and dK^T += Q^T dS: contraction over the step's queries
             // product pair i: queries 16u .. 16u+15 of the step (u = i / NC),
             // feature block c = i % NC (consecutive pairs use different blocks)
+            const int lt = SW ? (int)lane_here() : lane;
+            const uint32_t ltr0 = SW ? swz_trans_addr<0>(0, lt) : 0;
+            const uint32_t ltr8 = SW ? swz_trans_addr<8>(0, lt) : 0;
+            const uint32_t qt_a = SW ? qa + ltr0 : trans_addr<D>(qa, lane);
+            const uint32_t dt_a = SW ? da + ltr0 : trans_addr<D>(da, lane);
+            const uint32_t qt8 = qa + ltr8, dt8 = da + ltr8;
             operand_stream<2 * NC, 1, 4>(
                 [&](auto i, u32x4 &x, u32x4 &y) {
                     constexpr int I = decltype(i)::value, c = I % NC, u = I / NC;
-                    x = trans_read<D, 32 * qs + 16 * u, c>(dt_a);
-                    y = trans_read<D, 32 * qs + 16 * u, c>(qt_a);
+                    if constexpr (SW) {
+                        x = swz_trans_read<32 * qs + 16 * u, c>(dt_a, dt8);
+                        y = swz_trans_read<32 * qs + 16 * u, c>(qt_a, qt8);
+                    } else {
+                        x = trans_read<D, 32 * qs + 16 * u, c>(dt_a);
+                        y = trans_read<D, 32 * qs + 16 * u, c>(qt_a);
+                    }
                 },
                 [&](auto i, const u32x4 &x, const u32x4 &y) {
                     constexpr int I = decltype(i)::value, c = I % NC, u = I / NC;
@@ -593,7 +671,7 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s)
 {
     {
         constexpr int rows_per_block = 256 / (D / 8);
-        const long long nrows = (long long)a.B * a.H * a.N;
+        const long long nrows = (long long)a.B * a.H * bwd_rows(a.N);
         ProfScope ps("bwd_delta", s);
         hipLaunchKernelGGL((bwd_delta_kernel<D>),
                            dim3((unsigned)((nrows + rows_per_block - 1) / rows_per_block)),

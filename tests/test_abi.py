@@ -112,7 +112,9 @@ def test_bwd_validation(A, kw, status):
 
 
 def test_bwd_workspace_size(A):
-    assert A.attn_bwd_workspace_size(2, 4, 100) == 2 * (((4 * 2 * 4 * 100) + 255) // 256 * 256)
+    # fp32 D and lse*log2(e) per row, each head's rows padded to a multiple of 64
+    assert A.attn_bwd_workspace_size(2, 4, 100) == 2 * (((4 * 2 * 4 * 128) + 255) // 256 * 256)
+    assert A.attn_bwd_workspace_size(1, 1, 64) == 2 * 256
     assert A.attn_bwd_workspace_size(0, 4, 100) == 0
 
 
