@@ -301,7 +301,8 @@ attn_status attn_bwd(const void *q, const void *k, const void *v, const void *o,
                      int H, int Hkv, int N, int d, int causal, float scale, int grad_dtype,
                      void *workspace, size_t workspace_bytes, void *stream);
 
-/* Bytes of workspace attn_bwd needs (0 for invalid sizes). */
+/* Bytes of workspace attn_bwd needs (0 for invalid sizes and for sizes
+ * attn_bwd rejects: N beyond 2^24 or B*H*N beyond 2^31 - 1). */
 size_t attn_bwd_workspace_size(int B, int H, int N);
 
 /* Static description of a status code. */

@@ -327,7 +327,8 @@ attn_status attn_fwd_varlen(const void *q, const void *k, const void *v, void *o
 
 size_t attn_bwd_workspace_size(int B, int H, int N)
 {
-    if (B <= 0 || H <= 0 || N <= 0)
+    // 0 as well beyond the sizes attn_bwd accepts
+    if (B <= 0 || H <= 0 || N <= 0 || N > (1 << 24) || !product_le(B, H, N, 0x7fffffffLL))
         return 0;
     return 2 * align_up(sizeof(float) * (size_t)B * H * attn::bwd_rows(N), 256);
 }
