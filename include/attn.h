@@ -290,11 +290,14 @@ attn_status attn_decode_paged(const void *q, const void *k_pages, const void *v_
  *   lse        device fp32 [B, H, N] as written by attn_fwd (natural log).
  *   dq         device [B, H, N, d];  dk, dv  device [B, Hkv, N, d]; all of
  *              dtype grad_dtype (attn_dtype).
- *   workspace  at least attn_bwd_workspace_size() bytes (fp32 D and
- *              lse*log2(e) per row, each head's rows padded to a multiple
+ *   workspace  at least attn_bwd_workspace_size() bytes (fp32 -D and
+ *              -lse/scale per row, each head's rows padded to a multiple
  *              of 64); overwritten.
- * Errors: as attn_fwd (d in {64, 128}); null lse or any null tensor is
- * ATTN_ERR_INVALID_ARG; a missing or short workspace ATTN_ERR_WORKSPACE.
+ *   scale      as attn_fwd, and at least 2^-64 (so that lse/scale stays
+ *              finite).
+ * Errors: as attn_fwd (d in {64, 128}); null lse, any null tensor or a scale
+ * below 2^-64 is ATTN_ERR_INVALID_ARG; a missing or short workspace
+ * ATTN_ERR_WORKSPACE.
  */
 attn_status attn_bwd(const void *q, const void *k, const void *v, const void *o,
                      const float *lse, const void *dout, void *dq, void *dk, void *dv, int B,

@@ -348,6 +348,10 @@ attn_status attn_bwd(const void *q, const void *k, const void *v, const void *o,
         return fail(ATTN_ERR_INVALID_ARG, "H=%d is not a multiple of Hkv=%d", H, Hkv);
     if (!valid_scale(scale))
         return fail(ATTN_ERR_INVALID_ARG, "scale must be finite and > 0");
+    // the kernels work with -lse/scale, which must stay finite
+    if (scale < 0x1p-64f)
+        return fail(ATTN_ERR_INVALID_ARG, "the backward needs scale >= 2^-64 (got %g)",
+                    (double)scale);
     if (grad_dtype != ATTN_OUT_BF16 && grad_dtype != ATTN_OUT_FP32)
         return fail(ATTN_ERR_INVALID_ARG, "unknown gradient dtype %d", grad_dtype);
     if (d != 64 && d != 128)
@@ -378,8 +382,8 @@ attn_status attn_bwd(const void *q, const void *k, const void *v, const void *o,
     a.causal = causal != 0;
     a.scale = scale;
     a.out_fp32 = grad_dtype == ATTN_OUT_FP32;
-    a.delta = (float *)workspace;
-    a.lse2 = (float *)((char *)workspace +
+    a.ndelta = (float *)workspace;
+    a.nlse = (float *)((char *)workspace +
                        align_up(sizeof(float) * (size_t)B * H * attn::bwd_rows(N), 256));
     return from_hip(attn::launch_bwd(a, (hipStream_t)stream), "backward launch");
 }

@@ -52,11 +52,11 @@ struct BwdArgs {
     int causal;
     float scale;
     int out_fp32;  // gradients in fp32 (1) or bf16 (0)
-    float *delta;  // workspace [B,H,bwd_rows(N)]: dO . O per row, 0 past N
-    float *lse2;   // workspace [B,H,bwd_rows(N)]: lse * log2(e), 0 past N
+    float *ndelta;  // workspace [B,H,bwd_rows(N)]: -(dO . O) per row, 0 past N
+    float *nlse;    // workspace [B,H,bwd_rows(N)]: -lse / scale per row, 0 past N
 };
 
-// Rows per head of the backward's D and lse*log2(e) arrays: N rounded up to
+// Rows per head of the backward's -D and -lse/scale arrays: N rounded up to
 // the 64-row tiles the dK/dV kernel loads whole (the rows past N hold 0).
 constexpr int kBwdRowPad = 64;
 __host__ __device__ inline int bwd_rows(int N) { return (N + kBwdRowPad - 1) / kBwdRowPad * kBwdRowPad; }

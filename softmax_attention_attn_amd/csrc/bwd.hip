@@ -11,7 +11,7 @@
 //
 // Three kernels, no atomics (every output element has one writer, so the
 // result is deterministic):
-//  * bwd_delta: D_i = dO_i . O_i in fp32, and lse_i * log2(e), per row.
+//  * bwd_delta: -D_i = -(dO_i . O_i) in fp32, and -lse_i / s, per row.
 //  * bwd_dq: query-stationary.  A workgroup owns 128 queries (4 waves x 32)
 //    of one head, keeps their Q and dO in registers and streams the K/V
 //    tiles (64 keys) through LDS: S^T = K Q^T and dP^T = V dO^T on the MFMA,
@@ -250,8 +250,11 @@ __device__ __forceinline__ void operand_stream(Rd &&rd, Use &&use)
     });
 }
 
-// ---------------------------------------------------------------- D, lse2
-// One 16-lane group per row: D = dO . O (fp32), lse2 = lse * log2(e).
+// ---------------------------------------------------------------- -D, -lse/s
+// One 16-lane group per row: -D = -(dO . O) (fp32) and -lse / s.  These are
+// the values the dK/dV kernel starts its dP and S accumulators from, so the
+// products deliver dP - D and S - lse/s (the exponent over s log2(e)) with
+// no further per-score subtraction.
 // The arrays hold bwd_rows(N) rows per head; the rows past N get 0, so a
 // whole 64-row tile of them can be loaded and, with the zero Q and dO rows
 // the tile loads read past N, adds nothing to any product.
@@ -280,8 +283,8 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a)
     for (int off = LPR / 2; off > 0; off >>= 1)
         dot += __shfl_xor(dot, off, LPR);
     if (prow < nprows && sub == 0) {
-        a.delta[prow] = dot;
-        a.lse2[prow] = real ? a.lse[row] * kLog2e : 0.f;
+        a.ndelta[prow] = -dot;
+        a.nlse[prow] = real ? -a.lse[row] / a.scale : 0.f;
     }
 }
 
@@ -343,9 +346,9 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
                                    : u32x4{0, 0, 0, 0});
     }
     const size_t prow = (size_t)bh * bwd_rows(N) + my_q;  // row in the padded arrays
-    const float lse2 = valid_q ? a.lse2[prow] : 0.f;
-    const float dlt = valid_q ? a.delta[prow] : 0.f;
     const float cs = a.scale * kLog2e;
+    const float lse2 = valid_q ? -a.nlse[prow] * cs : 0.f;  // lse log2(e)
+    const float dlt = valid_q ? -a.ndelta[prow] : 0.f;
 
     f32x16 acc[NC];
 #pragma unroll
@@ -449,23 +452,26 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 // ---------------------------------------------------------------- dK, dV
 // Workgroup: 128 keys of one (b, kv head); wave w owns keys k0 + 32w .. +31
 // (lane n is key k0 + 32w + n).  For each query head of the group, query
-// tiles of 64 (with their lse2 and D rows) stream through a 2-stage LDS ring.
+// tiles of 64 (with their -lse/s and -D rows) stream through a 2-stage LDS ring.
 // Two waves per SIMD (two workgroups per CU): the register budget of 256
 // then holds the dK/dV accumulators (128), the K/V fragments (64) and one
 // product of operand read-ahead; the second wave hides the LDS latency and
 // the score arithmetic, which the read-ahead of a single wave did not.
 // d = 128: the Q and dO tiles use the swizzled layout (rows of 320 bytes; the
 // row reads of S and dP and the transposing reads of dV and dK fall on
-// distinct banks), two stages fill 80 KB, so the tile's lse2 and D go into
-// the row padding: pad chunks 0 and 1 of row j hold lse2 and D of rows
-// 4j .. 4j+3.  d = 64: padded rows and a separate lse2 / D area.
+// distinct banks), two stages fill 80 KB, so the tile's -lse/s and -D go
+// into the row padding: pad chunks 0 and 1 of row j hold them for rows
+// 4j .. 4j+3.  d = 64: padded rows and a separate -lse/s, -D area.
+// The S and dP accumulators of a step start from those values, so the
+// products deliver S - lse/s and dP - D, and a score costs a multiply, an
+// exponential, a multiply and the two bf16 conversions.
 template <int D, bool CAUSAL, bool OUT_F32>
 __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkv_kernel(BwdArgs a)
 {
     constexpr bool SW = D == 128;
     using Cf = BCfg<D, SW>;
     constexpr int KB = Cf::kBytes, KS = D / 16, NC = D / 32;
-    constexpr int STAGE = 2 * KB + (SW ? 0 : 2 * kTile * 4);  // Q, dO (, lse2, D)
+    constexpr int STAGE = 2 * KB + (SW ? 0 : 2 * kTile * 4);  // Q, dO (, -lse/s, -D)
     __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
     const int lane = threadIdx.x & 63, g = lane >> 5, n = lane & 31;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -531,11 +537,11 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
                 }
             }
         }
-        const float *lsrc = a.lse2 + (size_t)hh * NP + q0, *dsrc = a.delta + (size_t)hh * NP + q0;
+        const float *lsrc = a.nlse + (size_t)hh * NP + q0, *dsrc = a.ndelta + (size_t)hh * NP + q0;
         if constexpr (SW) {
             // wave w fills the pads of rows 4w .. 4w+3: lane 20i + c writes
             // pad chunk c of row 4w + i (rows are 20 chunks apart), 16 bytes
-            // of lse2 (c = 0) or D (c = 1) of rows 4(4w+i) .. +3; the other
+            // of -lse/s (c = 0) or -D (c = 1) of rows 4(4w+i) .. +3; the other
             // lanes are off
             const int l = (int)lane_here(), li = l / 20, c = l - 20 * li;
             const uint32_t off = 16 * (4 * wave + li);
@@ -568,8 +574,29 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
             // causal: skip when every query of the step precedes every key of the wave
             if (CAUSAL && q0 + 32 * qs + 31 < kw0)
                 return;
-            // S = Q K^T and dP = dO V^T: rows = queries 32 qs + 8(r/4) + 4g + r%4
-            f32x16 s = f32x16{}, dp = f32x16{};
+            // S = Q K^T - lse/s and dP = dO V^T - D: rows = queries
+            // 32 qs + 8(r/4) + 4g + r%4; the accumulators start from -lse/s
+            // and -D of their rows (rows r0 .. r0+3 for registers 4R .. 4R+3)
+            f32x16 s, dp;
+#pragma unroll
+            for (int R = 0; R < 4; ++R) {
+                const int r0 = 32 * qs + 8 * R + 4 * g;
+                f32x4 l4, d4;
+                if constexpr (SW) {
+                    const unsigned char *pad = st + (r0 / 4) * Cf::kPitch + 2 * D;
+                    l4 = *(const f32x4 *)pad;
+                    d4 = *(const f32x4 *)(pad + 16);
+                } else {
+                    const float *lse_s = (const float *)(st + 2 * KB);
+                    l4 = *(const f32x4 *)(lse_s + r0);
+                    d4 = *(const f32x4 *)(lse_s + kTile + r0);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    s[4 * R + e] = l4[e];
+                    dp[4 * R + e] = d4[e];
+                }
+            }
             // the lane parts of the swizzled addresses are recomputed here
             // from the lane index (lane_here), not kept live across the loop:
             // at the 256-register bound they spilled
@@ -598,34 +625,25 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
                     s = mfma_bf16_32x32x16(as_bf16x8(x), kf[ks], s);
                     dp = mfma_bf16_32x32x16(as_bf16x8(y), vf[ks], dp);
                 });
-            // P = 2^(s cs - lse2), dS = P (dP - D).  Only the causal mask is
-            // tested, and only on sub-steps with a query before the wave's
-            // last key.  Queries past N need no test: their Q, dO, lse2 and D
-            // rows read as zero, so P = 1 and dP - D = 0 and both products
-            // add nothing.  Keys past N touch only their own (unstored) lane.
+            // P = 2^((S - lse/s) s log2(e)), dS = P (dP - D).  Only the
+            // causal mask is tested, and only on sub-steps with a query before
+            // the wave's last key (a masked exponent becomes -inf, so P = 0).
+            // Queries past N need no test: their Q, dO, -lse/s and -D rows
+            // read as zero, so P = 1 and dP - D = 0 and both products add
+            // nothing.  Keys past N touch only their own (unstored) lane.
             const int qf = q0 + 32 * qs;  // the sub-step's first query
-            const bool diag = CAUSAL && qf < kw0 + 31;
+            if (CAUSAL && qf < kw0 + 31) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int q = qf + 8 * (r >> 2) + 4 * g + (r & 3);
+                    s[r] = my_k <= q ? s[r] : -INFINITY;
+                }
+            }
             float p[16], ds[16];
 #pragma unroll
-            for (int R = 0; R < 4; ++R) {
-                const int r0 = 32 * qs + 8 * R + 4 * g;  // rows r0 .. r0+3 of the tile
-                f32x4 l4, d4;
-                if constexpr (SW) {
-                    const unsigned char *pad = st + (r0 / 4) * Cf::kPitch + 2 * D;
-                    l4 = *(const f32x4 *)pad;
-                    d4 = *(const f32x4 *)(pad + 16);
-                } else {
-                    const float *lse_s = (const float *)(st + 2 * KB);
-                    l4 = *(const f32x4 *)(lse_s + r0);
-                    d4 = *(const f32x4 *)(lse_s + kTile + r0);
-                }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * R + e, q = q0 + r0 + e;
-                    const bool ok = !diag || my_k <= q;
-                    p[r] = ok ? fast_exp2(s[r] * cs - l4[e]) : 0.f;
-                    ds[r] = p[r] * (dp[r] - d4[e]);
-                }
+            for (int r = 0; r < 16; ++r) {
+                p[r] = fast_exp2(s[r] * cs);
+                ds[r] = p[r] * dp[r];
             }
             uint32_t pw[8], dsw[8];
             pack16(p, pw);

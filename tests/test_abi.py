@@ -104,7 +104,8 @@ def _bwd(A, **kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(lse=None), -1), (dict(dout=None), -1), (dict(dk=None), -1), (dict(B=0), -1),
     (dict(N=0), -1), (dict(H=3), -1), (dict(scale=-2.0), -1), (dict(grad_dtype=5), -1),
-    (dict(d=32), -2), (dict(workspace=None), -3), (dict(workspace_bytes=10), -3),
+    (dict(scale=2.0 ** -65), -1), (dict(d=32), -2), (dict(workspace=None), -3),
+    (dict(workspace_bytes=10), -3),
 ])
 def test_bwd_validation(A, kw, status):
     assert _bwd(A, **kw) == status
@@ -112,7 +113,7 @@ def test_bwd_validation(A, kw, status):
 
 
 def test_bwd_workspace_size(A):
-    # fp32 D and lse*log2(e) per row, each head's rows padded to a multiple of 64
+    # fp32 -D and -lse/scale per row, each head's rows padded to a multiple of 64
     assert A.attn_bwd_workspace_size(2, 4, 100) == 2 * (((4 * 2 * 4 * 128) + 255) // 256 * 256)
     assert A.attn_bwd_workspace_size(1, 1, 64) == 2 * 256
     assert A.attn_bwd_workspace_size(0, 4, 100) == 0
