@@ -454,9 +454,11 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 // (lane n is key k0 + 32w + n).  For each query head of the group, query
 // tiles of 64 (with their -lse/s and -D rows) stream through a 2-stage LDS ring.
 // Two waves per SIMD (two workgroups per CU): the register budget of 256
-// then holds the dK/dV accumulators (128), the K/V fragments (64) and one
-// product of operand read-ahead; the second wave hides the LDS latency and
-// the score arithmetic, which the read-ahead of a single wave did not.
+// then holds the dK/dV accumulators (128), the K/V fragments (64) and the
+// operand read-ahead: one product while the S and dP accumulators are live,
+// two in the dV/dK products after them.  The second wave hides the LDS
+// latency and the score arithmetic, which the read-ahead of a single wave
+// did not.
 // d = 128: the Q and dO tiles use the swizzled layout (rows of 320 bytes; the
 // row reads of S and dP and the transposing reads of dV and dK fall on
 // distinct banks), two stages fill 80 KB, so the tile's -lse/s and -D go
@@ -650,14 +652,15 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
             pack16(ds, dsw);
             // dV^T += dO^T P and dK^T += Q^T dS: contraction over the step's queries
             // product pair i: queries 16u .. 16u+15 of the step (u = i / NC),
-            // feature block c = i % NC (consecutive pairs use different blocks)
+            // feature block c = i % NC (consecutive pairs use different
+            // blocks); the reads run two pairs ahead
             const int lt = SW ? (int)lane_here() : lane;
             const uint32_t ltr0 = SW ? swz_trans_addr<0>(0, lt) : 0;
             const uint32_t ltr8 = SW ? swz_trans_addr<8>(0, lt) : 0;
             const uint32_t qt_a = SW ? qa + ltr0 : trans_addr<D>(qa, lane);
             const uint32_t dt_a = SW ? da + ltr0 : trans_addr<D>(da, lane);
             const uint32_t qt8 = qa + ltr8, dt8 = da + ltr8;
-            operand_stream<2 * NC, 1, 4>(
+            operand_stream<2 * NC, 2, 4>(
                 [&](auto i, u32x4 &x, u32x4 &y) {
                     constexpr int I = decltype(i)::value, c = I % NC, u = I / NC;
                     if constexpr (SW) {
