@@ -104,8 +104,13 @@ def summed_traffic(keys, files):
     return None if any(p is None for p in parts) else sum(parts)
 
 
+# the backward's kernels, in launch order (the dQ kernel also writes the
+# per-row -D and -lse/scale the dK/dV kernel reads)
+BWD_KERNELS = ("bwd_dq", "bwd_dkv")
+
+
 def bwd_traffic():
-    return summed_traffic(("bwd_delta", "bwd_dq", "bwd_dkv"), ["bwd.hip", "cdna4.hpp"])
+    return summed_traffic(BWD_KERNELS, ["bwd.hip", "cdna4.hpp"])
 
 
 def stats(xs):
@@ -239,7 +244,7 @@ def bench_bwd(args, stream):
     # forward's FLOPs; the recomputation of S and dP in the dQ kernel is not
     # counted
     flops = 2.5 * w.flops()
-    names = ("bwd_delta", "bwd_dq", "bwd_dkv")
+    names = BWD_KERNELS
     ksum = {"mean": sum(per_kernel[n]["mean"] for n in names),
             "median": sum(per_kernel[n]["median"] for n in names)}
     files = ["bwd.hip", "cdna4.hpp"]
@@ -247,7 +252,7 @@ def bench_bwd(args, stream):
         "workload": w.name + "_bwd", "value": flops / (st["mean"] * 1e-3) / 1e12,
         "unit": "TFLOP/s", "ms_per_step": st["mean"], "step_ms": st, "flops": flops,
         "kernels_ms": per_kernel,
-        "roofline": roofline("mfma", "bwd_delta + bwd_dq + bwd_dkv", flops, ksum,
+        "roofline": roofline("mfma", " + ".join(names), flops, ksum,
                              PEAK_BF16_TFLOPS, "TFLOP/s",
                              traffic=summed_traffic(names, files),
                              counters={n: measured_util(n, files) for n in ("bwd_dq", "bwd_dkv")}),

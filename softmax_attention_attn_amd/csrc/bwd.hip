@@ -9,14 +9,15 @@
 //     dQ_i = s sum_j dS_ij K_j,  dK_j = s sum_i dS_ij Q_i,  dV_j = sum_i P_ij dO_i,
 // and a kv head's dK/dV sum over the query heads of its group.
 //
-// Three kernels, no atomics (every output element has one writer, so the
+// Two kernels, no atomics (every output element has one writer, so the
 // result is deterministic):
-//  * bwd_delta: -D_i = -(dO_i . O_i) in fp32, and -lse_i / s, per row.
 //  * bwd_dq: query-stationary.  A workgroup owns 128 queries (4 waves x 32)
 //    of one head, keeps their Q and dO in registers and streams the K/V
 //    tiles (64 keys) through LDS: S^T = K Q^T and dP^T = V dO^T on the MFMA,
 //    dS^T in registers, dQ^T += K^T dS^T with K^T gathered by transposing
-//    LDS reads.
+//    LDS reads.  It computes D_i = dO_i . O_i (fp32) for its own queries and
+//    also writes -D_i and -lse_i / s for the dK/dV kernel, which runs after
+//    it.
 //  * bwd_dkv: key-stationary.  A workgroup owns 128 keys (4 waves x 32) of
 //    one kv head, keeps their K and V in registers and streams, for every
 //    query head of the group, the Q/dO tiles (64 queries) through LDS:
@@ -250,44 +251,6 @@ __device__ __forceinline__ void operand_stream(Rd &&rd, Use &&use)
     });
 }
 
-// ---------------------------------------------------------------- -D, -lse/s
-// One 16-lane group per row: -D = -(dO . O) (fp32) and -lse / s.  These are
-// the values the dK/dV kernel starts its dP and S accumulators from, so the
-// products deliver dP - D and S - lse/s (the exponent over s log2(e)) with
-// no further per-score subtraction.
-// The arrays hold bwd_rows(N) rows per head; the rows past N get 0, so a
-// whole 64-row tile of them can be loaded and, with the zero Q and dO rows
-// the tile loads read past N, adds nothing to any product.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a)
-{
-    constexpr int LPR = D / 8;  // lanes per row (16 bytes each)
-    const int rows_per_block = 256 / LPR;
-    const int NP = bwd_rows(a.N);
-    const long long prow = (long long)blockIdx.x * rows_per_block + threadIdx.x / LPR;
-    const long long bh = prow / NP;
-    const int qi = (int)(prow - bh * NP);
-    const long long row = bh * a.N + qi;  // the row in the [B,H,N] tensors
-    const int sub = threadIdx.x % LPR;
-    const long long nprows = (long long)a.B * a.H * NP;
-    const bool real = prow < nprows && qi < a.N;
-    float dot = 0.f;
-    if (real) {
-        const u32x4 x = ld16_nt((const uint16_t *)a.dout + row * D + sub * 8);
-        const u32x4 y = ld16_nt((const uint16_t *)a.o + row * D + sub * 8);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            dot += bf16_lo(x[e]) * bf16_lo(y[e]) + bf16_hi(x[e]) * bf16_hi(y[e]);
-    }
-#pragma unroll
-    for (int off = LPR / 2; off > 0; off >>= 1)
-        dot += __shfl_xor(dot, off, LPR);
-    if (prow < nprows && sub == 0) {
-        a.ndelta[prow] = -dot;
-        a.nlse[prow] = real ? -a.lse[row] / a.scale : 0.f;
-    }
-}
-
 // ---------------------------------------------------------------- dQ
 // Workgroup: 128 queries of one (b, h); wave w owns queries q0 + 32w .. +31
 // (lane n = l % 32 is query q0 + 32w + n).  Key tiles of 64 stream through a
@@ -345,10 +308,29 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         df[ks] = as_bf16x8(valid_q ? ld16((const uint16_t *)a.dout + qrow * D + 16 * ks + 8 * g)
                                    : u32x4{0, 0, 0, 0});
     }
-    const size_t prow = (size_t)bh * bwd_rows(N) + my_q;  // row in the padded arrays
+    // D = dO . O (fp32 from the bf16 tensors): the lane holds columns
+    // 16ks + 8g .. +7 of its query's dO; the other half-wave the rest
+    float dpart = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 o4 = valid_q ? ld16_nt((const uint16_t *)a.o + qrow * D + 16 * ks + 8 * g)
+                                 : u32x4{0, 0, 0, 0};
+        const u32x4 d4 = __builtin_bit_cast(u32x4, df[ks]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            dpart += bf16_lo(d4[e]) * bf16_lo(o4[e]) + bf16_hi(d4[e]) * bf16_hi(o4[e]);
+    }
+    const float dlt = dpart + xor32(dpart);
+    const float lse = valid_q ? a.lse[qrow] : 0.f;
     const float cs = a.scale * kLog2e;
-    const float lse2 = valid_q ? -a.nlse[prow] * cs : 0.f;  // lse log2(e)
-    const float dlt = valid_q ? -a.ndelta[prow] : 0.f;
+    const float lse2 = lse * kLog2e;
+    // the dK/dV kernel's per-row -D and -lse/s, 0 on the padding rows past N
+    // (the workgroups cover every row of bwd_rows(N))
+    if (g == 0 && my_q < bwd_rows(N)) {
+        const size_t prow = (size_t)bh * bwd_rows(N) + my_q;
+        a.ndelta[prow] = valid_q ? -dlt : 0.f;
+        a.nlse[prow] = valid_q ? -lse / a.scale : 0.f;
+    }
 
     f32x16 acc[NC];
 #pragma unroll
@@ -690,14 +672,6 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 template <int D, bool CAUSAL, bool OUT_F32>
 hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t s)
 {
-    {
-        constexpr int rows_per_block = 256 / (D / 8);
-        const long long nrows = (long long)a.B * a.H * bwd_rows(a.N);
-        ProfScope ps("bwd_delta", s);
-        hipLaunchKernelGGL((bwd_delta_kernel<D>),
-                           dim3((unsigned)((nrows + rows_per_block - 1) / rows_per_block)),
-                           dim3(256), 0, s, a);
-    }
     const int nt = (a.N + kRows - 1) / kRows;
     {
         ProfScope ps("bwd_dq", s);
