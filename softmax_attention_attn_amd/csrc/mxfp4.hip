@@ -194,69 +194,86 @@ __global__ __launch_bounds__(D) void mx_kmean_kernel(MxWs w, int N)
     w.kmean[(size_t)bg * D + c] = (float)(s / (double)N);
 }
 
-// One thread per (row, 32-channel block) of Q (rows of BH*Npad) or of
-// K' = K - kmean (rows of BG*Npad); rows past N are zero (codes 0, scale 1).
-// A Q row's four threads also sum q . kmean for the LSE correction.
+// Q rows, then K' = K - kmean rows (each sequence padded to Npad rows, the
+// rows past N all zero): every 32-channel block gets its E8M0 exponent (R24)
+// and 16 bytes of E2M1 codes.  A workgroup takes 64 rows of one sequence as
+// CR = D/8 16-byte chunks per row; thread t takes chunks t, t + 256, ..., so
+// every load and store instruction of a wave covers contiguous memory and a
+// thread's channels are the same 8 in every chunk.  A block's four chunks sit
+// in four consecutive lanes: its amax is two lane shuffles, and each lane
+// writes the block's word for its chunk.
 template <int D>
 __global__ __launch_bounds__(kThreads) void mx_quant_qk_kernel(const uint16_t *q, const uint16_t *k,
                                                                MxWs w, int B, int H, int Hkv, int N)
 {
-    constexpr int NB = D / 32;  // blocks per row
+    constexpr int CR = D / 8;                  // chunks per row
+    constexpr int NB = D / 32;                 // blocks per row
+    constexpr int NCH = kTile * CR / kThreads;  // chunks per thread
+    static_assert(kThreads % CR == 0 && NCH * kThreads == kTile * CR, "chunk split");
     const int Npad = (N + kTile - 1) / kTile * kTile;
-    const long long t = (long long)blockIdx.x * kThreads + threadIdx.x;
-    const long long nq = (long long)B * H * Npad * NB, nk = (long long)B * Hkv * Npad * NB;
-    if (t >= nq + nk)
-        return;
-    const bool is_q = t < nq;
-    const long long u = is_q ? t : t - nq;
-    const int blk = (int)(u % NB);
-    const long long row = u / NB;  // seq * Npad + tok
-    const int tok = (int)(row % Npad);
-    const long long seq = row / Npad;  // b*H + h or b*Hkv + g
+    const int tid = threadIdx.x, ch = tid % CR;  // channels 8ch .. 8ch+7
+    const long long row0 = (long long)blockIdx.x * kTile;  // seq * Npad + tok0
+    const long long nqrows = (long long)B * H * Npad;
+    const bool is_q = row0 < nqrows;
+    const long long u0 = is_q ? row0 : row0 - nqrows;
+    const long long seq = u0 / Npad;  // b*H + h or b*Hkv + g
+    const int tok0 = (int)(u0 % Npad);
     const int g = is_q ? (int)((seq / H) * Hkv + (seq % H) / (H / Hkv)) : (int)seq;
-    const float *km = w.kmean + (size_t)g * D + 32 * blk;
-    float x[32];
-    if (tok < N) {
-        const uint16_t *src = (is_q ? q : k) + ((size_t)seq * N + tok) * D + 32 * blk;
+    float km[8];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const u32x4 v = ld16(src + 8 * j);
+    for (int e = 0; e < 8; ++e)
+        km[e] = w.kmean[(size_t)g * D + 8 * ch + e];
+    const uint16_t *src = (is_q ? q : k) + ((size_t)seq * N + tok0) * D;
+    uint8_t *dst = (is_q ? w.qhat : w.khat) + (size_t)u0 * (D / 2);
+    uint8_t *dsc = (is_q ? w.qsc : w.ksc) + (size_t)u0 * NB;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+        const int chunk = kThreads * j + tid, r = chunk / CR;
+        const bool real = tok0 + r < N;
+        float x[8];
+        {
+            u32x4 v = {0, 0, 0, 0};
+            if (real)
+                v = ld16(src + (size_t)chunk * 8);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                x[8 * j + 2 * e] = bf16_lo(v[e]);
-                x[8 * j + 2 * e + 1] = bf16_hi(v[e]);
+                x[2 * e] = bf16_lo(v[e]);
+                x[2 * e + 1] = bf16_hi(v[e]);
             }
         }
-    } else {
+        if (is_q) {
+            // q . kmean for the LSE correction; the row's CR lanes are consecutive
+            float dot = 0.f;
 #pragma unroll
-        for (int i = 0; i < 32; ++i)
-            x[i] = 0.f;
+            for (int i = 0; i < 8; ++i)
+                dot = fmaf(x[i], km[i], dot);
+#pragma unroll
+            for (int off = 1; off < CR; off <<= 1)
+                dot += __shfl_xor(dot, off, 64);
+            if (ch == 0 && real)
+                w.qkdot[(size_t)seq * N + tok0 + r] = dot;
+        } else if (real) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                x[i] -= km[i];
+        }
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            amax = fmaxf(amax, fabsf(x[i]));
+        amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+        amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+        const int e = mx_exp(amax);
+        const float sc = pow2f(e);
+        uint32_t word = 0;
+        word = fp4x2<0>(word, x[0], x[1], sc);
+        word = fp4x2<1>(word, x[2], x[3], sc);
+        word = fp4x2<2>(word, x[4], x[5], sc);
+        word = fp4x2<3>(word, x[6], x[7], sc);
+        *(uint32_t *)(dst + (size_t)chunk * 4) = word;
+        if ((ch & 3) == 0)
+            dsc[(size_t)r * NB + ch / 4] = (uint8_t)(e + 127);
     }
-    if (is_q) {
-        float dot = 0.f;
-#pragma unroll
-        for (int i = 0; i < 32; ++i)
-            dot = fmaf(x[i], km[i], dot);
-        // the row's NB threads are consecutive lanes
-#pragma unroll
-        for (int off = 1; off < NB; off <<= 1)
-            dot += __shfl_xor(dot, off, 64);
-        if (blk == 0 && tok < N)
-            w.qkdot[(size_t)seq * N + tok] = dot;
-    } else if (tok < N) {
-#pragma unroll
-        for (int i = 0; i < 32; ++i)
-            x[i] -= km[i];
-    }
-    float amax = 0.f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i)
-        amax = fmaxf(amax, fabsf(x[i]));
-    const int e = mx_exp(amax);
-    const u32x4 codes = fp4x32(x, e);
-    uint8_t *dst = (is_q ? w.qhat : w.khat) + (size_t)row * (D / 2) + 16 * blk;
-    st16(dst, codes);
-    (is_q ? w.qsc : w.ksc)[(size_t)row * NB + blk] = (uint8_t)(e + 127);
 }
 
 // One 64-key tile of V for one (batch, kv head): thread (c, h) turns the 32
@@ -604,8 +621,8 @@ hipError_t launch_d(const SageArgs &sa, hipStream_t s)
     }
     {
         ProfScope ps("mx_quant_qk", s);
-        const long long items = (long long)(BH + BG) * Npad * (D / 32);
-        hipLaunchKernelGGL(mx_quant_qk_kernel<D>, dim3((unsigned)((items + kThreads - 1) / kThreads)),
+        const long long rows = (long long)(BH + BG) * Npad;  // 64 rows per workgroup
+        hipLaunchKernelGGL(mx_quant_qk_kernel<D>, dim3((unsigned)(rows / kTile)),
                            dim3(kThreads), 0, s, q, k, w, a.B, a.H, a.Hkv, a.N);
     }
     {

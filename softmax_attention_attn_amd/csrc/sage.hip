@@ -228,115 +228,148 @@ __device__ __forceinline__ int q_i8(float x, float inv)
 }
 
 // One 64-token block of Q (blockIdx.x < BH*nblk) or of K' = K - kmean.
-// Thread t owns row t / 4 and channels (t % 4) * D/4 .. + D/4.
+// The block is 64 rows of D bf16 (CR = D/8 16-byte chunks per row); thread t
+// takes chunks t, t + 256, ...: every load and store instruction of a wave
+// covers one contiguous run of memory, and a thread's channels are the same
+// 8 in every chunk (256 is a multiple of CR).
 template <int D>
 __global__ __launch_bounds__(kThreads) void sage_quant_qk_kernel(const uint16_t *q, const uint16_t *k,
                                                                  SageWs w, int B, int H, int Hkv,
                                                                  int N)
 {
-    constexpr int CPT = D / 4;  // channels per thread
+    constexpr int CR = D / 8;               // chunks per row
+    constexpr int NCH = kBlk * CR / kThreads;  // chunks per thread
+    static_assert(kThreads % CR == 0 && NCH * kThreads == kBlk * CR, "chunk split");
     __shared__ float scratch[4];
     const int nblk = (N + kBlk - 1) / kBlk, Npad = nblk * kBlk;
-    const int tid = threadIdx.x, row = tid >> 2, c0 = (tid & 3) * CPT;
+    const int tid = threadIdx.x, c0 = (tid % CR) * 8;
     int id = blockIdx.x;
     const bool is_q = id < B * H * nblk;
     if (!is_q)
         id -= B * H * nblk;
     const int seq = id / nblk, blk = id % nblk;  // seq = b*H + h or b*Hkv + g
-    const int tok = blk * kBlk + row;
-    const uint16_t *src = (is_q ? q : k) + ((size_t)seq * N + tok) * D + c0;
+    const int tok0 = blk * kBlk;
+    const uint16_t *src = (is_q ? q : k) + ((size_t)seq * N + tok0) * D;
     const int g = is_q ? (seq / H) * Hkv + (seq % H) / (H / Hkv) : seq;
-    const float *km = w.kmean + (size_t)g * D + c0;
+    float km[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        km[e] = w.kmean[(size_t)g * D + c0 + e];
 
-    float x[CPT];
-    if (tok < N) {
+    float x[NCH][8];
 #pragma unroll
-        for (int j = 0; j < CPT / 8; ++j) {
-            const u32x4 u = ld16(src + 8 * j);
+    for (int j = 0; j < NCH; ++j) {
+        const int chunk = kThreads * j + tid, row = chunk / CR;
+        u32x4 u = {0, 0, 0, 0};
+        if (tok0 + row < N)
+            u = ld16(src + (size_t)chunk * 8);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                x[8 * j + 2 * e] = bf16_lo(u[e]);
-                x[8 * j + 2 * e + 1] = bf16_hi(u[e]);
-            }
+        for (int e = 0; e < 4; ++e) {
+            x[j][2 * e] = bf16_lo(u[e]);
+            x[j][2 * e + 1] = bf16_hi(u[e]);
+        }
+    }
+    if (is_q) {
+        // q . kmean per row, for the LSE correction: CR consecutive lanes
+        // hold one row
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            float dot = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                dot = fmaf(x[j][e], km[e], dot);
+#pragma unroll
+            for (int off = 1; off < CR; off <<= 1)
+                dot += __shfl_xor(dot, off, 64);
+            const int row = (kThreads * j + tid) / CR;
+            if (tid % CR == 0 && tok0 + row < N)
+                w.qkdot[(size_t)seq * N + tok0 + row] = dot;
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < CPT; ++i)
-            x[i] = 0.f;
-    }
-    if (is_q) {
-        // q . kmean for the LSE correction
-        float dot = 0.f;
+        for (int j = 0; j < NCH; ++j) {
+            if (tok0 + (kThreads * j + tid) / CR < N) {
 #pragma unroll
-        for (int i = 0; i < CPT; ++i)
-            dot = fmaf(x[i], km[i], dot);
-        dot += __shfl_xor(dot, 1, 64);
-        dot += __shfl_xor(dot, 2, 64);
-        if ((tid & 3) == 0 && tok < N)
-            w.qkdot[(size_t)seq * N + tok] = dot;
-    } else if (tok < N) {
-#pragma unroll
-        for (int i = 0; i < CPT; ++i)
-            x[i] -= km[i];
+                for (int e = 0; e < 8; ++e)
+                    x[j][e] -= km[e];
+            }
+        }
     }
     float amax = 0.f;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i)
-        amax = fmaxf(amax, fabsf(x[i]));
+    for (int j = 0; j < NCH; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            amax = fmaxf(amax, fabsf(x[j][e]));
     amax = block_max_256(amax, scratch);
     const float inv = amax > 0.f ? 127.f / amax : 1.f;
     if (tid == 0)
         (is_q ? w.qdelta : w.kdelta)[(size_t)seq * nblk + blk] = amax > 0.f ? amax / 127.f : 1.f;
-    int8_t *dst = (is_q ? w.qhat : w.khat) + ((size_t)seq * Npad + tok) * D + c0;
+    int8_t *dst = (is_q ? w.qhat : w.khat) + ((size_t)seq * Npad + tok0) * D;
 #pragma unroll
-    for (int j = 0; j < CPT / 16; ++j) {
-        u32x4 out;
+    for (int j = 0; j < NCH; ++j) {
+        uint32_t out[2];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int b = 16 * j + 4 * e;
-            out[e] = (uint32_t)(q_i8(x[b], inv) & 0xff) | ((uint32_t)(q_i8(x[b + 1], inv) & 0xff) << 8) |
-                     ((uint32_t)(q_i8(x[b + 2], inv) & 0xff) << 16) |
-                     ((uint32_t)(q_i8(x[b + 3], inv) & 0xff) << 24);
-        }
-        st16(dst + 16 * j, out);
+        for (int h = 0; h < 2; ++h)
+            out[h] = (uint32_t)(q_i8(x[j][4 * h], inv) & 0xff) |
+                     ((uint32_t)(q_i8(x[j][4 * h + 1], inv) & 0xff) << 8) |
+                     ((uint32_t)(q_i8(x[j][4 * h + 2], inv) & 0xff) << 16) |
+                     ((uint32_t)(q_i8(x[j][4 * h + 3], inv) & 0xff) << 24);
+        *(uint2 *)(dst + (size_t)(kThreads * j + tid) * 8) = make_uint2(out[0], out[1]);
     }
 }
 
 // E4M3 of V / delta_V (round to nearest even, saturated to +-448) for one
-// 64-key tile, written feature-major: vhatT[bg][c][tile*64 + key].
+// 64-key tile, written feature-major: vhatT[bg][c][tile*64 + key].  Thread t
+// takes channels 8 (t % CR) .. +7 of the 4 consecutive tokens 4 (t / CR) ..
+// +3 (CR = D/8: 256 threads cover the 64 tokens when D = 128, the first 128
+// when D = 64); a channel's 4 bytes form one word, written to LDS rows of 68
+// bytes (the 17-word pitch spreads a wave's words over the banks), then whole
+// 16-byte runs of a channel go out.
 template <int D>
 __global__ __launch_bounds__(kThreads) void sage_quant_v_kernel(const uint16_t *v, SageWs w, int N)
 {
-    constexpr int CPT = D / 4;
-    __shared__ __attribute__((aligned(16))) uint8_t tile[D][kBlk];
+    constexpr int CR = D / 8;         // 16-byte chunks per row
+    constexpr int kPitch = kBlk + 4;  // bytes per LDS row (channel)
+    static_assert(kBlk / 4 * CR <= kThreads, "one group of 4 tokens per thread");
+    __shared__ __attribute__((aligned(16))) uint32_t tile[D * kPitch / 4];
     const int nblk = (N + kBlk - 1) / kBlk, Npad = nblk * kBlk;
     const int bg = blockIdx.x, blk = blockIdx.y, tid = threadIdx.x;
-    const int row = tid >> 2, c0 = (tid & 3) * CPT;
-    const int tok = blk * kBlk + row;
-    const float *vi = w.vinv + (size_t)bg * D + c0;
+    const int c0 = (tid % CR) * 8;
+    float vi[8];
 #pragma unroll
-    for (int j = 0; j < CPT / 8; ++j) {
-        u32x4 u = {0, 0, 0, 0};
-        if (tok < N)
-            u = ld16(v + ((size_t)bg * N + tok) * D + c0 + 8 * j);
+    for (int e = 0; e < 8; ++e)
+        vi[e] = w.vinv[(size_t)bg * D + c0 + e];
+    const int tg = tid / CR;  // tokens 4tg .. 4tg+3
+    if (tg < kBlk / 4) {
+        u32x4 u[4];
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-            const int c = 8 * j + e;
-            float a = bf16_lo(u[e >> 1]);
-            float b = bf16_hi(u[e >> 1]);
-            a = fminf(fmaxf(a * vi[c], -448.f), 448.f);
-            b = fminf(fmaxf(b * vi[c + 1], -448.f), 448.f);
-            const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-            tile[c0 + c][row] = (uint8_t)(pk & 0xff);
-            tile[c0 + c + 1][row] = (uint8_t)((pk >> 8) & 0xff);
+        for (int i = 0; i < 4; ++i) {
+            const int tok = blk * kBlk + 4 * tg + i;
+            u[i] = u32x4{0, 0, 0, 0};
+            if (tok < N)
+                u[i] = ld16(v + ((size_t)bg * N + tok) * D + c0);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float x[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float f = (e & 1) ? bf16_hi(u[i][e >> 1]) : bf16_lo(u[i][e >> 1]);
+                x[i] = fminf(fmaxf(f * vi[e], -448.f), 448.f);
+            }
+            int wd = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+            wd = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], wd, true);
+            tile[((c0 + e) * kPitch + 4 * tg) / 4] = (uint32_t)wd;
         }
     }
     __syncthreads();
-    // D rows x 64 bytes = D*4 chunks of 16 bytes
+    // D rows x 64 bytes = D*4 runs of 16 bytes
     for (int i = tid; i < D * 4; i += kThreads) {
         const int c = i >> 2, part = i & 3;
+        const uint32_t *r = tile + (c * kPitch + part * 16) / 4;
         st16(w.vhatT + ((size_t)bg * D + c) * Npad + blk * kBlk + part * 16,
-             *(const u32x4 *)&tile[c][part * 16]);
+             u32x4{r[0], r[1], r[2], r[3]});
     }
 }
 
