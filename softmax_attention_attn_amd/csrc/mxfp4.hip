@@ -163,6 +163,8 @@ __global__ __launch_bounds__(kThreads) void mx_ksum_kernel(const uint16_t *k, Mx
     const int r0 = chunk * len, r1 = min(N, r0 + len);
     const uint16_t *kb = k + (size_t)bg * N * D;
     double s[8] = {};
+    // unrolled, so that several rows' loads are in flight per thread
+#pragma unroll 4
     for (int r = r0 + rg; r < r1; r += RPP) {
         const u32x4 kw = ld16_nt(kb + (size_t)r * D + fc * 8);
 #pragma unroll

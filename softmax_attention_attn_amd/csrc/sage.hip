@@ -162,6 +162,8 @@ __global__ __launch_bounds__(kThreads) void sage_stats_kernel(const uint16_t *k,
     const uint16_t *kb = k + (size_t)bg * N * D, *vb = v + (size_t)bg * N * D;
     double ks[8] = {};
     float vm[8] = {};
+    // unrolled, so that several rows' loads are in flight per thread
+#pragma unroll 4
     for (int r = r0 + rg; r < r1; r += RPP) {
         const u32x4 kw = ld16_nt(kb + (size_t)r * D + fc * 8);
         const u32x4 vw = ld16_nt(vb + (size_t)r * D + fc * 8);
