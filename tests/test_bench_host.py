@@ -1,6 +1,6 @@
 """Host logic of bench.py, on the CPU: the committed counter runs are reported
 only while the kernel source they were taken on is unchanged, the backward's
-traffic is the sum of its three kernels', and a request for more than one GPU
+traffic is the sum of its kernels', and a request for more than one GPU
 is refused before anything touches a device."""
 import json
 import os
