@@ -615,6 +615,30 @@ __device__ __forceinline__ void attend_qtile(const PrefillArgs &a, unsigned char
     }
 }
 
+// Packed batch: the sequence of rank r when the sequences are ordered by
+// length, longest first (ties by index), for B <= 64 (lane x holds sequence
+// x's clamped length); larger batches keep their own order.  Dispatching the
+// longest sequences first leaves the short ones to fill the end of the grid.
+__device__ __forceinline__ int seq_of_rank(const PrefillArgs &a, int r)
+{
+    if (a.B > 64)
+        return r;
+    const int x = (int)(threadIdx.x & 63);
+    int len = -1;
+    if (x < a.B) {
+        const int t0 = min(max(a.cu_seqlens[x], 0), a.total);
+        const int t1 = min(max(a.cu_seqlens[x + 1], t0), a.total);
+        len = min(t1 - t0, a.N);
+    }
+    int rank = 0;
+    for (int y = 0; y < a.B; ++y) {
+        const int ly = __shfl(len, y, 64);
+        rank += (ly > len || (ly == len && y < x)) ? 1 : 0;
+    }
+    const unsigned long long hit = __ballot(x < a.B && rank == r);
+    return hit ? __ffsll((long long)hit) - 1 : r;
+}
+
 template <int D, bool CAUSAL, bool OUT_F32, bool VARLEN>
 __global__ __launch_bounds__(kThreads) void prefill_exact_kernel(PrefillArgs a)
 {
@@ -642,7 +666,8 @@ __global__ __launch_bounds__(kThreads) void prefill_exact_kernel(PrefillArgs a)
         bh = wg / nw;
         j = wg % nw;
     }
-    const int h = bh % a.H, b = bh / a.H;
+    const int h = bh % a.H;
+    const int b = VARLEN ? seq_of_rank(a, bh / a.H) : bh / a.H;
     const int kvh = h / (a.H / a.Hkv);
     SeqView sv;
     if constexpr (VARLEN) {
