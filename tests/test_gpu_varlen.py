@@ -52,6 +52,24 @@ def test_varlen_small(attn, case, causal, out_dtype):
                 bf16_out=out_dtype == torch.bfloat16, what="varlen %s" % (case,))
 
 
+@pytest.mark.parametrize("nseq", [64, 70], ids=["B64", "B70"])
+def test_varlen_many_sequences(attn, nseq):
+    """Up to 64 sequences are dispatched longest first (ranked in a wave,
+    ties by index); beyond 64 they keep their order.  Both sides of that
+    bound, with repeated and zero lengths, every row against the oracle."""
+    g = torch.Generator().manual_seed(nseq)
+    lens = tuple(int(x) for x in torch.randint(0, 160, (nseq,), generator=g))
+    lens = lens[:5] + (lens[5],) * 3 + (0,) + lens[9:]
+    H, Hkv, d = 2, 1, 64
+    q, k, v, cu = workloads.make_varlen(lens, H, Hkv, d, seed=nseq)
+    o, lse = attn.fwd_varlen(q.cuda(), k.cuda(), v.cuda(), cu.cuda(), max(lens), causal=True,
+                             out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = _oracle(q, k, v, cu, True, 1 / math.sqrt(d))
+    check_exact(o.float().cpu().numpy(), o_ref, lse.cpu().numpy(), lse_ref, bf16_out=False,
+                what="varlen %d sequences" % nseq)
+
+
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
 def test_varlen_equal_lengths_match_fixed_layout(attn, causal):
     B, H, Hkv, N, d = 3, 8, 2, 700, 128
