@@ -103,6 +103,16 @@ struct KeySplit {
     }
 };
 
+// the split of Hkv * (sum of the clamped lengths) keys
+__device__ __forceinline__ KeySplit key_split_of(const DecodeArgs &a, long long len_sum)
+{
+    KeySplit ks;
+    ks.K = uniform64(len_sum * a.Hkv);
+    const long long w = ks.K / kMinKeysPerWave;
+    ks.W = (int)(w < 1 ? 1 : (w > kDecodeWaves ? kDecodeWaves : w));
+    return ks;
+}
+
 __device__ __forceinline__ KeySplit key_split(const DecodeArgs &a, int lane)
 {
     long long s = 0;
@@ -113,11 +123,7 @@ __device__ __forceinline__ KeySplit key_split(const DecodeArgs &a, int lane)
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1)
         s += __shfl_xor(s, off, 64);
-    KeySplit ks;
-    ks.K = uniform64(s * a.Hkv);
-    const long long w = ks.K / kMinKeysPerWave;
-    ks.W = (int)(w < 1 ? 1 : (w > kDecodeWaves ? kDecodeWaves : w));
-    return ks;
+    return key_split_of(a, s);
 }
 
 // The segment holding global key x: its sequence b, the global offset of its
@@ -543,21 +549,27 @@ __global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(DecodeAr
     const int bh = (int)blockIdx.x * kMergeWaves + (int)(threadIdx.x >> 6);
     if (bh >= a.B * a.H)
         return;
-    const KeySplit ks = key_split(a, lane);
     const int G = a.H / a.Hkv;
     const int b = bh / a.H, h = bh % a.H, kvh = h / G, g = h % G;
-    // global offset of the segment (b, kvh): locate its sequence's first key
+    // one pass over the lengths gives both the key split (their sum, as
+    // key_split computes it) and the global offset of the segment (b, kvh)
+    // (the sum over the sequences before b)
+    KeySplit ks{};
     long long seq0 = 0;
     {
-        long long base = 0;
-        for (int b0 = 0; b0 < b; b0 += 64) {
+        long long tot = 0, base = 0;
+        for (int b0 = 0; b0 < a.B; b0 += 64) {
             const int bb = b0 + lane;
-            long long len = bb < b ? clamp_len(a.seqlens, bb, a.N_max) : 0;
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1)
-                len += __shfl_xor(len, off, 64);
-            base += len;
+            const long long len = bb < a.B ? clamp_len(a.seqlens, bb, a.N_max) : 0;
+            tot += len;
+            base += bb < b ? len : 0;
         }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            tot += __shfl_xor(tot, off, 64);
+            base += __shfl_xor(base, off, 64);
+        }
+        ks = key_split_of(a, tot);
         seq0 = base * a.Hkv;
     }
     const int L = clamp_len(a.seqlens, b, a.N_max);
@@ -567,8 +579,10 @@ __global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(DecodeAr
     const int n = last - first + 1;
     const float *pl = a.part_lse + g;             // slot s: pl[s * G]
     const float *po = a.part_o + (size_t)g * D + F * lane;  // slot s: po[s * G * D]
-    float M = -INFINITY;
-    for (int j = lane; j < n; j += 64)
+    // the first 64 partials' LSEs stay in registers for their weights
+    const float l0 = lane < n ? pl[(size_t)(first + lane) * G] : -INFINITY;
+    float M = l0;
+    for (int j = lane + 64; j < n; j += 64)
         M = fmaxf(M, pl[(size_t)(first + j) * G]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1)
@@ -576,7 +590,8 @@ __global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(DecodeAr
     float wsum = 0.f;
     float acc[F] = {};
     for (int j0 = 0; j0 < n; j0 += 64) {
-        const float wj_l = j0 + lane < n ? fast_exp2(pl[(size_t)(first + j0 + lane) * G] - M) : 0.f;
+        const float lj = j0 == 0 ? l0 : (j0 + lane < n ? pl[(size_t)(first + j0 + lane) * G] : 0.f);
+        const float wj_l = j0 + lane < n ? fast_exp2(lj - M) : 0.f;
         wsum += wj_l;
         const int m = min(64, n - j0);
         for (int j = 0; j < m; ++j) {
