@@ -280,12 +280,14 @@ __global__ __launch_bounds__(kThreads) void mx_quant_qk_kernel(const uint16_t *q
 
 // One 64-key tile of V for one (batch, kv head): thread (c, h) turns the 32
 // keys 32h .. 32h+31 of channel c into one block: 16 bytes of vhatT and its
-// scale byte.  The tile is staged through LDS to read it by channel.
+// scale byte.  The tile is staged through LDS as bf16 (rows of D + 8
+// elements, 17 KB, so that nine workgroups fit a CU) to read it by channel.
 template <int D>
 __global__ __launch_bounds__(kThreads) void mx_quant_v_kernel(const uint16_t *v, MxWs w, int N)
 {
     static_assert(2 * D <= kThreads, "one thread per (channel, half tile)");
-    __shared__ float tile[kTile][D + 1];
+    constexpr int P = D + 8;  // row pitch (elements): 16-byte aligned rows
+    __shared__ __attribute__((aligned(16))) uint16_t tile[kTile * P];
     const int Npad = (N + kTile - 1) / kTile * kTile;
     const int bg = blockIdx.x, tt = blockIdx.y, tid = threadIdx.x;
     for (int i = tid; i < kTile * D / 8; i += kThreads) {
@@ -294,11 +296,7 @@ __global__ __launch_bounds__(kThreads) void mx_quant_v_kernel(const uint16_t *v,
         u32x4 u = {0, 0, 0, 0};
         if (tok < N)
             u = ld16_nt(v + ((size_t)bg * N + tok) * D + c8);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            tile[r][c8 + 2 * e] = bf16_lo(u[e]);
-            tile[r][c8 + 2 * e + 1] = bf16_hi(u[e]);
-        }
+        *(u32x4 *)&tile[r * P + c8] = u;
     }
     __syncthreads();
     if (tid < 2 * D) {
@@ -307,7 +305,7 @@ __global__ __launch_bounds__(kThreads) void mx_quant_v_kernel(const uint16_t *v,
         float amax = 0.f;
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
-            x[i] = tile[32 * h + i][c];
+            x[i] = __uint_as_float((uint32_t)tile[(32 * h + i) * P + c] << 16);
             amax = fmaxf(amax, fabsf(x[i]));
         }
         const int e = mx_exp(amax);
