@@ -123,6 +123,25 @@ def test_bwd_llm_prefill_slices(attn):
         print("llm_prefill", b, h, res)
 
 
+def test_bwd_noncausal_headline_slices(attn):
+    """The headline shape without the mask (every query sees every key, so
+    no tile of either kernel skips or masks anything), fp32 gradients: two
+    whole (b, h) slices against the oracle."""
+    w = workloads.WORKLOADS["llm_prefill"]
+    inp = workloads.make(w)
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    do = workloads.make_prefill(w.B, w.H, w.Hkv, w.N, w.d, seed=2)[0]
+    dq, dk, dv = _run(attn, q, k, v, do, False)
+    slices = ((1, 3), (2, 30))
+    st = lambda t: torch.cat([t[b:b + 1, h:h + 1] for b, h in slices]).contiguous()
+    ref = _ref(st(q), st(k), st(v), st(do), False, w.scale)
+    for i, (b, h) in enumerate(slices):
+        one = tuple(r[i:i + 1] for r in ref)
+        res = check_grads(dq[b:b + 1, h:h + 1], dk[b:b + 1, h:h + 1], dv[b:b + 1, h:h + 1],
+                          one, "llm_prefill non-causal slice %d,%d" % (b, h))
+        print("llm_prefill non-causal", b, h, res)
+
+
 def test_bwd_gqa_headline_size(attn):
     """GQA at the headline size (B4 H32 Hkv8 N4096 d128 causal, bf16
     gradients): a kv head's dK/dV sum the gradients of its 4 query heads.
