@@ -34,9 +34,15 @@ What each routine follows:
   FP4 microscaling on CDNA4's MX formats: E2M1 elements with a power-of-two
   E8M0 scale per block of 32, for Q, K, V and P; "gpu-kernel-porting-with-ai-agents"
   page, SageAttention 3 section; "GPU kernel overview" page, insights on FP4).
+* ``mx_rows`` -- the same recipe with the element format as a parameter:
+  E2M1 (``mxfp4_rows``) or the MX FP6 format E2M3 (``mxfp6_rows``); the
+  "GPU kernel overview" page's insights name FP4 and FP6 as the low-bit
+  formats of CDNA4's matrix cores.
 * ``e4m3_decode`` / ``e4m3_encode`` -- the OCP E4M3 ("fn") format;
   ``e2m1_decode`` / ``e2m1_encode`` / ``mx_scale_exp`` -- the MX FP4 element
-  format and the choice of a block's scale.
+  format and the choice of a block's scale; ``e2m3_decode`` /
+  ``e2m3_encode`` / ``mx_scale_exp_max`` -- the MX FP6 element format and the
+  scale rule for a format of any largest magnitude.
 * ``gather_pages`` -- the paged KV layout (a pool of fixed-size pages named by
   a per-sequence page table) turned back into contiguous caches, so that
   paged decode is checked against ``attn_rows`` ("flashattention-kernels"
@@ -114,11 +120,18 @@ def _load():
     lib.oracle_e2m1_encode.argtypes = [ctypes.c_double]
     lib.oracle_mx_scale_exp.restype = ctypes.c_int
     lib.oracle_mx_scale_exp.argtypes = [ctypes.c_double]
-    lib.oracle_mxfp4_rows.restype = ctypes.c_double
-    lib.oracle_mxfp4_rows.argtypes = [
+    lib.oracle_e2m3_decode.restype = ctypes.c_double
+    lib.oracle_e2m3_decode.argtypes = [ctypes.c_uint8]
+    lib.oracle_e2m3_encode.restype = ctypes.c_uint8
+    lib.oracle_e2m3_encode.argtypes = [ctypes.c_double]
+    lib.oracle_mx_scale_exp_max.restype = ctypes.c_int
+    lib.oracle_mx_scale_exp_max.argtypes = [ctypes.c_double, ctypes.c_double]
+    lib.oracle_mx_rows.restype = ctypes.c_double
+    lib.oracle_mx_rows.argtypes = [
         _u16p, _u16p, _u16p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-        ctypes.c_int, ctypes.c_int, _i64p, ctypes.c_int64, _f64p, _f64p, ctypes.c_int]
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, _i64p, ctypes.c_int64, _f64p, _f64p,
+        ctypes.c_int]
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -316,13 +329,16 @@ def sage_quantise(q, k, v, *, blk: int = 64, smooth_k: bool = True):
     return out
 
 
-def mxfp4_rows(q, k, v, *, causal: bool, scale: float, rows=None, tile_n: int = 64,
-               smooth_k: bool = True, quant_qk: bool = True, quant_p: bool = True,
-               quant_v: bool = True, threads: int | None = None):
-    """MXFP4 quantised attention (SageAttention3-style, MX block formats)
-    emulated step by step in fp64; see ``oracle_mxfp4_rows`` in oracle.c.
-    Same shapes and ``rows`` convention as :func:`sage_rows`.  Returns
-    (o, lse)."""
+MX_ELEMS = {"e2m1": 0, "e2m3": 1}
+
+
+def mx_rows(q, k, v, *, causal: bool, scale: float, elem: str, rows=None, tile_n: int = 64,
+            smooth_k: bool = True, quant_qk: bool = True, quant_p: bool = True,
+            quant_v: bool = True, threads: int | None = None):
+    """MX quantised attention (SageAttention3-style, MX block formats) with
+    elements ``elem`` ("e2m1": MXFP4, "e2m3": MXFP6), emulated step by step in
+    fp64; see ``oracle_mx_rows`` in oracle.c.  Same shapes and ``rows``
+    convention as :func:`sage_rows`.  Returns (o, lse)."""
     q, k, v = _u16(q), _u16(k), _u16(v)
     B, H, N, d = q.shape
     Hkv = k.shape[1]
@@ -337,17 +353,27 @@ def mxfp4_rows(q, k, v, *, causal: bool, scale: float, rows=None, tile_n: int = 
         rows_p = _ptr(rows, _i64p)
     o = np.empty((nrows, d), dtype=np.float64)
     lse = np.empty((nrows,), dtype=np.float64)
-    r = _load().oracle_mxfp4_rows(_ptr(q, _u16p), _ptr(k, _u16p), _ptr(v, _u16p), B, H, Hkv, N,
-                                  d, int(bool(causal)), float(scale), int(tile_n),
-                                  int(smooth_k), int(quant_qk), int(quant_p), int(quant_v),
-                                  rows_p, nrows, _ptr(o, _f64p), _ptr(lse, _f64p),
-                                  int(threads or default_threads()))
+    r = _load().oracle_mx_rows(_ptr(q, _u16p), _ptr(k, _u16p), _ptr(v, _u16p), B, H, Hkv, N,
+                               d, int(bool(causal)), float(scale), int(tile_n), MX_ELEMS[elem],
+                               int(smooth_k), int(quant_qk), int(quant_p), int(quant_v),
+                               rows_p, nrows, _ptr(o, _f64p), _ptr(lse, _f64p),
+                               int(threads or default_threads()))
     if r < 0:
-        raise ValueError("oracle_mxfp4_rows rejected its arguments")
+        raise ValueError("oracle_mx_rows rejected its arguments")
     if rows is None:
         o = o.reshape(B, H, N, d)
         lse = lse.reshape(B, H, N)
     return o, lse
+
+
+def mxfp4_rows(q, k, v, **kw):
+    """:func:`mx_rows` with E2M1 elements (the MXFP4 recipe)."""
+    return mx_rows(q, k, v, elem="e2m1", **kw)
+
+
+def mxfp6_rows(q, k, v, **kw):
+    """:func:`mx_rows` with E2M3 elements (the MXFP6 recipe)."""
+    return mx_rows(q, k, v, elem="e2m3", **kw)
 
 
 def e2m1_decode(codes) -> np.ndarray:
@@ -367,6 +393,26 @@ def mx_scale_exp(amax) -> np.ndarray:
     lib = _load()
     a = np.asarray(amax, dtype=np.float64)
     return np.array([lib.oracle_mx_scale_exp(float(t)) for t in a.ravel()],
+                    dtype=np.int64).reshape(a.shape)
+
+
+def e2m3_decode(codes) -> np.ndarray:
+    lib = _load()
+    codes = np.asarray(codes, dtype=np.uint8)
+    return np.array([lib.oracle_e2m3_decode(int(c)) for c in codes.ravel()]).reshape(codes.shape)
+
+
+def e2m3_encode(x) -> np.ndarray:
+    lib = _load()
+    x = np.asarray(x, dtype=np.float64)
+    return np.array([lib.oracle_e2m3_encode(float(t)) for t in x.ravel()],
+                    dtype=np.uint8).reshape(x.shape)
+
+
+def mx_scale_exp_max(amax, emax: float) -> np.ndarray:
+    lib = _load()
+    a = np.asarray(amax, dtype=np.float64)
+    return np.array([lib.oracle_mx_scale_exp_max(float(t), float(emax)) for t in a.ravel()],
                     dtype=np.int64).reshape(a.shape)
 
 

@@ -697,17 +697,84 @@ int oracle_mx_scale_exp(double amax)
     return e;
 }
 
+/*
+ * OCP MX FP6 E2M3: 1 sign bit, 2 exponent bits (bias 1), 3 mantissa bits, no
+ * infinities or NaN.  Exponent field 0 is subnormal (M/8); otherwise
+ * 2^(E-1) * (1 + M/8).  The positive magnitudes are the multiples of 1/8 in
+ * [0, 2), of 1/4 in [2, 4) and of 1/2 in [4, 7.5].
+ */
+double oracle_e2m3_decode(uint8_t code)
+{
+    int s = (code >> 5) & 1, e = (code >> 3) & 3, m = code & 7;
+    double mag = e == 0 ? m / 8.0 : ldexp(1.0 + m / 8.0, e - 1);
+    return s ? -mag : mag;
+}
+
+/* Nearest E2M3 code, ties to the even code, saturating at +-7.5 (the
+ * positive codes 0..31 are increasing in value). */
+uint8_t oracle_e2m3_encode(double x)
+{
+    uint8_t sign = x < 0 ? 32 : 0;
+    double a = fabs(x);
+    if (a >= 7.5)
+        return sign | 31;
+    int c = 0;
+    while (c < 31 && oracle_e2m3_decode((uint8_t)(c + 1)) <= a)
+        ++c;
+    if (c < 31) {
+        double db = a - oracle_e2m3_decode((uint8_t)c);
+        double da = oracle_e2m3_decode((uint8_t)(c + 1)) - a;
+        if (da < db || (da == db && ((c + 1) & 1) == 0))
+            c = c + 1;
+    }
+    return sign | (uint8_t)c;
+}
+
+/* The element formats of the MX blocks: E2M1 (FP4) and E2M3 (FP6). */
+enum { MX_E2M1 = 0, MX_E2M3 = 1 };
+
+static double mx_elem_max(int elem) { return elem == MX_E2M3 ? 7.5 : 6.0; }
+
+static double mx_elem_round(int elem, double y)
+{
+    return elem == MX_E2M3 ? oracle_e2m3_decode(oracle_e2m3_encode(y))
+                           : oracle_e2m1_decode(oracle_e2m1_encode(y));
+}
+
+/*
+ * Exponent e of the shared scale 2^e of an MX block whose elements have the
+ * largest magnitude `emax`: the smallest e with amax <= emax * 2^e, clamped
+ * to E8M0's range [-127, 127]; an all-zero block gets e = 0.
+ */
+int oracle_mx_scale_exp_max(double amax, double emax)
+{
+    if (!(amax > 0.0))
+        return 0;
+    int e = -127;
+    while (e < 127 && amax > ldexp(emax, e))
+        ++e;
+    return e;
+}
+
 typedef struct {
     double *kmean; /* [B*Hkv][d] (fp32 values) */
-    double *qd;    /* [B*H][N][d]   dequantised MXFP4 Q */
-    double *kd;    /* [B*Hkv][N][d] dequantised MXFP4 K - kmean */
-    double *vd;    /* [B*Hkv][N][d] dequantised MXFP4 V */
+    double *qd;    /* [B*H][N][d]   dequantised MX Q */
+    double *kd;    /* [B*Hkv][N][d] dequantised MX K - kmean */
+    double *vd;    /* [B*Hkv][N][d] dequantised MX V */
+    int elem;      /* MX_E2M1 or MX_E2M3 */
 } mx_state;
 
-/* Dequantised value of x in an MX block with shared exponent e. */
-static double mx_round(double x, int e)
+/* Dequantised value of x in an MX block of the state's element format with
+ * shared exponent e. */
+static double mx_round(const mx_state *st, double x, int e)
 {
-    return ldexp(oracle_e2m1_decode(oracle_e2m1_encode(ldexp(x, -e))), e);
+    return ldexp(mx_elem_round(st->elem, ldexp(x, -e)), e);
+}
+
+/* The block exponent in the state's element format. */
+static int mx_block_exp(const mx_state *st, double amax)
+{
+    return oracle_mx_scale_exp_max(amax, mx_elem_max(st->elem));
 }
 
 static void mx_prepare(const uint16_t *q, const uint16_t *k, const uint16_t *v, int B, int H,
@@ -744,11 +811,11 @@ static void mx_prepare(const uint16_t *q, const uint16_t *k, const uint16_t *v, 
                     if (fabs(x[c]) > amax)
                         amax = fabs(x[c]);
                 }
-                int e = oracle_mx_scale_exp(amax);
+                int e = mx_block_exp(st, amax);
                 /* without quantisation K - kmean is taken exactly */
                 for (int c = 0; c < 32; ++c)
                     st->kd[(bg * N + n) * d + c0 + c] =
-                        quant_qk ? mx_round(x[c], e)
+                        quant_qk ? mx_round(st, x[c], e)
                                  : bf16_to_f64(kb[n * d + c0 + c]) - st->kmean[bg * d + c0 + c];
             }
         for (int c = 0; c < d; ++c)
@@ -758,10 +825,10 @@ static void mx_prepare(const uint16_t *q, const uint16_t *k, const uint16_t *v, 
                 for (int64_t n = n0; n < n1; ++n)
                     if (fabs(bf16_to_f64(vb[n * d + c])) > amax)
                         amax = fabs(bf16_to_f64(vb[n * d + c]));
-                int e = oracle_mx_scale_exp(amax);
+                int e = mx_block_exp(st, amax);
                 for (int64_t n = n0; n < n1; ++n) {
                     double x = bf16_to_f64(vb[n * d + c]);
-                    st->vd[(bg * N + n) * d + c] = quant_v ? mx_round(x, e) : x;
+                    st->vd[(bg * N + n) * d + c] = quant_v ? mx_round(st, x, e) : x;
                 }
             }
     }
@@ -774,38 +841,40 @@ static void mx_prepare(const uint16_t *q, const uint16_t *k, const uint16_t *v, 
                 for (int c = 0; c < 32; ++c)
                     if (fabs(bf16_to_f64(qb[n * d + c0 + c])) > amax)
                         amax = fabs(bf16_to_f64(qb[n * d + c0 + c]));
-                int e = oracle_mx_scale_exp(amax);
+                int e = mx_block_exp(st, amax);
                 for (int c = 0; c < 32; ++c) {
                     double x = bf16_to_f64(qb[n * d + c0 + c]);
-                    st->qd[(bh * N + n) * d + c0 + c] = quant_qk ? mx_round(x, e) : x;
+                    st->qd[(bh * N + n) * d + c0 + c] = quant_qk ? mx_round(st, x, e) : x;
                 }
             }
     }
 }
 
 /*
- * MXFP4 quantised attention for the listed rows, the steps in order:
+ * MX quantised attention for the listed rows, elements E2M1 (elem 0, MXFP4)
+ * or E2M3 (elem 1, MXFP6), the steps in order:
  *   1. Smooth-K: K' = K - mean_n K (per channel, all tokens of the kv head);
- *   2. Q and K' to MXFP4 in blocks of 32 channels, V in blocks of 32 tokens
- *      (E2M1 elements, shared power-of-two scale, oracle_mx_scale_exp);
+ *   2. Q and K' to MX blocks of 32 channels, V in blocks of 32 tokens (the
+ *      element format's codes, shared power-of-two scale 2^e with e the
+ *      smallest exponent that keeps the block's max within the format's
+ *      largest magnitude, oracle_mx_scale_exp_max);
  *   3. S_ij = scale * (q^_i . k^_j);
  *   4. keys in tiles of tile_n (a multiple of 32) from key 0 upward, with the
  *      exact running max m: m' = max(m, the tile's max visible score),
  *      p_j = exp(S_ij - m') in (0, 1] (the per-row normalisation), l =
- *      l * exp(m - m') + sum_j p_j, and P^ = MXFP4(p) in blocks of 32
+ *      l * exp(m - m') + sum_j p_j, and P^ = MX(p) in blocks of 32
  *      consecutive keys (the block's max sets its scale), acc = acc *
  *      exp(m - m') + sum_j P^_j V^_j;
  *   5. O = acc / l;  lse = m + ln l + scale * (q_i . kmean).
  * quant_qk / quant_p / quant_v = 0 skip a quantisation step.
  */
-double oracle_mxfp4_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v, int B, int H,
-                         int Hkv, int N, int d, int causal, double scale, int tile_n,
-                         int smooth_k, int quant_qk, int quant_p, int quant_v,
-                         const int64_t *rows, int64_t nrows, double *o, double *lse,
-                         int nthreads)
+double oracle_mx_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v, int B, int H,
+                      int Hkv, int N, int d, int causal, double scale, int tile_n, int elem,
+                      int smooth_k, int quant_qk, int quant_p, int quant_v,
+                      const int64_t *rows, int64_t nrows, double *o, double *lse, int nthreads)
 {
     if (B <= 0 || H <= 0 || Hkv <= 0 || H % Hkv != 0 || N <= 0 || d <= 0 || d % 32 != 0 ||
-        tile_n <= 0 || tile_n % 32 != 0)
+        tile_n <= 0 || tile_n % 32 != 0 || (elem != MX_E2M1 && elem != MX_E2M3))
         return -1.0;
 #ifdef _OPENMP
     if (nthreads > 0)
@@ -816,6 +885,7 @@ double oracle_mxfp4_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v
     if (!rows)
         nrows = (int64_t)B * H * N;
     mx_state st;
+    st.elem = elem;
     mx_prepare(q, k, v, B, H, Hkv, N, d, smooth_k, quant_qk, quant_v, &st);
 #pragma omp parallel
     {
@@ -861,9 +931,9 @@ double oracle_mxfp4_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v
                     for (int64_t j = u0; j < u1; ++j)
                         if (P[j - j0] > pmax)
                             pmax = P[j - j0];
-                    int e = oracle_mx_scale_exp(pmax);
+                    int e = mx_block_exp(&st, pmax);
                     for (int64_t j = u0; j < u1; ++j) {
-                        double ph = quant_p ? mx_round(P[j - j0], e) : P[j - j0];
+                        double ph = quant_p ? mx_round(&st, P[j - j0], e) : P[j - j0];
                         const double *vr = st.vd + (bg * N + j) * d;
                         for (int c = 0; c < d; ++c)
                             acc[c] += ph * vr[c];
@@ -887,6 +957,17 @@ double oracle_mxfp4_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v
     free(st.kd);
     free(st.vd);
     return 0.0;
+}
+
+/* The MXFP4 recipe: oracle_mx_rows with E2M1 elements. */
+double oracle_mxfp4_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v, int B, int H,
+                         int Hkv, int N, int d, int causal, double scale, int tile_n,
+                         int smooth_k, int quant_qk, int quant_p, int quant_v,
+                         const int64_t *rows, int64_t nrows, double *o, double *lse,
+                         int nthreads)
+{
+    return oracle_mx_rows(q, k, v, B, H, Hkv, N, d, causal, scale, tile_n, MX_E2M1, smooth_k,
+                          quant_qk, quant_p, quant_v, rows, nrows, o, lse, nthreads);
 }
 
 int oracle_num_threads(void)
