@@ -19,11 +19,12 @@ workload has a bound worth stating:
   sage       the quantised prefill B2 H24 N16384 d128, with its quantisation
              statistics read back from the workspace;
   mxfp4      the same inputs in the MXFP4 mode (FP4 MFMA);
+  mxfp6      the same inputs in the MXFP6 mode (FP6 MFMA, the FP4 rate);
   decode     GQA split-KV decode, contiguous caches and 16-row pages;
 and the fp64 CPU oracle timed on a bounded sample of the headline workload.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                  [--only prefill|noncausal|tiny|long|bwd|varlen|sage|mxfp4|decode]
+                  [--only prefill|noncausal|tiny|long|bwd|varlen|sage|mxfp4|mxfp6|decode]
                   [--calibrate-copy]
 """
 from __future__ import annotations
@@ -50,7 +51,8 @@ PEAK_HBM_GBS = 8000.0       # HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 UTIL_FILE = os.path.join(ROOT, "profiles", "mfma_util.json")
 CSRC = os.path.join(ROOT, "softmax_attention_attn_amd", "csrc")
-LEGS = ("prefill", "noncausal", "tiny", "long", "bwd", "varlen", "sage", "mxfp4", "decode")
+LEGS = ("prefill", "noncausal", "tiny", "long", "bwd", "varlen", "sage", "mxfp4", "mxfp6",
+        "decode")
 
 
 def log(*a):
@@ -356,9 +358,10 @@ def bench_sage(args, stream):
     }
 
 
-def bench_mxfp4(args, stream):
-    """The quantised-prefill inputs (B2 H24 N16384 d128) in the MXFP4 mode:
-    roofline for the fused FP4 kernel against the dense FP4 peak."""
+def bench_mx(args, stream, mode):
+    """The quantised-prefill inputs (B2 H24 N16384 d128) in an MX mode
+    ("mxfp4": E2M1, "mxfp6": E2M3): roofline for the fused kernel against the
+    dense FP4/FP6 peak (the scaled MFMA runs both at one rate)."""
     import softmax_attention_attn_amd as A
     w = workloads.WORKLOADS["sage_prefill"]
     inp = workloads.make(w)
@@ -366,24 +369,26 @@ def bench_mxfp4(args, stream):
     del inp
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
-    ws = torch.empty((A.attn_fwd_workspace_size(w.B, w.H, w.Hkv, w.N, w.d, A.MODES["mxfp4"]),),
+    ws = torch.empty((A.attn_fwd_workspace_size(w.B, w.H, w.Hkv, w.N, w.d, A.MODES[mode]),),
                      dtype=torch.uint8, device="cuda")
 
     def step():
-        A.fwd(q, k, v, causal=w.causal, mode="mxfp4", o=o, lse=lse, workspace=ws, stream=stream)
+        A.fwd(q, k, v, causal=w.causal, mode=mode, o=o, lse=lse, workspace=ws, stream=stream)
 
     st, per_kernel = time_calls(step, args.steps, args.warmup, stream)
     ops = w.flops()
-    files = ["mxfp4.hip", "cdna4.hpp"]
+    files = ["mx.hip", "cdna4.hpp"]
+    kern = "mx_attn" if mode == "mxfp4" else "mx6_attn"
+    elem = "FP4 (E2M1)" if mode == "mxfp4" else "FP6 (E2M3)"
     return {
-        "workload": w.name + "_mxfp4", "value": ops / (st["mean"] * 1e-3) / 1e12, "unit": "TOP/s",
-        "ms_per_step": st["mean"], "step_ms": st,
-        "note": "MXFP4 Q/K/V/P on the FP4 MFMA; value includes the quantisation prologue "
-                "kernels, the roofline the fused attention kernel",
+        "workload": w.name + "_" + mode, "value": ops / (st["mean"] * 1e-3) / 1e12,
+        "unit": "TOP/s", "ms_per_step": st["mean"], "step_ms": st,
+        "note": "MX %s Q/K/V/P on the scaled MFMA; value includes the quantisation prologue "
+                "kernels, the roofline the fused attention kernel" % elem,
         "kernels_ms": per_kernel,
-        "roofline": roofline("mfma", "mx_attn", ops, per_kernel["mx_attn"], PEAK_FP4_TFLOPS,
-                             "TOP/s", traffic=measured_traffic("mx_attn", files),
-                             counters=measured_util("mx_attn", files)),
+        "roofline": roofline("mfma", kern, ops, per_kernel[kern], PEAK_FP4_TFLOPS,
+                             "TOP/s", traffic=measured_traffic(kern, files),
+                             counters=measured_util(kern, files)),
     }
 
 
@@ -574,13 +579,14 @@ def main():
             sg["ms_per_step"], sg["value"], sg["roofline"]["achieved"]))
         out["sage"] = sg
         torch.cuda.empty_cache()
-    if want("mxfp4"):
-        log("mxfp4: sage_prefill inputs, MXFP4 mode")
-        mx = bench_mxfp4(args, stream)
-        log("mxfp4 %.3f ms/step, %.1f TOP/s (attention kernel %.1f TOP/s)" % (
-            mx["ms_per_step"], mx["value"], mx["roofline"]["achieved"]))
-        out["mxfp4"] = mx
-        torch.cuda.empty_cache()
+    for mode in ("mxfp4", "mxfp6"):
+        if want(mode):
+            log("%s: sage_prefill inputs, %s mode" % (mode, mode.upper()))
+            mx = bench_mx(args, stream, mode)
+            log("%s %.3f ms/step, %.1f TOP/s (attention kernel %.1f TOP/s)" % (
+                mode, mx["ms_per_step"], mx["value"], mx["roofline"]["achieved"]))
+            out[mode] = mx
+            torch.cuda.empty_cache()
     if want("decode"):
         log("decode: gqa_decode")
         dec = bench_decode(args, stream)

@@ -83,7 +83,14 @@ typedef enum {
      * max|x| <= 6 * 2^e (no element saturates); S = Q^ K^^T and O = P^ V^ on
      * the FP4 MFMA with fp32 accumulation; l sums the unquantised P; lse is
      * the true LSE.  Prefill only; needs a workspace. */
-    ATTN_MODE_SAGE3_QK_MXFP4_PV_MXFP4 = 2
+    ATTN_MODE_SAGE3_QK_MXFP4_PV_MXFP4 = 2,
+    /* The same recipe with the MX FP6 element format E2M3 ("GPU kernel
+     * overview" page, insights: CDNA4's matrix cores take FP4 and FP6): OCP
+     * E2M3 elements (1 sign, 2 exponent, 3 mantissa bits; largest magnitude
+     * 7.5; nearest, ties to even), one E8M0 scale 2^e per block of 32, e the
+     * smallest exponent with max|x| <= 7.5 * 2^e; the FP6 MFMA runs at the
+     * FP4 rate.  Prefill only; needs a workspace. */
+    ATTN_MODE_SAGE3_QK_MXFP6_PV_MXFP6 = 3
 } attn_mode;
 
 typedef enum { ATTN_OUT_BF16 = 0, ATTN_OUT_FP32 = 1 } attn_dtype;

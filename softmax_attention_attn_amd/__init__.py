@@ -33,11 +33,12 @@ ATTN_ERR_HIP = -4
 ATTN_MODE_EXACT_BF16 = 0
 ATTN_MODE_SAGE_QK_I8_BLK64_PV_FP8_E4M3 = 1
 ATTN_MODE_SAGE3_QK_MXFP4_PV_MXFP4 = 2
+ATTN_MODE_SAGE3_QK_MXFP6_PV_MXFP6 = 3
 ATTN_OUT_BF16 = 0
 ATTN_OUT_FP32 = 1
 
 MODES = {"exact": ATTN_MODE_EXACT_BF16, "sage": ATTN_MODE_SAGE_QK_I8_BLK64_PV_FP8_E4M3,
-         "mxfp4": ATTN_MODE_SAGE3_QK_MXFP4_PV_MXFP4}
+         "mxfp4": ATTN_MODE_SAGE3_QK_MXFP4_PV_MXFP4, "mxfp6": ATTN_MODE_SAGE3_QK_MXFP6_PV_MXFP6}
 
 EXPORTS = ("attn_fwd", "attn_fwd_workspace_size", "attn_fwd_varlen", "attn_bwd",
            "attn_bwd_workspace_size", "attn_decode", "attn_decode_workspace_size",

@@ -132,6 +132,13 @@ void set_partials(attn::DecodeArgs &a, void *base)
         (float *)((char *)base + align_up(sizeof(float) * slots * (a.H / a.Hkv) * a.d, 256));
 }
 
+// The quantised prefill modes (valid modes that only attn_fwd implements).
+bool quant_mode(int mode)
+{
+    return mode == ATTN_MODE_SAGE_QK_I8_BLK64_PV_FP8_E4M3 ||
+           mode == ATTN_MODE_SAGE3_QK_MXFP4_PV_MXFP4 || mode == ATTN_MODE_SAGE3_QK_MXFP6_PV_MXFP6;
+}
+
 // Checks shared by the contiguous and the paged decode; fills everything of
 // DecodeArgs but the cache layout.
 attn_status decode_common(const void *q, const void *k_cache, const void *v_cache,
@@ -155,9 +162,7 @@ attn_status decode_common(const void *q, const void *k_cache, const void *v_cach
         return fail(ATTN_ERR_INVALID_ARG, "split_tokens=%d must be a positive multiple of 64",
                     split_tokens);
     if (mode != ATTN_MODE_EXACT_BF16)
-        return fail(mode == ATTN_MODE_SAGE_QK_I8_BLK64_PV_FP8_E4M3 ||
-                            mode == ATTN_MODE_SAGE3_QK_MXFP4_PV_MXFP4
-                        ? ATTN_ERR_UNSUPPORTED
+        return fail(quant_mode(mode) ? ATTN_ERR_UNSUPPORTED
                         : ATTN_ERR_INVALID_ARG,
                     "decode supports only the exact bf16 mode (mode=%d)", mode);
     if (d != 64 && d != 128)
@@ -229,7 +234,9 @@ size_t attn_fwd_workspace_size(int B, int H, int Hkv, int N, int d, int mode)
     if (mode == ATTN_MODE_SAGE_QK_I8_BLK64_PV_FP8_E4M3)
         return attn::sage_workspace_bytes(B, H, Hkv, N, d);
     if (mode == ATTN_MODE_SAGE3_QK_MXFP4_PV_MXFP4)
-        return attn::mxfp4_workspace_bytes(B, H, Hkv, N, d);
+        return attn::mx_workspace_bytes(B, H, Hkv, N, d, 4);
+    if (mode == ATTN_MODE_SAGE3_QK_MXFP6_PV_MXFP6)
+        return attn::mx_workspace_bytes(B, H, Hkv, N, d, 6);
     return 0;
 }
 
@@ -259,8 +266,7 @@ attn_status attn_fwd(const void *q, const void *k, const void *v, void *o, float
         return fail(ATTN_ERR_INVALID_ARG, "scale must be finite and > 0");
     if (o_dtype != ATTN_OUT_BF16 && o_dtype != ATTN_OUT_FP32)
         return fail(ATTN_ERR_INVALID_ARG, "unknown output dtype %d", o_dtype);
-    if (mode != ATTN_MODE_EXACT_BF16 && mode != ATTN_MODE_SAGE_QK_I8_BLK64_PV_FP8_E4M3 &&
-        mode != ATTN_MODE_SAGE3_QK_MXFP4_PV_MXFP4)
+    if (mode != ATTN_MODE_EXACT_BF16 && !quant_mode(mode))
         return fail(ATTN_ERR_INVALID_ARG, "unknown mode %d", mode);
     if (d != 64 && d != 128)
         return fail(ATTN_ERR_UNSUPPORTED, "head dim d=%d (supported: 64, 128)", d);
@@ -281,7 +287,9 @@ attn_status attn_fwd(const void *q, const void *k, const void *v, void *o, float
         return from_hip(attn::launch_prefill_exact(a, s), "prefill launch");
     attn::SageArgs sa{a, workspace, workspace_bytes};
     if (mode == ATTN_MODE_SAGE3_QK_MXFP4_PV_MXFP4)
-        return from_hip(attn::launch_mxfp4(sa, s), "mxfp4 launch");
+        return from_hip(attn::launch_mx(sa, 4, s), "mxfp4 launch");
+    if (mode == ATTN_MODE_SAGE3_QK_MXFP6_PV_MXFP6)
+        return from_hip(attn::launch_mx(sa, 6, s), "mxfp6 launch");
     return from_hip(attn::launch_sage(sa, s), "sage launch");
 }
 
@@ -304,9 +312,7 @@ attn_status attn_fwd_varlen(const void *q, const void *k, const void *v, void *o
     if (o_dtype != ATTN_OUT_BF16 && o_dtype != ATTN_OUT_FP32)
         return fail(ATTN_ERR_INVALID_ARG, "unknown output dtype %d", o_dtype);
     if (mode != ATTN_MODE_EXACT_BF16)
-        return fail(mode == ATTN_MODE_SAGE_QK_I8_BLK64_PV_FP8_E4M3 ||
-                            mode == ATTN_MODE_SAGE3_QK_MXFP4_PV_MXFP4
-                        ? ATTN_ERR_UNSUPPORTED
+        return fail(quant_mode(mode) ? ATTN_ERR_UNSUPPORTED
                         : ATTN_ERR_INVALID_ARG,
                     "the packed variable-length call supports only the exact mode (mode=%d)",
                     mode);

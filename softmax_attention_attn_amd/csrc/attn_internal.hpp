@@ -79,8 +79,9 @@ size_t decode_partial_slots(int B, int Hkv);
 // partials of attn_decode_noalloc (ATTN_DECODE_SCRATCH_BYTES bytes).
 hipError_t decode_scratch(void **ptr);
 hipError_t launch_sage(const SageArgs &a, hipStream_t s);
-hipError_t launch_mxfp4(const SageArgs &a, hipStream_t s);  // the MXFP4 mode (same arguments)
-size_t mxfp4_workspace_bytes(int B, int H, int Hkv, int N, int d);
+// the MX modes (same arguments): elem_bits 4 = MXFP4 (E2M1), 6 = MXFP6 (E2M3)
+hipError_t launch_mx(const SageArgs &a, int elem_bits, hipStream_t s);
+size_t mx_workspace_bytes(int B, int H, int Hkv, int N, int d, int elem_bits);
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t s);
 size_t sage_workspace_bytes(int B, int H, int Hkv, int N, int d);
 // byte offset of each piece of the quantised mode's workspace (attn.h's

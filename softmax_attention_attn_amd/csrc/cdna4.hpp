@@ -187,6 +187,15 @@ __device__ __forceinline__ void dma16_rsrc(__amdgpu_buffer_rsrc_t r, uint32_t vo
                                              voff, 0, 0, 0);
 }
 
+// The same with a wave-uniform byte offset soff added to voff (a scalar
+// operand, so that loads at different soff share one voff register).
+__device__ __forceinline__ void dma16_rsrc_so(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                              void *lds)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16,
+                                             voff, soff, 0, 0);
+}
+
 // 4-byte direct load through a buffer resource into LDS: lane l's bytes
 // [voff, voff + 4) land at lds + 4 * l (lds wave-uniform).
 __device__ __forceinline__ void dma4_rsrc(__amdgpu_buffer_rsrc_t r, uint32_t voff, void *lds)

@@ -66,6 +66,19 @@ def test_mxfp4_mode(A):
     assert _dec(A, mode=2) == -2
 
 
+def test_mxfp6_mode(A):
+    need4 = A.attn_fwd_workspace_size(1, 4, 2, 100, 128, A.ATTN_MODE_SAGE3_QK_MXFP4_PV_MXFP4)
+    need = A.attn_fwd_workspace_size(1, 4, 2, 100, 128, A.ATTN_MODE_SAGE3_QK_MXFP6_PV_MXFP6)
+    # FP6 codes take 3/4 of a byte per value against FP4's 1/2: the Q^, K^,
+    # V^^T pieces (8 * 128 * 128 values at 64-token padding) grow by 1/4 byte each
+    assert need >= need4 + (4 + 2 + 2) * 128 * 128 // 4
+    assert _fwd(A, mode=3, N=100, workspace=None, workspace_bytes=0) == -3
+    assert _fwd(A, mode=3, N=100, workspace=P, workspace_bytes=need - 1) == -3
+    assert _fwd(A, mode=3, d=96) == -2
+    assert _dec(A, mode=3) == -2
+    assert _fwd(A, mode=4) == -1
+
+
 def test_fwd_sage_workspace_required(A):
     need = A.attn_fwd_workspace_size(1, 4, 2, 16, 128, A.ATTN_MODE_SAGE_QK_I8_BLK64_PV_FP8_E4M3)
     if need == 0:

@@ -149,14 +149,15 @@ def test_sage_workspace_contents_do_not_matter(attn):
         assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]), causal
 
 
-def test_mxfp4_workspace_contents_do_not_matter(attn):
+@pytest.mark.parametrize("mode", ["mxfp4", "mxfp6"])
+def test_mx_workspace_contents_do_not_matter(attn, mode):
     q, k, v = _prefill(B=1, H=4, Hkv=2, N=333, d=128, seed=12)
     B, H, N, d = q.shape
-    need = attn.attn_fwd_workspace_size(B, H, k.shape[1], N, d, attn.MODES["mxfp4"])
+    need = attn.attn_fwd_workspace_size(B, H, k.shape[1], N, d, attn.MODES[mode])
     for causal in (False, True):
-        a = attn.fwd(q, k, v, causal=causal, mode="mxfp4", out_dtype=torch.float32,
+        a = attn.fwd(q, k, v, causal=causal, mode=mode, out_dtype=torch.float32,
                      workspace=torch.zeros((need,), dtype=torch.uint8, device="cuda"))
-        b = attn.fwd(q, k, v, causal=causal, mode="mxfp4", out_dtype=torch.float32,
+        b = attn.fwd(q, k, v, causal=causal, mode=mode, out_dtype=torch.float32,
                      workspace=_poisoned(need))
         torch.cuda.synchronize()
         assert torch.isfinite(b[0]).all() and torch.isfinite(b[1]).all()
