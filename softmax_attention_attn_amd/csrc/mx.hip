@@ -369,6 +369,7 @@ __global__ __launch_bounds__(kThreads) void mx6_quant_qk_kernel(const uint16_t *
     constexpr int NB = D / 32, P = D + 8, TB = kTile * D * 6 / 8;
     static_assert(kTile * NB <= kThreads, "one thread per block of the tile");
     __shared__ __attribute__((aligned(16))) uint16_t tile[kTile * P];
+    __shared__ __attribute__((aligned(16))) float kms[D];  // the kv head's kmean
     const int Npad = (N + kTile - 1) / kTile * kTile;
     const int tid = threadIdx.x;
     const long long row0 = (long long)blockIdx.x * kTile;  // seq * Npad + tok0
@@ -379,6 +380,8 @@ __global__ __launch_bounds__(kThreads) void mx6_quant_qk_kernel(const uint16_t *
     const int tok0 = (int)(u0 % Npad);
     const int g = is_q ? (int)((seq / H) * Hkv + (seq % H) / (H / Hkv)) : (int)seq;
     const uint16_t *src = (is_q ? q : k) + ((size_t)seq * N + tok0) * D;
+    if (tid < D)
+        kms[tid] = w.kmean[(size_t)g * D + tid];
     for (int i = tid; i < kTile * D / 8; i += kThreads) {
         const int r = i / (D / 8);
         u32x4 u = {0, 0, 0, 0};
@@ -401,7 +404,7 @@ __global__ __launch_bounds__(kThreads) void mx6_quant_qk_kernel(const uint16_t *
             x[8 * j + 2 * e + 1] = bf16_hi(u[e]);
         }
     }
-    const float *km = w.kmean + (size_t)g * D + 32 * blk;
+    const float *km = kms + 32 * blk;
     if (is_q) {
         // q . kmean for the LSE correction; the token's NB lanes are consecutive
         float dot = 0.f;
@@ -633,10 +636,13 @@ __device__ __forceinline__ void mx_qtile(const PrefillArgs &a, const MxWs &w, un
                 qf[hh] = ld16(w.qhat + qrow * C::kRow + (2 * hh + g) * 16);
                 qh[hh] = u32x2{0, 0};
             } else {
+                // read once: the non-temporal policy keeps Q^ from pushing the
+                // head's K^ / V^^T (3.2 MB at d = 128, N = 16384) out of the
+                // XCD's 4 MB L2 (HBM reads 564 -> 449 MB at that shape)
                 const uint8_t *qt = w.qhat + (qrow / kTile) * C::kKBytes;
-                qf[hh] = ld16(qt + (qr % kTile) * C::kRow + (2 * hh + g) * 16);
-                qh[hh] = *(const u32x2 *)(qt + C::kKLoBytes +
-                                          ((2 * hh + g) * kTile + kperm(qr % kTile)) * 8);
+                qf[hh] = ld16_nt(qt + (qr % kTile) * C::kRow + (2 * hh + g) * 16);
+                qh[hh] = __builtin_nontemporal_load(
+                    (const u32x2 *)(qt + C::kKLoBytes + ((2 * hh + g) * kTile + kperm(qr % kTile)) * 8));
             }
             qs[hh] = w.qsc[qrow * NB + 2 * hh + g];
         }
