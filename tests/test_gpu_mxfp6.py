@@ -172,3 +172,26 @@ def test_workload_sampled(attn):
     print("mxfp6 %d rows: vs emulator cos %.7f rel-L1 %.2e max |dlse| %.2e per-row max %.2e; "
           "vs exact cos %.5f rel-L1 %.4f" % (len(rows), cos, rel, dl, row.max(), cos_x, rel_x))
     assert row.max() <= EMU_ROW_REL, row.max()
+
+
+@pytest.mark.parametrize("mode", ["sage", "mxfp4", "mxfp6"])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_quantised_modes_deterministic_and_in_bounds(attn, mode, causal):
+    """Every quantised mode gives bitwise the same result on a second call,
+    and on inputs embedded in NaN-filled storage (a read past a tensor's end
+    would poison the output)."""
+    B, H, Hkv, N, d = 1, 4, 2, 333, 128
+    q, k, v, _ = workloads.make_prefill(B, H, Hkv, N, d, seed=17, k_bias_std=3.0)
+    q, k, v = q.cuda(), k.cuda(), v.cuda()
+    o1, l1 = attn.fwd(q, k, v, causal=causal, mode=mode, out_dtype=torch.float32)
+    o2, l2 = attn.fwd(q, k, v, causal=causal, mode=mode, out_dtype=torch.float32)
+    dev = []
+    for t in (q, k, v):
+        buf = torch.full((t.numel() + 8192,), float("nan"), dtype=torch.bfloat16, device="cuda")
+        buf[: t.numel()] = t.reshape(-1)
+        dev.append(buf[: t.numel()].view(t.shape))
+    o3, l3 = attn.fwd(*dev, causal=causal, mode=mode, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o1).all() and torch.isfinite(l1).all()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(o1, o3) and torch.equal(l1, l3)
