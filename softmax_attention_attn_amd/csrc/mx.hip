@@ -23,7 +23,7 @@
 //
 // Kernels: mx_ksum (partial per-channel K sums, fp64) and mx_kmean,
 // mx_quant_qk / mx6_quant_qk (Q and K' blocks and q . kmean), mx_quant_v (V
-// blocks, written feature-major through LDS), mx_attn (the fused attention).
+// blocks, read by channel through LDS), mx_attn (the fused attention).
 //
 // mx_attn: 4 waves x 32 queries per workgroup, three workgroups per CU (the
 // kernel is held to 168 registers, three waves per SIMD: the per-score
@@ -35,7 +35,11 @@
 // block alone, and its codes are directly the B operand of O^T += V^^T P^^T
 // (lane half g supplies keys 32g .. 32g+31, one block, one scale byte).  K^,
 // V^^T and their scales go global -> LDS through direct loads into two
-// stages, one workgroup barrier per tile.
+// stages, one workgroup barrier per tile.  Every operand read is a per-lane
+// base offset plus an immediate, and a V^^T tile is laid out [key
+// block][feature], so that the 16 lanes of a 16-byte read take 256
+// contiguous bytes (with feature rows of 32 bytes, as first built, they
+// conflicted two ways; the change made the FP4 kernel 6% faster).
 //
 // An FP6 block is 24 bytes: the MFMA takes a lane's 32 six-bit codes in bit
 // order over six registers.  Its first 16 bytes are laid out as a whole FP4
@@ -173,12 +177,13 @@ __device__ __forceinline__ int lane_id_here()
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Workspace pieces (byte-addressed; Npad = N rounded up to kTile).  FP4:
-// Q^ and K^ rows of D/2 bytes (channel 2i in the low nibble), V^^T
-// feature-major rows of Npad/2 bytes (key 2i in the low nibble).  FP6: tiles
-// of 64 tokens of 48 D bytes each; a Q^ / K^ tile holds the first 16 bytes of
-// every block token-major ([token][block]) and then their last 8 bytes
-// block-major ([block][kperm(token)]); a V^^T tile holds the first 16 bytes
-// as [key block][feature] and then the last 8 bytes the same way.
+// Q^ and K^ rows of D/2 bytes (channel 2i in the low nibble); V^^T in tiles
+// of 64 keys, each [key block][feature] x 16 bytes (key 2i in the low
+// nibble).  FP6: tiles of 64 tokens of 48 D bytes each; a Q^ / K^ tile holds
+// the first 16 bytes of every block token-major ([token][block]) and then
+// their last 8 bytes block-major ([block][kperm(token)]); a V^^T tile holds
+// the first 16 bytes as [key block][feature] and then the last 8 bytes the
+// same way.
 struct MxWs {
     double *ksum_part;  // [BG][kNCh][D]
     float *kmean;       // [BG][D]
@@ -465,9 +470,11 @@ __global__ __launch_bounds__(kThreads) void mx_quant_v_kernel(const uint16_t *v,
             amax = fmaxf(amax, fabsf(x[i]));
         }
         const int e = mx_exp<F>(amax);
+        // thread tid = h D + c writes slot tid of the tile's [key block][feature]
+        // area(s): contiguous over the threads
         if constexpr (F == 4) {
-            st16(w.vhatT + ((size_t)bg * D + c) * (Npad / 2) + tt * (kTile / 2) + 16 * h,
-                 fp4x32(x, e));
+            uint8_t *tb = w.vhatT + ((size_t)bg * (Npad / kTile) + tt) * (kTile * D / 2);
+            st16(tb + (size_t)tid * 16, fp4x32(x, e));
         } else {
             // the tile's [key block][feature] areas: 16-byte parts, then 8-byte parts
             const i32x6 c6 = fp6x32(x, e);
@@ -576,8 +583,7 @@ __device__ __forceinline__ void mx_qtile(const PrefillArgs &a, const MxWs &w, un
     // kWaves; pieces 0 .. kKLoPieces-1 are the K^ rows (lane l of piece j
     // fills chunk l % kChunks of row (64 j + l) / kChunks, with the chunk
     // swizzle), then (FP6) the K^ tile's block-major 8-byte parts as they
-    // are, then the V^^T tile: FP4 feature rows of 32 bytes, Npad/2 apart;
-    // FP6 the whole tile as it is.  Wave 0 also loads the scales: lanes
+    // are, then the V^^T tile as it is.  Wave 0 also loads the scales: lanes
     // 0..15 the K^ scales of the tile's 64 keys, lanes 16..31 its two V^
     // scale rows (each contiguous; lane l writes LDS bytes 16 l .. 16 l + 15
     // of the scale area)
@@ -601,15 +607,8 @@ __device__ __forceinline__ void mx_qtile(const PrefillArgs &a, const MxWs &w, un
                 dma16_rsrc_so(raw_rsrc(khat + (size_t)t * C::kKBytes, C::kKBytes), 16 * ln,
                               C::kKLoBytes + (pc - C::kKLoPieces) * 1024, st + pc * 1024);
             } else if (pc < C::kKPieces + C::kVPieces) {
-                if constexpr (F == 4) {
-                    const int i = (pc - C::kKPieces) * 64 + lane;  // 16-byte piece of the tile
-                    dma16_rsrc(raw_rsrc(vhatT + (size_t)t * (kTile / 2),
-                                        (uint32_t)((D - 1) * (Npad / 2) + kTile / 2)),
-                               (uint32_t)((i >> 1) * (Npad / 2) + (i & 1) * 16), st + pc * 1024);
-                } else {
-                    dma16_rsrc_so(raw_rsrc(vhatT + (size_t)t * C::kVBytes, C::kVBytes), 16 * ln,
-                                  (pc - C::kKPieces) * 1024, st + pc * 1024);
-                }
+                dma16_rsrc_so(raw_rsrc(vhatT + (size_t)t * C::kVBytes, C::kVBytes), 16 * ln,
+                              (pc - C::kKPieces) * 1024, st + pc * 1024);
             }
         }
         if (wave == 0) {
@@ -647,10 +646,10 @@ __device__ __forceinline__ void mx_qtile(const PrefillArgs &a, const MxWs &w, un
             qs[hh] = w.qsc[qrow * NB + 2 * hh + g];
         }
     }
-    // FP6 operand reads: per-lane byte offsets within a stage (the rest of
-    // each address is an immediate)
+    // operand reads: per-lane byte offsets within a stage (the rest of each
+    // address is an immediate)
     uint32_t k_lo[KH], k_hi = 0, k_sc = 0, v_lo = 0, v_hi = 0, v_sc = 0;
-    if constexpr (F == 6) {
+    {
         const int key0 = key_of_row(n, 0);
 #pragma unroll
         for (int hh = 0; hh < KH; ++hh)
@@ -683,23 +682,21 @@ __device__ __forceinline__ void mx_qtile(const PrefillArgs &a, const MxWs &w, un
         u32x2 kh[2][KH], vh[NC];
         uint32_t ks[2][KH], vs[NC];
         if constexpr (F == 4) {
-#pragma unroll
-            for (int bb = 0; bb < 2; ++bb) {
-                const int key = key_of_row(n, bb);
-#pragma unroll
-                for (int hh = 0; hh < KH; ++hh) {
-                    kf[bb][hh] = lds_read_b128<0>(
-                        st + key * C::kRow + (((2 * hh + g) ^ kswz<D>(key)) * 16));
+            static_for<0, 2>([&](auto bbc) {
+                constexpr int bb = decltype(bbc)::value;
+                static_for<0, KH>([&](auto hhc) {
+                    constexpr int hh = decltype(hhc)::value;
+                    kf[bb][hh] = lds_read_b128<bb * 16 * C::kRow>(st + k_lo[hh]);
                     kh[bb][hh] = u32x2{0, 0};
-                    ks[bb][hh] = lds_read_u8(st + C::kKSc + key * NB + 2 * hh + g);
-                }
-            }
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                vf[c] = lds_read_b128<0>(st + C::kKBytes + (32 * c + n) * (kTile / 2) + g * 16);
+                    ks[bb][hh] = lds_read_u8<bb * 16 * NB + 2 * hh>(st + k_sc);
+                });
+            });
+            static_for<0, NC>([&](auto cc) {
+                constexpr int c = decltype(cc)::value;
+                vf[c] = lds_read_b128<32 * c * 16>(st + v_lo);
                 vh[c] = u32x2{0, 0};
-                vs[c] = lds_read_u8(st + C::kVSc + g * D + 32 * c + n);
-            }
+                vs[c] = lds_read_u8<32 * c>(st + v_sc);
+            });
         } else {
             // key block bb is key_of_row(n, 0) + 16 bb: the same swizzle, the
             // next 16 rows, the next 32 slots of the block-major area
