@@ -164,16 +164,6 @@ __device__ __forceinline__ f32x16 mfma_mx(i32x8 a, i32x8 b, f32x16 c, int sa, in
 // slots.
 __device__ __forceinline__ int kperm(int r) { return (r & 15) | ((r >> 1) & 16) | ((r << 1) & 32); }
 
-// The lane id, read where it is called (volatile: the compiler cannot hoist
-// the value, or what is computed from it, out of a loop).
-__device__ __forceinline__ int lane_id_here()
-{
-    int lo, id;
-    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0" : "=v"(lo));
-    asm volatile("v_mbcnt_hi_u32_b32 %0, -1, %1" : "=v"(id) : "v"(lo));
-    return id;
-}
-
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Workspace pieces (byte-addressed; Npad = N rounded up to kTile).  FP4:
@@ -591,9 +581,7 @@ __device__ __forceinline__ void mx_qtile(const PrefillArgs &a, const MxWs &w, un
         if (t >= ntiles)
             return;
         unsigned char *st = stage(t);
-        // FP6: the lane offsets are recomputed from a lane id read here, not
-        // kept live across the loop (the FP6 kernel is at its register limit)
-        const int ln = F == 6 ? lane_id_here() : lane;
+        const int ln = lane;
 #pragma unroll
         for (int u = 0; u < C::kPieceLoads; ++u) {
             const int pc = wave + kWaves * u;
