@@ -358,6 +358,37 @@ def bench_sage(args, stream):
     }
 
 
+def mx_quant_stats(A, ws, w, mode):
+    """Block-scale exponents of Q, K - kmean and V that one MX call left in
+    its workspace (read back after the timed region)."""
+    lay = A.attn_mx_workspace_layout(w.B, w.H, w.Hkv, w.N, w.d, mode)
+    npad = (w.N + 63) // 64 * 64
+    nb = w.d // 32
+    BH, BG = w.B * w.H, w.B * w.Hkv
+
+    def u8(name, n):
+        off = lay[name]
+        return ws[off:off + n]
+
+    def rng(t):
+        t = t.to(torch.int32) - 127
+        return {"min": int(t.min()), "max": int(t.max()), "median": int(t.median())}
+
+    qs = u8("qsc", BH * npad * nb).view(BH, npad, nb)[:, :w.N]
+    ks = u8("ksc", BG * npad * nb).view(BG, npad, nb)[:, :w.N]
+    vs = u8("vscT", BG * (npad // 32) * w.d).view(BG, npad // 32, w.d)[:, :(w.N + 31) // 32]
+    km = ws[lay["kmean"]:lay["kmean"] + 4 * BG * w.d].view(torch.float32)
+    return {
+        "q_block_exp": rng(qs), "k_block_exp": rng(ks), "v_block_exp": rng(vs),
+        "k_mean": {"min": float(km.min()), "max": float(km.max())},
+        "blocks": {"q": qs.numel(), "k": ks.numel(), "v": vs.numel()},
+        "note": "a block of 32 elements has the scale 2^e with e the smallest exponent that "
+                "keeps its max|x| within the element format's largest magnitude (6 for E2M1, "
+                "7.5 for E2M3), so no element saturates; P's block exponents live in "
+                "registers only",
+    }
+
+
 def bench_mx(args, stream, mode):
     """The quantised-prefill inputs (B2 H24 N16384 d128) in an MX mode
     ("mxfp4": E2M1, "mxfp6": E2M3): roofline for the fused kernel against the
@@ -386,6 +417,7 @@ def bench_mx(args, stream, mode):
         "note": "MX %s Q/K/V/P on the scaled MFMA; value includes the quantisation prologue "
                 "kernels, the roofline the fused attention kernel" % elem,
         "kernels_ms": per_kernel,
+        "quant_stats": mx_quant_stats(A, ws, w, mode),
         "roofline": roofline("mfma", kern, ops, per_kernel[kern], PEAK_FP4_TFLOPS,
                              "TOP/s", traffic=measured_traffic(kern, files),
                              counters=measured_util(kern, files)),

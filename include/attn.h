@@ -158,6 +158,47 @@ typedef enum {
 attn_status attn_sage_workspace_layout(int B, int H, int Hkv, int N, int d, size_t *offsets);
 
 /*
+ * The quantisation state an MX-mode attn_fwd call (MXFP4 or MXFP6) leaves in
+ * its workspace, for the same inspection (the "cuda-kernel-pretrain" page's
+ * practice list: scale distributions of a low-precision path).  With Npad =
+ * 64 * ceil(N / 64) and F = 4 or 6 bits per element, the pieces are:
+ *   ATTN_MX_WS_KSUM_PART  fp64 [B*Hkv][16][d]     partial per-channel K sums
+ *   ATTN_MX_WS_KMEAN      fp32 [B*Hkv][d]         per-channel mean of K (Smooth-K)
+ *   ATTN_MX_WS_QKDOT      fp32 [B*H][N]           q . kmean per query
+ *   ATTN_MX_WS_QHAT       [B*H][Npad * d * F / 8] Q codes (see below)
+ *   ATTN_MX_WS_QSC        u8 [B*H][Npad][d/32]    Q block scales, E8M0 (2^(byte - 127))
+ *   ATTN_MX_WS_KHAT       [B*Hkv][Npad * d * F / 8] K - kmean codes
+ *   ATTN_MX_WS_KSC        u8 [B*Hkv][Npad][d/32]  their block scales
+ *   ATTN_MX_WS_VHATT      [B*Hkv][d * Npad * F / 8] V codes, in 64-key tiles
+ *   ATTN_MX_WS_VSCT       u8 [B*Hkv][Npad/32][d]  V block scales (32 keys of a channel)
+ * Codes are in tiles of 64 tokens.  A block of 32 codes is 16 bytes (E2M1,
+ * element i in nibble i % 2 of byte i / 2, low nibble first) or 24 bytes
+ * (E2M3, element i in bits 6i .. 6i+5 of the block read as a little-endian
+ * 192-bit number).  A Q or K tile holds every block's first 16 bytes as
+ * [token][block], then (E2M3) their last 8 bytes as [block][token with
+ * bits 4 and 5 swapped].  A V tile holds them as [key block][channel], in
+ * the same two parts.  Rows past N hold zero codes.
+ */
+typedef enum {
+    ATTN_MX_WS_KSUM_PART = 0,
+    ATTN_MX_WS_KMEAN,
+    ATTN_MX_WS_QKDOT,
+    ATTN_MX_WS_QHAT,
+    ATTN_MX_WS_QSC,
+    ATTN_MX_WS_KHAT,
+    ATTN_MX_WS_KSC,
+    ATTN_MX_WS_VHATT,
+    ATTN_MX_WS_VSCT,
+    ATTN_MX_WS_COUNT
+} attn_mx_ws_piece;
+
+/* Fills offsets[0 .. ATTN_MX_WS_COUNT-1] with the byte offset of each piece
+ * for these sizes and MX mode.  ATTN_ERR_INVALID_ARG for a null offsets, for
+ * a mode that is not an MX mode, or for sizes attn_fwd rejects. */
+attn_status attn_mx_workspace_layout(int B, int H, int Hkv, int N, int d, int mode,
+                                     size_t *offsets);
+
+/*
  * Attention forward over a packed batch of variable-length sequences (the
  * exact mode only): each sequence attends to its own tokens, with the same
  * computation as attn_fwd applied sequence by sequence.  Packing without

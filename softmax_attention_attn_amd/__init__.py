@@ -44,7 +44,7 @@ EXPORTS = ("attn_fwd", "attn_fwd_workspace_size", "attn_fwd_varlen", "attn_bwd",
            "attn_bwd_workspace_size", "attn_decode", "attn_decode_workspace_size",
            "attn_decode_paged", "attn_status_string", "attn_last_error",
            "attn_profiler_enable", "attn_profiler_read", "attn_profiler_launches",
-           "attn_sage_workspace_layout", "attn_decode_noalloc")
+           "attn_sage_workspace_layout", "attn_mx_workspace_layout", "attn_decode_noalloc")
 
 
 class AttnError(RuntimeError):
@@ -188,6 +188,18 @@ def attn_sage_workspace_layout(B, H, Hkv, N, d) -> dict:
     off = (ctypes.c_size_t * len(SAGE_WS_PIECES))()
     _check(_lib.attn_sage_workspace_layout(B, H, Hkv, N, d, off))
     return dict(zip(SAGE_WS_PIECES, off))
+
+
+MX_WS_PIECES = ("ksum_part", "kmean", "qkdot", "qhat", "qsc", "khat", "ksc", "vhatT", "vscT")
+
+
+def attn_mx_workspace_layout(B, H, Hkv, N, d, mode) -> dict:
+    """{piece name: byte offset} of an MX mode's workspace (mode "mxfp4" or
+    "mxfp6", or its attn_mode value)."""
+    m = MODES[mode] if isinstance(mode, str) else int(mode)
+    off = (ctypes.c_size_t * len(MX_WS_PIECES))()
+    _check(_lib.attn_mx_workspace_layout(B, H, Hkv, N, d, m, off))
+    return dict(zip(MX_WS_PIECES, off))
 
 
 # ----------------------------------------------------------------- tensor API

@@ -45,4 +45,6 @@ def declare(lib):
     lib.attn_profiler_launches.argtypes = [ctypes.c_char_p, i, ctypes.POINTER(ctypes.c_float), i]
     lib.attn_sage_workspace_layout.restype = i
     lib.attn_sage_workspace_layout.argtypes = [i, i, i, i, i, ctypes.POINTER(sz)]
+    lib.attn_mx_workspace_layout.restype = i
+    lib.attn_mx_workspace_layout.argtypes = [i, i, i, i, i, i, ctypes.POINTER(sz)]
     return lib

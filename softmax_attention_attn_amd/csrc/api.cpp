@@ -251,6 +251,21 @@ attn_status attn_sage_workspace_layout(int B, int H, int Hkv, int N, int d, size
     return ok();
 }
 
+attn_status attn_mx_workspace_layout(int B, int H, int Hkv, int N, int d, int mode,
+                                     size_t *offsets)
+{
+    if (!offsets)
+        return fail(ATTN_ERR_INVALID_ARG, "offsets must be non-null");
+    if (mode != ATTN_MODE_SAGE3_QK_MXFP4_PV_MXFP4 && mode != ATTN_MODE_SAGE3_QK_MXFP6_PV_MXFP6)
+        return fail(ATTN_ERR_INVALID_ARG, "mode %d is not an MX mode", mode);
+    if (!fwd_sizes_supported(B, H, Hkv, N, d))
+        return fail(ATTN_ERR_INVALID_ARG, "invalid sizes (B=%d H=%d Hkv=%d N=%d d=%d)", B, H, Hkv,
+                    N, d);
+    attn::mx_workspace_layout(B, H, Hkv, N, d,
+                              mode == ATTN_MODE_SAGE3_QK_MXFP6_PV_MXFP6 ? 6 : 4, offsets);
+    return ok();
+}
+
 attn_status attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B,
                      int H, int Hkv, int N, int d, int causal, float scale, int mode,
                      int o_dtype, void *workspace, size_t workspace_bytes, void *stream)

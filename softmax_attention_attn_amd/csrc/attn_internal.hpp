@@ -82,6 +82,10 @@ hipError_t launch_sage(const SageArgs &a, hipStream_t s);
 // the MX modes (same arguments): elem_bits 4 = MXFP4 (E2M1), 6 = MXFP6 (E2M3)
 hipError_t launch_mx(const SageArgs &a, int elem_bits, hipStream_t s);
 size_t mx_workspace_bytes(int B, int H, int Hkv, int N, int d, int elem_bits);
+// byte offset of each piece of an MX mode's workspace (attn.h's
+// attn_mx_ws_piece order, kMxWsPieces entries)
+constexpr int kMxWsPieces = 9;
+void mx_workspace_layout(int B, int H, int Hkv, int N, int d, int elem_bits, size_t *offsets);
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t s);
 size_t sage_workspace_bytes(int B, int H, int Hkv, int N, int d);
 // byte offset of each piece of the quantised mode's workspace (attn.h's

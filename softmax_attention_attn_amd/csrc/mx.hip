@@ -903,6 +903,14 @@ size_t mx_workspace_bytes(int B, int H, int Hkv, int N, int d, int elem_bits)
     return off[9];
 }
 
+void mx_workspace_layout(int B, int H, int Hkv, int N, int d, int elem_bits, size_t *offsets)
+{
+    size_t off[10];
+    mx_layout(B, H, Hkv, N, d, elem_bits, off);
+    for (int i = 0; i < kMxWsPieces; ++i)
+        offsets[i] = off[i];
+}
+
 hipError_t launch_mx(const SageArgs &sa, int elem_bits, hipStream_t s)
 {
     if (elem_bits == 6)

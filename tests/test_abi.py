@@ -79,6 +79,29 @@ def test_mxfp6_mode(A):
     assert _fwd(A, mode=4) == -1
 
 
+def test_mx_workspace_layout(A):
+    for mode, bits in (("mxfp4", 4), ("mxfp6", 6)):
+        B, H, Hkv, N, d = 2, 4, 2, 100, 128
+        lay = A.attn_mx_workspace_layout(B, H, Hkv, N, d, mode)
+        off = list(lay.values())
+        npad = 128
+        sizes = {"ksum_part": 8 * B * Hkv * 16 * d, "kmean": 4 * B * Hkv * d,
+                 "qkdot": 4 * B * H * N, "qhat": B * H * npad * d * bits // 8,
+                 "qsc": B * H * npad * d // 32, "khat": B * Hkv * npad * d * bits // 8,
+                 "ksc": B * Hkv * npad * d // 32, "vhatT": B * Hkv * d * npad * bits // 8,
+                 "vscT": B * Hkv * npad // 32 * d}
+        assert off == sorted(off) and all(o % 256 == 0 for o in off)
+        names = list(lay)
+        for a, b in zip(names, names[1:]):  # pieces in order, each large enough
+            assert lay[b] - lay[a] >= sizes[a], (mode, a)
+        need = A.attn_fwd_workspace_size(B, H, Hkv, N, d, A.MODES[mode])
+        assert need - lay["vscT"] >= sizes["vscT"]
+    with pytest.raises(A.AttnError):
+        A.attn_mx_workspace_layout(1, 2, 2, 10, 128, "sage")
+    with pytest.raises(A.AttnError):
+        A.attn_mx_workspace_layout(1, 2, 2, 10, 96, "mxfp4")
+
+
 def test_fwd_sage_workspace_required(A):
     need = A.attn_fwd_workspace_size(1, 4, 2, 16, 128, A.ATTN_MODE_SAGE_QK_I8_BLK64_PV_FP8_E4M3)
     if need == 0:

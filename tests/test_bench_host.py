@@ -75,3 +75,33 @@ def test_summed_traffic_needs_every_kernel(bench):
     B, files, _ = bench
     assert B.summed_traffic(("bwd_dq", "bwd_dkv"), files) == 110.0
     assert B.summed_traffic(("bwd_dq", "decode_merge"), files) is None
+
+
+@pytest.mark.parametrize("mode", ["mxfp4", "mxfp6"])
+def test_mx_quant_stats_reads_the_scale_pieces(mode):
+    """The MX statistics read the block-scale bytes of real tokens only
+    (padding rows past N are excluded) at the offsets the library reports."""
+    import types
+
+    import torch
+
+    import bench as B
+    import softmax_attention_attn_amd as A
+    w = types.SimpleNamespace(B=1, H=2, Hkv=1, N=70, d=64)
+    need = A.attn_fwd_workspace_size(w.B, w.H, w.Hkv, w.N, w.d, A.MODES[mode])
+    ws = torch.zeros((need,), dtype=torch.uint8)
+    lay = A.attn_mx_workspace_layout(w.B, w.H, w.Hkv, w.N, w.d, mode)
+    npad, nb = 128, 2
+    qs = torch.full((2, npad, nb), 127 - 3, dtype=torch.uint8)
+    qs[1, 5, 1] = 127 + 4   # a real token
+    qs[0, 100, 0] = 255     # padding: must not count
+    ks = torch.full((1, npad, nb), 127 - 1, dtype=torch.uint8)
+    vs = torch.full((1, npad // 32, w.d), 127 + 2, dtype=torch.uint8)
+    vs[0, 3] = 0            # the fourth 32-key block starts at key 96 >= N: padding
+    for name, t in (("qsc", qs), ("ksc", ks), ("vscT", vs)):
+        ws[lay[name]:lay[name] + t.numel()] = t.reshape(-1)
+    st = B.mx_quant_stats(A, ws, w, mode)
+    assert st["q_block_exp"] == {"min": -3, "max": 4, "median": -3}
+    assert st["k_block_exp"] == {"min": -1, "max": -1, "median": -1}
+    assert st["v_block_exp"] == {"min": 2, "max": 2, "median": 2}
+    assert st["blocks"] == {"q": 2 * 70 * 2, "k": 70 * 2, "v": 3 * 64}
