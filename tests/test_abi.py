@@ -121,7 +121,8 @@ def _fwdv(A, **kw):
     (dict(cu_seqlens=None), -1), (dict(q=None), -1), (dict(o=None), -1), (dict(B=0), -1),
     (dict(total=0), -1), (dict(max_seqlen=0), -1), (dict(H=3), -1), (dict(scale=0.0), -1),
     (dict(o_dtype=2), -1), (dict(mode=7), -1),
-    (dict(mode=1), -2), (dict(d=96), -2), (dict(max_seqlen=1 << 25), -2),
+    (dict(mode=1), -2), (dict(mode=2), -2), (dict(mode=3), -2), (dict(d=96), -2),
+    (dict(max_seqlen=1 << 25), -2),
     (dict(B=1 << 20, H=1 << 10, Hkv=1 << 10, d=64, max_seqlen=4096), -2),
 ])
 def test_fwd_varlen_validation(A, kw, status):
@@ -219,7 +220,8 @@ def _decp(A, **kw):
     (dict(page_size=0), -1), (dict(page_size=24), -1), (dict(page_size=-16), -1),
     (dict(page_size=8), -2),                                   # below 16
     (dict(page_size=1 << 20, max_pages=4096), -2),             # 2^32 positions
-    (dict(H=7), -1), (dict(split_tokens=100), -1), (dict(mode=1), -2), (dict(d=80), -2),
+    (dict(H=7), -1), (dict(split_tokens=100), -1), (dict(mode=1), -2), (dict(mode=2), -2),
+    (dict(mode=3), -2), (dict(mode=4), -1), (dict(d=80), -2),
     (dict(workspace=None), -3), (dict(workspace_bytes=1000), -3),
 ])
 def test_decode_paged_validation(A, kw, status):
