@@ -64,6 +64,7 @@ CASES = [
     (1, 2, 2, 257, 128, True),
     (1, 4, 4, 512, 128, True),
     (2, 8, 2, 1000, 128, True),
+    (1, 6, 2, 333, 64, True),
 ]
 
 
@@ -130,3 +131,15 @@ def test_workload_sampled(attn):
     print("mxfp4 %d rows: vs emulator cos %.7f rel-L1 %.2e max |dlse| %.2e per-row max %.2e; "
           "vs exact cos %.5f rel-L1 %.4f" % (len(rows), cos, rel, dl, row.max(), cos_x, rel_x))
     assert row.max() <= EMU_ROW_REL, row.max()
+
+
+def test_without_lse(attn):
+    """lse is optional: O is the same with and without it."""
+    B, H, N, d = 1, 2, 200, 128
+    q, k, v, _ = workloads.make_prefill(B, H, H, N, d, seed=40, k_bias_std=3.0)
+    q, k, v = q.cuda(), k.cuda(), v.cuda()
+    o1, _ = attn.fwd(q, k, v, causal=True, mode="mxfp4", out_dtype=torch.float32)
+    o2 = torch.empty_like(o1)
+    attn.fwd(q, k, v, causal=True, mode="mxfp4", o=o2, with_lse=False, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)

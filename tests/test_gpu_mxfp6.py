@@ -63,6 +63,7 @@ CASES = [
     (1, 2, 2, 257, 128, True),
     (1, 4, 4, 512, 128, True),
     (2, 8, 2, 1000, 128, True),
+    (1, 6, 2, 333, 64, True),
     (1, 2, 2, 1, 64, True),
 ]
 
@@ -195,3 +196,15 @@ def test_quantised_modes_deterministic_and_in_bounds(attn, mode, causal):
     assert torch.isfinite(o1).all() and torch.isfinite(l1).all()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     assert torch.equal(o1, o3) and torch.equal(l1, l3)
+
+
+def test_without_lse(attn):
+    """lse is optional: O is the same with and without it."""
+    B, H, N, d = 1, 2, 200, 128
+    q, k, v, _ = workloads.make_prefill(B, H, H, N, d, seed=40, k_bias_std=3.0)
+    q, k, v = q.cuda(), k.cuda(), v.cuda()
+    o1, _ = attn.fwd(q, k, v, causal=True, mode="mxfp6", out_dtype=torch.float32)
+    o2 = torch.empty_like(o1)
+    attn.fwd(q, k, v, causal=True, mode="mxfp6", o=o2, with_lse=False, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
